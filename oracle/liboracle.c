@@ -1,0 +1,268 @@
+/*
+ * liboracle -- plain C statement of the 4-bit codecs, for sizes where the
+ * numpy oracle would take minutes.  TEST INFRASTRUCTURE ONLY: loaded by the
+ * test-suite and by the CPU-baseline leg of the benchmark, never by the GPU
+ * library, and it includes no header of the GPU library.
+ *
+ * Same definitions as the Python oracle (oracle/*.py), written again as
+ * straight loops so that the two can be checked against each other:
+ *
+ *  - dyadic codec (DyadicGumbel page, sections 2.1, 2.2, 2.5): scale = group
+ *    absmax, codes (s/8)(j-8), index = lowest j minimising |w - c_j| over the
+ *    16 codes in double, all-zero group -> index 8, dequant RNE_bf16 of the
+ *    exact product with a zero result stored as +0;
+ *  - LUT16 codec (k-means page, sections 1.2, 2.2): levels v_j = s*L_j in
+ *    float (exact), index = lowest j minimising |fl32(w - v_j)|;
+ *  - sign + magnitude codec (int4-g32 page, sections 1.3, 2): sign = (w < 0),
+ *    magnitude index = lowest j minimising |fl32(|w| - M_j)|;
+ *  - the 1D Lloyd fit (k-means page section 1.2; int4-g32 page section 1.3):
+ *    quantile start sorted[k*stride + stride/2], then `iters` rounds of
+ *    nearest-centre assignment (double, lowest index on a tie) and member
+ *    mean (double sum in increasing element order); empty centres stay.
+ *
+ * Build: gcc -O2 -fno-fast-math -ffp-contract=off -fopenmp -shared -fPIC.
+ * Every function returns 0, or -1 on a shape it does not accept.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------ formats */
+static double bf16_val(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+static double f16_val(uint16_t b) {
+  int s = b >> 15, e = (b >> 10) & 31, m = b & 1023;
+  double v;
+  if (e == 0) v = ldexp((double)m, -24);
+  else if (e == 31) v = m ? NAN : INFINITY;
+  else v = ldexp((double)(m + 1024), e - 25);
+  return s ? -v : v;
+}
+
+/* Round |x| to a grid with p significant bits and subnormal quantum 2^qmin. */
+static double round_grid(double a, int p, int qmin) {
+  if (a == 0.0) return 0.0;
+  int E;
+  frexp(a, &E);          /* a = m * 2^E, m in [0.5, 1) */
+  int q = E - 1 - (p - 1);
+  if (q < qmin) q = qmin;
+  return ldexp(nearbyint(ldexp(a, -q)), q);  /* default mode: ties to even */
+}
+
+static uint16_t rne_bf16(double x) {
+  int neg = signbit(x) != 0;
+  double m = round_grid(fabs(x), 8, -133);
+  uint32_t u;
+  if (m >= ldexp(1.0, 128)) {
+    u = 0x7F800000u;
+  } else {
+    float f = (float)m; /* exact */
+    memcpy(&u, &f, 4);
+  }
+  return (uint16_t)((u >> 16) | (neg ? 0x8000u : 0u));
+}
+
+static uint16_t rne_fp16(double x) {
+  int neg = signbit(x) != 0;
+  double m = round_grid(fabs(x), 11, -24);
+  uint16_t b;
+  if (m >= 65536.0) {
+    b = 0x7C00;
+  } else if (m < ldexp(1.0, -14)) {
+    b = (uint16_t)ldexp(m, 24); /* subnormal: integer multiple of 2^-24 */
+  } else {
+    int E;
+    double fr = frexp(m, &E);   /* m = fr * 2^E, fr in [0.5,1) */
+    int e = E - 1;              /* m in [2^e, 2^(e+1)) */
+    uint16_t mant = (uint16_t)(ldexp(fr, 11) - 1024.0);
+    b = (uint16_t)(((e + 15) << 10) | mant);
+  }
+  return (uint16_t)(b | (neg ? 0x8000u : 0u));
+}
+
+/* ------------------------------------------------------------ dyadic */
+int oracle_dyadic_quantize(const uint16_t* w, int64_t n, int64_t k, uint8_t* idx,
+                           uint16_t* scales) {
+  if (k % 64) return -1;
+  const int64_t g = k / 64;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n; ++r) {
+    for (int64_t gi = 0; gi < g; ++gi) {
+      const uint16_t* wg = w + r * k + gi * 64;
+      double s = 0.0;
+      for (int i = 0; i < 64; ++i) {
+        double a = fabs(bf16_val(wg[i]));
+        if (a > s) s = a;
+      }
+      scales[r * g + gi] = rne_bf16(s); /* s is a bf16 value: exact */
+      for (int i = 0; i < 64; ++i) {
+        int best = 8;
+        if (s != 0.0) {
+          double wi = bf16_val(wg[i]);
+          double bd = INFINITY;
+          for (int j = 0; j < 16; ++j) {
+            double c = (s / 8.0) * (double)(j - 8);
+            double d = fabs(wi - c);
+            if (d < bd) { bd = d; best = j; }
+          }
+        }
+        idx[r * k + gi * 64 + i] = (uint8_t)best;
+      }
+    }
+  }
+  return 0;
+}
+
+int oracle_dyadic_dequant(const uint8_t* idx, const uint16_t* scales, int64_t n, int64_t k,
+                          uint16_t* out) {
+  if (k % 64) return -1;
+  const int64_t g = k / 64;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n; ++r)
+    for (int64_t c = 0; c < k; ++c) {
+      double s = bf16_val(scales[r * g + c / 64]);
+      double v = (s / 8.0) * (double)((int)idx[r * k + c] - 8);
+      if (v == 0.0) v = 0.0; /* a zero result is +0 */
+      out[r * k + c] = rne_bf16(v);
+    }
+  return 0;
+}
+
+/* ------------------------------------------------------------ LUT16 */
+int oracle_lut16_indices(const uint16_t* w, const uint16_t* scales, const uint16_t* lut,
+                         int64_t n, int64_t k, uint8_t* idx) {
+  if (k % 64) return -1;
+  const int64_t g = k / 64;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n; ++r)
+    for (int64_t gi = 0; gi < g; ++gi) {
+      float v[16];
+      double s = bf16_val(scales[r * g + gi]);
+      for (int j = 0; j < 16; ++j) v[j] = (float)(s * bf16_val(lut[(r * g + gi) * 16 + j]));
+      for (int i = 0; i < 64; ++i) {
+        float wi = (float)bf16_val(w[r * k + gi * 64 + i]);
+        int best = 0;
+        float bd = fabsf(wi - v[0]);
+        for (int j = 1; j < 16; ++j) {
+          float d = fabsf(wi - v[j]);
+          if (d < bd) { bd = d; best = j; }
+        }
+        idx[r * k + gi * 64 + i] = (uint8_t)best;
+      }
+    }
+  return 0;
+}
+
+/* ------------------------------------------------------------ sign + magnitude */
+int oracle_signmag8_indices(const uint16_t* w, const uint16_t* cb, int64_t n, int64_t k,
+                            uint8_t* nib) {
+  if (k % 32) return -1;
+  const int64_t g = k / 32;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n; ++r)
+    for (int64_t gi = 0; gi < g; ++gi) {
+      float m[8];
+      for (int j = 0; j < 8; ++j) m[j] = (float)f16_val(cb[(r * g + gi) * 8 + j]);
+      for (int i = 0; i < 32; ++i) {
+        float wi = (float)bf16_val(w[r * k + gi * 32 + i]);
+        float a = fabsf(wi);
+        int best = 0;
+        float bd = fabsf(a - m[0]);
+        for (int j = 1; j < 8; ++j) {
+          float d = fabsf(a - m[j]);
+          if (d < bd) { bd = d; best = j; }
+        }
+        nib[r * k + gi * 32 + i] = (uint8_t)(((wi < 0.0f) ? 8 : 0) | best);
+      }
+    }
+  return 0;
+}
+
+/* ------------------------------------------------------------ 1D Lloyd */
+static void sort_doubles(double* a, int n) { /* insertion sort, n <= 64 */
+  for (int i = 1; i < n; ++i) {
+    double v = a[i];
+    int j = i - 1;
+    while (j >= 0 && a[j] > v) { a[j + 1] = a[j]; --j; }
+    a[j + 1] = v;
+  }
+}
+
+static void lloyd1d(const double* u, int gsz, double* c, int nc, int iters) {
+  double srt[64];
+  memcpy(srt, u, sizeof(double) * gsz);
+  sort_doubles(srt, gsz);
+  const int stride = gsz / nc;
+  for (int q = 0; q < nc; ++q) c[q] = srt[q * stride + stride / 2];
+  int a[64];
+  for (int it = 0; it < iters; ++it) {
+    for (int i = 0; i < gsz; ++i) {
+      int best = 0;
+      double bd = fabs(u[i] - c[0]);
+      for (int q = 1; q < nc; ++q) {
+        double d = fabs(u[i] - c[q]);
+        if (d < bd) { bd = d; best = q; }
+      }
+      a[i] = best;
+    }
+    double sum[16];
+    int cnt[16];
+    for (int q = 0; q < nc; ++q) { sum[q] = 0.0; cnt[q] = 0; }
+    for (int i = 0; i < gsz; ++i) { sum[a[i]] += u[i]; cnt[a[i]] += 1; }
+    for (int q = 0; q < nc; ++q)
+      if (cnt[q] > 0) c[q] = sum[q] / (double)cnt[q];
+  }
+}
+
+int oracle_lut16_fit(const uint16_t* w, int64_t n, int64_t k, int iters, uint16_t* scales,
+                     uint16_t* lut) {
+  if (k % 64) return -1;
+  const int64_t g = k / 64;
+#pragma omp parallel for schedule(dynamic, 256)
+  for (int64_t t = 0; t < n * g; ++t) {
+    const int64_t r = t / g, gi = t % g;
+    double u[64], c[16];
+    double s = 0.0;
+    for (int i = 0; i < 64; ++i) {
+      u[i] = bf16_val(w[r * k + gi * 64 + i]);
+      if (fabs(u[i]) > s) s = fabs(u[i]);
+    }
+    scales[t] = rne_bf16(s);
+    if (s == 0.0) {
+      for (int q = 0; q < 16; ++q) lut[t * 16 + q] = 0;
+      continue;
+    }
+    for (int i = 0; i < 64; ++i) u[i] = u[i] / s;
+    lloyd1d(u, 64, c, 16, iters);
+    for (int q = 0; q < 16; ++q) lut[t * 16 + q] = rne_bf16(c[q]);
+  }
+  return 0;
+}
+
+int oracle_signmag8_fit(const uint16_t* w, int64_t n, int64_t k, int iters, uint16_t* cb) {
+  if (k % 32) return -1;
+  const int64_t g = k / 32;
+#pragma omp parallel for schedule(dynamic, 256)
+  for (int64_t t = 0; t < n * g; ++t) {
+    const int64_t r = t / g, gi = t % g;
+    double a[32], c[8];
+    for (int i = 0; i < 32; ++i) a[i] = fabs(bf16_val(w[r * k + gi * 32 + i]));
+    lloyd1d(a, 32, c, 8, iters);
+    for (int q = 0; q < 8; ++q) cb[t * 8 + q] = rne_fp16(c[q]);
+  }
+  return 0;
+}
+
+/* number of OpenMP threads a parallel region uses (reported by the benchmark) */
+#ifdef _OPENMP
+#include <omp.h>
+int oracle_num_threads(void) { return omp_get_max_threads(); }
+#else
+int oracle_num_threads(void) { return 1; }
+#endif

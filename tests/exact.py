@@ -1,0 +1,109 @@
+"""Exact (rational / integer) arithmetic used to pin the oracle.
+
+Nothing here shares code with ``oracle/``: bf16 / fp16 patterns are decoded
+into integers by hand and rounding is done on Python integers, so a slip in
+the oracle's float-based helpers cannot hide behind the same slip here.
+"""
+
+from fractions import Fraction
+
+import numpy as np
+
+
+def bf16_fraction(b):
+    """bf16 bit pattern -> exact Fraction (finite only)."""
+    b = int(b)
+    sign = -1 if b & 0x8000 else 1
+    e = (b >> 7) & 0xFF
+    m = b & 0x7F
+    assert e != 0xFF
+    if e == 0:
+        v = Fraction(m, 1 << 133)
+    else:
+        v = Fraction(m + 128) * (Fraction(2) ** (e - 127 - 7))
+    return sign * v
+
+
+def f16_fraction(b):
+    b = int(b)
+    sign = -1 if b & 0x8000 else 1
+    e = (b >> 10) & 0x1F
+    m = b & 0x3FF
+    assert e != 0x1F
+    if e == 0:
+        v = Fraction(m, 1 << 24)
+    else:
+        v = Fraction(m + 1024) * (Fraction(2) ** (e - 15 - 10))
+    return sign * v
+
+
+def _floor_log2(a):
+    """floor(log2(a)) for a positive Fraction."""
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    elif Fraction(2) ** (e + 1) <= a:
+        e += 1
+    return e
+
+
+def _rne_int(x):
+    """Round a non-negative Fraction to the nearest integer, ties to even."""
+    n = x.numerator // x.denominator
+    rem = x - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return n
+
+
+def rne_fraction(v, p, qmin, emax):
+    """Exact round-to-nearest-even of a Fraction onto a binary format grid:
+    returns a Fraction, or +-inf as float."""
+    if v == 0:
+        return Fraction(0)
+    a = abs(v)
+    e = _floor_log2(a)
+    q = max(e - (p - 1), qmin)
+    r = _rne_int(a / (Fraction(2) ** q))
+    res = r * (Fraction(2) ** q)
+    if res >= Fraction(2) ** (emax + 1):
+        return float("inf") if v > 0 else float("-inf")
+    return res if v > 0 else -res
+
+
+def rne_bf16_fraction(v):
+    return rne_fraction(v, 8, -133, 127)
+
+
+def rne_fp16_fraction(v):
+    return rne_fraction(v, 11, -24, 15)
+
+
+def fraction_to_bf16_bits(v):
+    """Exact bf16 value (Fraction, or +-inf) -> bit pattern.  Zero -> +0."""
+    if isinstance(v, float):
+        return 0x7F80 if v > 0 else 0xFF80
+    sign = 0x8000 if v < 0 else 0
+    a = abs(v)
+    if a == 0:
+        return 0
+    e = _floor_log2(a)
+    if e < -126:
+        m = a * (Fraction(2) ** 133)
+        assert m.denominator == 1 and m < 128
+        return sign | int(m)
+    m = a / (Fraction(2) ** (e - 7))
+    assert m.denominator == 1 and 128 <= m < 256
+    return sign | ((e + 127) << 7) | (int(m) - 128)
+
+
+def bf16_int_parts(bits):
+    """Vectorised: bf16 bits -> (signed integer significand W, exponent a) with
+    value = W * 2**a exactly (zeros give W = 0)."""
+    b = np.asarray(bits, dtype=np.int64)
+    e = (b >> 7) & 0xFF
+    m = b & 0x7F
+    sig = np.where(e == 0, m, m + 128)
+    a = np.where(e == 0, -133, e - 127 - 7)
+    sig = np.where(b & 0x8000, -sig, sig)
+    return sig, a

@@ -1,0 +1,203 @@
+"""Pins for oracle/lut16.py and oracle/signmag8.py (and the shared Lloyd fit).
+
+The nearest-level decision, dequant and fit of both LUT codecs are pinned by
+exact-rational brute force, exact special cases, the Lloyd monotonicity the
+int4-g32 page states (section 1.3: the per-weight MSE never rises from one
+round to the next), the optimal 1D k-means cost computed by dynamic
+programming, and agreement between the numpy and C implementations.
+"""
+
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import synthetic
+from oracle import bits, lut16, native, packing, signmag8
+from tests import exact
+
+
+def _lut_data(rows=8, k=512, seed=21):
+    return synthetic.normal_outliers_bf16((rows, k), 0.015, 0.001, 0.15, seed)
+
+
+# ------------------------------------------------------------------ LUT16 argmin
+def test_lut16_decision_vs_exact_argmin():
+    w = _lut_data()
+    s, L = lut16.fit(w)
+    idx = lut16.indices(w, s, L)
+    n, k = w.shape
+    mism = 0
+    for r in range(n):
+        for c in range(0, k, 3):
+            g = c // 64
+            sv = exact.bf16_fraction(s[r, g])
+            lv = [sv * exact.bf16_fraction(x) for x in L[r, g]]
+            wv = exact.bf16_fraction(w[r, c])
+            d = [abs(wv - v) for v in lv]
+            want = d.index(min(d))
+            mism += int(idx[r, c] != want)
+    assert mism == 0
+
+
+def test_lut16_decision_ties_go_low_and_fp32_rule():
+    # two equal levels -> lower index; an exact midpoint -> lower index
+    s = np.array([[0x3F80]], np.uint16)                     # s = 1
+    L = np.zeros((1, 1, 16), np.uint16)
+    L[0, 0, :] = bits.rne_bf16(np.linspace(-1, 1, 16))
+    L[0, 0, 9] = L[0, 0, 4]                                  # duplicate level
+    w = np.zeros((1, 64), np.uint16)
+    lv = bits.bf16_to_f64(L[0, 0])
+    w[0, 0] = L[0, 0, 4]
+    mid = (lv[10] + lv[11]) / 2
+    w[0, 1] = bits.rne_bf16(np.array([mid]))[0]
+    idx = lut16.indices(w, s, L)
+    assert idx[0, 0] == 4
+    wv = bits.bf16_to_f64(w[0, 1:2])[0]
+    d = np.abs(wv - lv)
+    assert idx[0, 1] == int(np.flatnonzero(d == d.min())[0])
+
+
+def test_lut16_dequant_exact_product_rounding():
+    w = _lut_data(4, 256, 22)
+    s, L = lut16.fit(w)
+    p = lut16.quantize_pack(w, s, L)
+    deq = lut16.dequant(p, s, L)
+    idx = packing.unpack(p)
+    for r in range(4):
+        for c in range(0, 256, 5):
+            v = exact.bf16_fraction(s[r, c // 64]) * exact.bf16_fraction(L[r, c // 64, idx[r, c]])
+            assert deq[r, c] == exact.fraction_to_bf16_bits(exact.rne_bf16_fraction(v)) or (
+                v == 0 and deq[r, c] in (0, 0x8000))
+
+
+# ------------------------------------------------------------------ Lloyd
+def _optimal_kmeans_cost(x, k):
+    """Optimal 1D k-means SSE by dynamic programming over the sorted points
+    (segment costs computed directly, no prefix-sum cancellation)."""
+    x = np.sort(np.asarray(x, dtype=np.float64))
+    n = len(x)
+    cost = np.full((n + 1, n + 1), np.inf)
+    for i in range(n):
+        for j in range(i + 1, n + 1):
+            seg = x[i:j]
+            cost[i, j] = np.sum((seg - seg.mean()) ** 2)
+    dp = np.full((k + 1, n + 1), np.inf)
+    dp[0, 0] = 0.0
+    for c in range(1, k + 1):
+        for j in range(c, n + 1):
+            dp[c, j] = np.min(dp[c - 1, c - 1:j] + cost[c - 1:j, j])
+    return float(np.min(dp[1:, n]))
+
+
+def test_lloyd_monotone_and_above_optimum():
+    g = np.random.default_rng(5)
+    u = g.standard_t(4, (40, 64)) / 6
+    c0 = lut16.quantile_init(u, 16)
+    c, hist = lut16.lloyd(u, c0, 25, history=True)
+    assert np.all(np.diff(hist, axis=-1) <= 1e-15)
+    for r in range(0, 40, 8):
+        opt = _optimal_kmeans_cost(list(u[r]), 16) / 64
+        assert hist[r, -1] >= opt * (1 - 1e-12)
+
+
+def test_lloyd_separated_clusters_reach_exact_means():
+    g = np.random.default_rng(6)
+    centres = np.arange(16) * 10.0
+    pts = (centres[:, None] + g.integers(-2, 3, (16, 4))).astype(np.float64)
+    u = g.permutation(pts.ravel())[None, :]
+    c = lut16.lloyd(u, lut16.quantile_init(u, 16), 25)[0]
+    for q in range(16):
+        mem = [Fraction(int(v)) for v in pts[q]]
+        assert Fraction(c[q]) == sum(mem) / 4
+
+
+def test_lloyd_known_fixed_point_two_clusters():
+    # points {0,1,2,10}: quantile start (k=2, stride 2) -> c = {1, 10};
+    # assignment {0,1,2}|{10} gives means {1, 10}: a fixed point.
+    u = np.array([[10.0, 0.0, 2.0, 1.0]])
+    c = lut16.lloyd(u, lut16.quantile_init(u, 2), 25)
+    assert list(c[0]) == [1.0, 10.0]
+    # points {0, 4, 5, 6}: start {4, 6}; round 1: {0,4}|{5,6} -> {2, 5.5};
+    # round 2: {0}|{4,5,6} -> {0, 5}; then stable.
+    u = np.array([[0.0, 4.0, 5.0, 6.0]])
+    c, h = lut16.lloyd(u, lut16.quantile_init(u, 2), 25, history=True)
+    assert list(c[0]) == [0.0, 5.0]
+
+
+def test_lut16_fit_recovers_16_point_groups():
+    # a group of 16 distinct values, each 4 times, with absmax 1: exact recovery
+    g = np.random.default_rng(7)
+    vals = np.sort(g.choice(np.arange(-127, 128), 16, replace=False)) / 128.0
+    vals[-1] = 1.0
+    w = bits.rne_bf16(g.permutation(np.repeat(vals, 4)))[None, :]
+    s, L = lut16.fit(w)
+    assert np.array_equal(bits.bf16_to_f64(L[0, 0]), vals)
+    p = lut16.quantize_pack(w, s, L)
+    assert np.array_equal(lut16.dequant(p, s, L), w)
+
+
+def test_lut16_zero_group():
+    w = np.zeros((1, 64), np.uint16)
+    s, L = lut16.fit(w)
+    assert s[0, 0] == 0 and np.all(L == 0)
+    p = lut16.quantize_pack(w, s, L)
+    assert np.all(lut16.dequant(p, s, L) == 0)
+
+
+def test_lut16_c_matches_python():
+    w = _lut_data(16, 1024, 23)
+    w[2, :64] = 0
+    s, L = lut16.fit(w)
+    s2, L2 = native.lut16_fit(w)
+    assert np.array_equal(s, s2) and np.array_equal(L, L2)
+    assert np.array_equal(lut16.indices(w, s, L), native.lut16_indices(w, s, L))
+
+
+# ------------------------------------------------------------------ SIGNMAG8
+def _sm_data(rows=8, k=512, seed=31):
+    return synthetic.student_t_bf16((rows, k), 5, 0.02, seed)
+
+
+def test_signmag8_decision_vs_exact():
+    w = _sm_data()
+    cb = signmag8.fit(w)
+    nib = signmag8.indices(w, cb)
+    for r in range(8):
+        for c in range(0, 512, 3):
+            g = c // 32
+            wv = exact.bf16_fraction(w[r, c])
+            m = [exact.f16_fraction(x) for x in cb[r, g]]
+            d = [abs(abs(wv) - v) for v in m]
+            want = d.index(min(d)) | (8 if wv < 0 else 0)
+            assert nib[r, c] == want
+
+
+def test_signmag8_dequant_sign_and_exact_levels():
+    w = _sm_data(4, 256, 32)
+    w[0, 0] = 0x8000        # -0.0 -> sign bit 0
+    cb = signmag8.fit(w)
+    cb[1, 0, 0] = 0         # a zero magnitude level
+    p = signmag8.quantize_pack(w, cb)
+    nib = packing.unpack(p)
+    assert nib[0, 0] >> 3 == 0
+    deq = signmag8.dequant(p, cb)
+    for r in range(4):
+        for c in range(256):
+            mag = exact.f16_fraction(cb[r, c // 32, nib[r, c] & 7])
+            neg = bool(nib[r, c] & 8)
+            assert exact.f16_fraction(deq[r, c]) == (-mag if neg else mag)
+            assert bool(deq[r, c] & 0x8000) == neg        # -0.0 reproduced
+    # the sign bit is exactly w < 0
+    wv = bits.bf16_to_f64(w)
+    assert np.array_equal((nib >> 3).astype(bool), wv < 0)
+
+
+def test_signmag8_fit_monotone_and_c_matches():
+    w = _sm_data(16, 1024, 33)
+    cb = signmag8.fit(w)
+    assert np.array_equal(cb, native.signmag8_fit(w))
+    assert np.array_equal(signmag8.indices(w, cb), native.signmag8_indices(w, cb))
+    a = np.abs(bits.bf16_to_f64(w)).reshape(-1, 32)
+    _, h = lut16.lloyd(a, lut16.quantile_init(a, 8), 25, history=True)
+    assert np.all(np.diff(h, axis=-1) <= 1e-15)

@@ -1,0 +1,44 @@
+"""Pins for oracle/matmul.py: the fp64 GEMV/GEMM reference and its bound."""
+
+from fractions import Fraction
+
+import numpy as np
+
+import synthetic
+from oracle import bits, dyadic, matmul
+from tests import exact
+
+
+def test_gemm_ref_vs_exact_dot_products():
+    x = synthetic.normal_bf16((3, 128), 1.0, 41)
+    w = synthetic.normal_bf16((5, 128), 0.02, 42)
+    wv = bits.bf16_to_f64(w)
+    y, b = matmul.gemm_ref(x, wv)
+    assert y.shape == (3, 5)
+    for i in range(3):
+        for n in range(5):
+            prods = [exact.bf16_fraction(x[i, k]) * exact.bf16_fraction(w[n, k]) for k in range(128)]
+            ye = sum(prods, Fraction(0))
+            be = sum((abs(p) for p in prods), Fraction(0))
+            assert abs(Fraction(y[i, n]) - ye) <= be * Fraction(1, 2 ** 45)
+            assert abs(Fraction(b[i, n]) - be) <= be * Fraction(1, 2 ** 45)
+
+
+def test_unit_vector_selects_a_column():
+    w = synthetic.normal_bf16((16, 256), 0.02, 43)
+    p, s = dyadic.quantize_pack(w)
+    wh = bits.bf16_to_f64(dyadic.dequant(p, s))
+    x = np.zeros((1, 256), np.uint16)
+    x[0, 77] = 0x3F80
+    y, _ = matmul.gemm_ref(x, wh)
+    assert np.array_equal(y[0], wh[:, 77])
+
+
+def test_tolerance_rule():
+    y_ref = np.array([1.0, -2.0, 0.0])
+    bound = np.array([10.0, 10.0, 10.0])
+    assert matmul.within_tolerance(y_ref + 0.0099, y_ref, bound).all()
+    assert not matmul.within_tolerance(y_ref + 0.0102, y_ref, bound).any()
+    assert matmul.within_tolerance(np.array([0, 0, 9e-7]), np.zeros(3), np.zeros(3)).all()
+    # bf16 output adds one output rounding
+    assert matmul.within_tolerance([1.0 + 2 ** -8], [1.0], [0.0], bf16_out=True).all()

@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark of the W4 dequant-GEMV / GEMM hot path on one MI355X.
+
+Headline (`value`): W4A16 GEMV at m = 1 over the whole 1B decode stack -- 24
+blocks x (q, k, v, o [2048, 2048]; gate, up [5632, 2048]; down [2048, 5632])
+= 168 matrices, 1,233,125,376 dyadic 4-bit weights in groups of 64, Student-t
+(nu = 4) weights scaled to sigma 0.02, one N(0, 1) bf16 activation vector per
+matrix.  One step = one pass over the stack (one batched launch), inputs
+resident in HBM.  `value` = algorithmic bytes of the pass (packed nibbles +
+bf16 scales + x + fp32 y) / step time, in GB/s.
+
+Also measured in the same run and reported under "rows": the same pass as
+168 separate w4_gemv calls, quantize_pack and unpack_dequant over the stack,
+and the prefill GEMM (M = 256, K = N = 8192, in TFLOP/s) with quantize_pack of
+its 8192^2 weight.  The CPU baseline times the oracle (numpy, one thread) on
+the first block of the stack.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+METRIC = "W4 dequant-GEMV GB/s (% HBM peak) at m=1; W4A16 GEMM TFLOP/s at m=256"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-headline", action="store_true",
+                    help="time only the batched decode pass (for profiler runs)")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    """Hash of the GEMV kernel sources, to tie stored counter readings to code."""
+    h = hashlib.sha256()
+    for f in ("w4_gemv.hip", "w4_device.h"):
+        with open(os.path.join(ROOT, "weight_only_bit_unpack_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(name, launches_bytes):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def timed(fn, stream, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps  # ms per step
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import synthetic
+    import weight_only_bit_unpack_amd as w4
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    # ---------------------------------------------------------- config 2 stack
+    shapes = synthetic.llama1b_stack_shapes()
+    log(f"generating + quantizing {len(shapes)} matrices on the GPU")
+    mats = []
+    for i, (n, k) in enumerate(shapes):
+        w = synthetic.student_t_bf16_device((n, k), 4, 0.02, synthetic.seed(2, i, 0), dev)
+        x = synthetic.normal_bf16_device((1, k), 1.0, synthetic.seed(2, i, 1), dev)
+        packed, scales = w4.w4_quantize_pack(w, w4.W4_DYADIC)
+        y = torch.empty((1, n), dtype=torch.float32, device=dev)
+        mats.append({"packed": packed, "scales": scales, "x": x, "y": y, "w": w})
+    torch.cuda.synchronize()
+    n_weights = sum(n * k for n, k in shapes)
+    gemv_bytes = sum(n * k // 2 + 2 * n * (k // 64) + 2 * k + 4 * n for n, k in shapes)
+
+    batch = w4.w4_gemv_batched_plan(
+        [{k_: m[k_] for k_ in ("packed", "scales", "x", "y")} for m in mats], w4.W4_DYADIC)
+
+    log("timing the batched decode pass")
+    ms = timed(lambda: batch(stream), stream, args.steps, args.warmup)
+    gbs = gemv_bytes / (ms * 1e-3) / 1e9
+    rows = {}
+    traffic = stored_traffic("gemv_batched_dyadic_m1_llama1b_stack", gemv_bytes)
+
+    if not args.only_headline:
+        # the same pass as 168 separate calls
+        def per_call():
+            for m in mats:
+                w4.w4_gemv(m["packed"], m["x"], w4.W4_DYADIC, scales=m["scales"], y=m["y"],
+                           stream=stream)
+        ms_pc = timed(per_call, stream, max(3, args.steps // 4), 2)
+        rows["gemv_m1_stack_per_call"] = {"ms": ms_pc, "GB/s": gemv_bytes / (ms_pc * 1e-3) / 1e9,
+                                          "launches": len(shapes)}
+
+        # quantize_pack and unpack_dequant over the stack
+        q_bytes = sum(2 * n * k + n * k // 2 + 2 * n * (k // 64) for n, k in shapes)
+
+        def quant():
+            for m in mats:
+                w4.w4_quantize_pack(m["w"], w4.W4_DYADIC, packed=m["packed"], scales=m["scales"],
+                                    stream=stream)
+        ms_q = timed(quant, stream, 3, 1)
+        rows["quantize_pack_stack"] = {"ms": ms_q, "GB/s": q_bytes / (ms_q * 1e-3) / 1e9}
+
+        outs = [torch.empty((n, k), dtype=torch.bfloat16, device=dev) for n, k in shapes[:7]]
+        d_bytes = sum(n * k // 2 + 2 * n * (k // 64) + 2 * n * k for n, k in shapes[:7])
+
+        def deq():
+            for m, o in zip(mats[:7], outs):
+                w4.w4_unpack_dequant(m["packed"], w4.W4_DYADIC, scales=m["scales"], out=o,
+                                     stream=stream)
+        ms_d = timed(deq, stream, 10, 2)
+        rows["unpack_dequant_block"] = {"ms": ms_d, "GB/s": d_bytes / (ms_d * 1e-3) / 1e9,
+                                        "matrices": 7}
+        del outs
+
+    for m in mats:
+        del m["w"]
+    torch.cuda.empty_cache()
+
+    if not args.only_headline:
+        # ------------------------------------------------------ config 5 GEMM
+        log("prefill GEMM M=256, K=N=8192")
+        W = synthetic.normal_bf16_device((8192, 8192), 0.02, synthetic.seed(5, 0, 0), dev)
+        X = synthetic.normal_bf16_device((256, 8192), 1.0, synthetic.seed(5, 0, 1), dev)
+        P, S = w4.w4_quantize_pack(W, w4.W4_DYADIC)
+        Y = torch.empty((256, 8192), dtype=torch.float32, device=dev)
+        ms_g = timed(lambda: w4.w4_gemm(P, X, w4.W4_DYADIC, scales=S, y=Y, stream=stream),
+                     stream, args.steps, args.warmup)
+        flops = 2 * 256 * 8192 * 8192
+        tf = flops / (ms_g * 1e-3) / 1e12
+        rows["gemm_m256_k8192_n8192"] = {"ms": ms_g, "TFLOP/s": tf,
+                                         "frac_of_bf16_peak": tf / BF16_MFMA_PEAK_TFLOPS}
+        ms_q5 = timed(lambda: w4.w4_quantize_pack(W, w4.W4_DYADIC, packed=P, scales=S,
+                                                  stream=stream), stream, 10, 2)
+        qb = 2 * 8192 * 8192 + 8192 * 4096 + 2 * 8192 * 128
+        rows["quantize_pack_8192x8192"] = {"ms": ms_q5, "GB/s": qb / (ms_q5 * 1e-3) / 1e9}
+        xv = torch.empty((1, 8192), dtype=torch.bfloat16, device=dev).copy_(X[:1])
+        yv = torch.empty((1, 8192), dtype=torch.float32, device=dev)
+        ms_v5 = timed(lambda: w4.w4_gemv(P, xv, w4.W4_DYADIC, scales=S, y=yv, stream=stream),
+                      stream, args.steps, args.warmup)
+        vb = 8192 * 4096 + 2 * 8192 * 128 + 2 * 8192 + 4 * 8192
+        rows["gemv_m1_8192x8192"] = {"ms": ms_v5, "GB/s": vb / (ms_v5 * 1e-3) / 1e9}
+        del W, X, P, S, Y
+
+    # ---------------------------------------------------------- CPU baseline
+    cpu = None
+    if not args.no_cpu_baseline and not args.only_headline:
+        cpu = cpu_baseline(mats, shapes)
+
+    out = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "llama1b_decode_stack_w4a16_gemv_m1", "matrices": len(shapes),
+                   "weights": n_weights, "m": 1, "codec": "dyadic", "group": 64,
+                   "weight_dist": "student_t_nu4_sigma0.02", "parallelism": "none"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+        "cpu_baseline": cpu,
+        "rows": rows,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(mats, shapes):
+    """The oracle (numpy dequant + fp64 matmul, one thread) on the first block
+    of the stack (7 matrices, 51.4 M weights).  Its input is the same bf16
+    weight quantized by the oracle itself on the host."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+    from oracle import dyadic, matmul, native, packing
+
+    log("cpu baseline: oracle on the first block")
+    sample = list(range(7))
+    host = []
+    for i in sample:
+        n, k = shapes[i]
+        # regenerate the same bf16 weight on the device and copy it back
+        import synthetic
+        w = synthetic.student_t_bf16_device((n, k), 4, 0.02, synthetic.seed(2, i, 0), "cuda")
+        wb = w.view(torch.int16).cpu().numpy().view(np.uint16)
+        xb = mats[i]["x"].view(torch.int16).cpu().numpy().view(np.uint16)
+        idx, s = native.dyadic_quantize(wb)
+        host.append((packing.pack(idx), s, xb))
+        del w
+    nbytes = sum(n * k // 2 + 2 * n * (k // 64) + 2 * k + 4 * n for n, k in (shapes[i] for i in sample))
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        for p, s, xb in host:
+            w_hat = dyadic.dequant(p, s)
+            from oracle.bits import bf16_to_f64
+            matmul.gemm_ref(xb, bf16_to_f64(w_hat))
+        dt = time.perf_counter() - t0
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "first decoder block of the stack (7 matrices, 51,380,224 weights): "
+                      "numpy dequant + fp64 GEMV, one thread",
+            "seconds": round(dt, 2)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,163 @@
+/*
+ * w4.h -- C ABI of the MI355X (gfx950) group-wise 4-bit weight library.
+ *
+ * The operation comes from three pages on weight-only 4-bit quantization:
+ *
+ *  [DG]  "MiniCPM5-1B 验证: 6× 压缩 ... 50ms Triton 推理" (DyadicGumbel 4-bit):
+ *        sec. 2.1 dyadic codebook step*{-8..7} with step = scale/8;
+ *        sec. 2.2 blocks of 64 weights, one bf16 scale each, reconstruction
+ *        w = step*(idx - 8); sec. 2.3/2.5 hard argmin to a 4-bit index, two
+ *        indices per byte as (lo | hi << 4), unpack + rebuild to bf16 per layer.
+ *  [KM]  "K-Means量化技术：突破LLM低比特部署瓶颈": sec. 1.2 per-block (64)
+ *        16-centre 1D k-means codebook + 16-bit scale, nearest-centre index;
+ *        sec. 2.2 decode by table lookup; sec. 4.1 kernel choice by batch m
+ *        (a LUT kernel for m <= 16, a mixed 4-bit kernel up to 256).
+ *  [G32] "int4-g32+warm 裸量化：原理与实验报告": sec. 1.3 nearest of 8 levels
+ *        per group of 32 with a separate sign bit; sec. 2 1 sign bit + 3-bit
+ *        level index per weight, dense fp16 rebuild or a fused int4 kernel
+ *        with the 8-value codebook in registers.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Pointers are DEVICE pointers owned by the caller; the library keeps none
+ *    of them after returning and allocates no memory.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  A call only enqueues
+ *    work on it; it never synchronises the stream or the device.
+ *  - All validation happens on the host before anything is enqueued.  On any
+ *    error return nothing is enqueued and no output byte changes.  Faults in
+ *    the kernels surface at the caller's next synchronisation.
+ *  - Results are deterministic: the same inputs give the same output bits
+ *    (fixed reduction order, no atomics).
+ *  - Weights are row-major [n][k] (n = output features, k = input features,
+ *    the layout of a PyTorch Linear weight).  A group is `group` consecutive
+ *    weights along k; k must be a multiple of 64 for every codec.
+ *  - Preconditions that are not checked: finite inputs; buffers contiguous,
+ *    of the sizes stated, and not overlapping one another.
+ *
+ * Quantized weight = three planar row-major arrays
+ *   packed   uint8 [n][k/2]  nibble(r, c) = (packed[r][c/2] >> (4*(c%2))) & 15
+ *   scales   bf16  [n][k/64] DYADIC, LUT16;           NULL for SIGNMAG8
+ *   codebook LUT16:    bf16 [n][k/64][16] normalised levels L_j;
+ *            SIGNMAG8: fp16 [n][k/32][8]  magnitudes M_j;    NULL for DYADIC
+ * Reconstruction (w_hat, "dequantized weight"):
+ *   DYADIC:   w_hat = RNE_bf16((s/8) * (nib - 8))    a zero result is +0.0
+ *   LUT16:    w_hat = RNE_bf16(s * L[nib])
+ *   SIGNMAG8: w_hat = (nib & 8 ? -1 : +1) * M[nib & 7]    (fp16, exact)
+ * (RNE = round to nearest, ties to even.)
+ */
+#ifndef W4_H
+#define W4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  W4_OK = 0,
+  W4_EINVAL = 1,       /* NULL pointer for a non-empty buffer, bad enum, negative size */
+  W4_ESHAPE = 2,       /* k not a multiple of 64, m outside the call's range           */
+  W4_EALIGN = 3,       /* a pointer not aligned as the call states                      */
+  W4_EUNSUPPORTED = 4, /* a codec / dtype combination the call does not provide         */
+  W4_EHIP = 5          /* the kernel launch failed (hipGetLastError)                    */
+} w4_status;
+
+typedef enum { W4_DYADIC = 0, W4_LUT16 = 1, W4_SIGNMAG8 = 2 } w4_codec;
+typedef enum { W4_F32 = 0, W4_BF16 = 1, W4_F16 = 2 } w4_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* w4_status_str(int32_t status);
+
+/* Weights per group of a codec: 64 (DYADIC, LUT16), 32 (SIGNMAG8); -1 if unknown. */
+int32_t w4_group_size(int32_t codec);
+
+/*
+ * w4_quantize_pack -- quantize a bf16 weight [n][k] and pack two 4-bit indices
+ * per byte.  [DG] sec. 2.1-2.3, 2.5; [KM] sec. 1.2; [G32] sec. 1.3 step 4.
+ *   DYADIC:   writes scales[r][g] = max |w| over the group (a bf16 value), then
+ *             idx = the lowest j minimising |w - (s/8)(j-8)| over the exact
+ *             codes; an all-zero group gets s = +0 and idx 8.  codebook: NULL.
+ *   LUT16:    reads scales (bf16 [n][k/64]) and codebook (bf16 [n][k/64][16]);
+ *             idx = the lowest j minimising |fl32(w - s*L_j)| (fp32 decision).
+ *   SIGNMAG8: reads codebook (fp16 [n][k/32][8]); scales: NULL;
+ *             nibble = (w < 0) << 3 | the lowest j minimising |fl32(|w| - M_j)|.
+ * w: bf16 [n][k], 16-byte aligned.  packed: uint8 [n][k/2], 16-byte aligned.
+ * scales: 2-byte aligned.  codebook: 16-byte aligned.
+ * n == 0 or k == 0: nothing to do, returns W4_OK.
+ */
+w4_status w4_quantize_pack(int32_t codec, int64_t n, int64_t k, const uint16_t* w,
+                           uint8_t* packed, uint16_t* scales, const uint16_t* codebook,
+                           void* stream);
+
+/*
+ * w4_unpack_dequant -- rebuild the dense weight.  [DG] sec. 2.2, 2.5 (unpack
+ * kernel: packed byte -> nibble split -> step -> bf16); [KM] sec. 2.2 (LUT
+ * decode); [G32] sec. 2 (dense fp16 weight).
+ * out: bf16 [n][k] for DYADIC and LUT16, fp16 [n][k] for SIGNMAG8; 16-byte aligned.
+ * packed and codebook 16-byte aligned, scales 2-byte aligned.
+ */
+w4_status w4_unpack_dequant(int32_t codec, int64_t n, int64_t k, const uint8_t* packed,
+                            const uint16_t* scales, const uint16_t* codebook, void* out,
+                            void* stream);
+
+/*
+ * w4_gemv -- fused dequant + matrix-vector product for small batches,
+ * y[i][r] = sum_c x[i][c] * w_hat[r][c], accumulated in fp32.  [KM] sec. 4.1
+ * (m <= 16 goes to the LUT kernel), sec. 2.2; [G32] sec. 5.2 (fused kernel with
+ * the codebook in registers).
+ * x: bf16 [m][k], 16-byte aligned.  m: 1..16 (m == 0: nothing to do).
+ * y: [m][n] of y_dtype W4_F32 (4-byte aligned) or W4_BF16 (RNE, 2-byte aligned).
+ * The result is within 1e-3 * sum_c |x w_hat| + 1e-6 of the exact sum.
+ */
+w4_status w4_gemv(int32_t codec, int64_t n, int64_t k, const uint8_t* packed,
+                  const uint16_t* scales, const uint16_t* codebook, const uint16_t* x,
+                  int32_t m, void* y, int32_t y_dtype, void* stream);
+
+/*
+ * w4_gemm -- fused dequant + matrix product for prefill-sized batches,
+ * Y[i][r] = sum_c X[i][c] * w_hat[r][c] with bf16 MFMA and fp32 accumulation;
+ * the weight tiles are rebuilt into LDS.  [KM] sec. 4.1 (the 4-bit mixed kernel
+ * band, m up to 256).  Same arguments as w4_gemv; m >= 1 (tuned for m >= 128).
+ */
+w4_status w4_gemm(int32_t codec, int64_t n, int64_t k, const uint8_t* packed,
+                  const uint16_t* scales, const uint16_t* codebook, const uint16_t* x,
+                  int32_t m, void* y, int32_t y_dtype, void* stream);
+
+/*
+ * Batched GEMV: one launch over many independent w4_gemv problems of one codec
+ * and one m (e.g. every linear layer of a decode step whose inputs are ready).
+ * [DG] sec. 2.5 runs one unpack launch per layer, 168 per forward; one launch
+ * for all of them removes the per-launch ramp.
+ *
+ * 1. Fill a HOST array of w4_gemv_problem (tile_begin is ignored) and call
+ *    w4_gemv_batched_plan: it validates every problem exactly as w4_gemv would
+ *    and writes tile_begin (an opaque work offset) and *total_tiles.
+ * 2. Copy the planned array byte for byte into device memory (16-byte aligned).
+ * 3. Call w4_gemv_batched with that device array, any number of times.  The
+ *    kernel trusts the device copy: it must equal an array the plan accepted.
+ */
+typedef struct {
+  const uint8_t* packed;
+  const uint16_t* scales;
+  const uint16_t* codebook;
+  const uint16_t* x; /* bf16 [m][k] */
+  void* y;           /* [m][n] of the call's y_dtype */
+  int64_t n;
+  int64_t k;
+  int64_t tile_begin; /* written by w4_gemv_batched_plan */
+} w4_gemv_problem;
+
+w4_status w4_gemv_batched_plan(int32_t codec, int32_t m, int32_t y_dtype,
+                               w4_gemv_problem* problems_host, int32_t count,
+                               int64_t* total_tiles);
+
+w4_status w4_gemv_batched(int32_t codec, int32_t m, int32_t y_dtype,
+                          const w4_gemv_problem* problems_device, int32_t count,
+                          int64_t total_tiles, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4_H */

@@ -1,0 +1,100 @@
+"""CPU tests of the C ABI: the library loads, exports every function that
+include/w4.h declares, and rejects bad arguments on the host before touching
+the GPU (these calls return before any HIP call is made)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "w4.h")) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(w4_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def w4():
+    import weight_only_bit_unpack_amd as m
+    return m
+
+
+def test_header_declares_the_calls():
+    names = _declared()
+    for n in ["w4_quantize_pack", "w4_unpack_dequant", "w4_gemv", "w4_gemm",
+              "w4_gemv_batched_plan", "w4_gemv_batched", "w4_status_str", "w4_group_size"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(w4):
+    lib = ctypes.CDLL(w4.LIB_PATH)
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert set(_declared()) == set(w4.EXPORTED)
+
+
+def test_group_sizes_and_status_strings(w4):
+    assert [w4.w4_group_size(c) for c in (0, 1, 2, 7)] == [64, 64, 32, -1]
+    for s in range(6):
+        assert w4.w4_status_str(s).startswith("W4_")
+
+
+def _gemv(w4, codec=0, n=16, k=64, packed=16, scales=16, cb=16, x=16, m=1, y=16, yd=0):
+    P = lambda v: None if v is None else ctypes.c_void_p(v)
+    return w4._lib.w4_gemv(codec, n, k, P(packed), P(scales), P(cb), P(x), m, P(y), yd, None)
+
+
+def test_validation_errors(w4):
+    E = {"inval": 1, "shape": 2, "align": 3, "unsup": 4}
+    assert _gemv(w4, codec=3) == E["inval"]
+    assert _gemv(w4, n=-1) == E["inval"]
+    assert _gemv(w4, k=96) == E["shape"]
+    assert _gemv(w4, m=17) == E["shape"]
+    assert _gemv(w4, m=-1) == E["inval"]
+    assert _gemv(w4, packed=None) == E["inval"]
+    assert _gemv(w4, packed=8) == E["align"]
+    assert _gemv(w4, scales=None) == E["inval"]
+    assert _gemv(w4, scales=17) == E["align"]
+    assert _gemv(w4, codec=1, cb=None) == E["inval"]
+    assert _gemv(w4, codec=2, scales=None, cb=32 + 8) == E["align"]
+    assert _gemv(w4, x=None) == E["inval"]
+    assert _gemv(w4, x=24) == E["align"]
+    assert _gemv(w4, y=None) == E["inval"]
+    assert _gemv(w4, y=18) == E["align"]
+    assert _gemv(w4, yd=2) == E["unsup"]
+    # empty problems are accepted without touching anything
+    assert _gemv(w4, n=0, packed=None, scales=None, x=None, y=None) == 0
+    assert _gemv(w4, m=0, x=None, y=None) == 0
+
+
+def test_quantize_dequant_validation(w4):
+    q = w4._lib.w4_quantize_pack
+    d = w4._lib.w4_unpack_dequant
+    P = ctypes.c_void_p
+    assert q(0, 4, 100, P(16), P(16), P(16), None, None) == 2
+    assert q(0, 4, 64, None, P(16), P(16), None, None) == 1
+    assert q(0, 4, 64, P(8), P(16), P(16), None, None) == 3
+    assert q(0, 0, 64, None, None, None, None, None) == 0
+    assert d(1, 4, 64, P(16), P(16), None, P(16), None) == 1
+    assert d(0, 4, 64, P(16), P(16), None, None, None) == 1
+    assert d(0, 4, 64, P(16), P(16), None, P(8), None) == 3
+
+
+def test_batched_plan_validation(w4):
+    import torch
+    arr = (w4.W4Problem * 2)()
+    for i in range(2):
+        arr[i] = w4.W4Problem(16, 16, None, 16, 16, 100 + 64 * i, 128, 0)
+    total = ctypes.c_int64(-1)
+    assert w4._lib.w4_gemv_batched_plan(0, 1, 0, arr, 2, ctypes.byref(total)) == 0
+    assert total.value == 2 + 3 and arr[0].tile_begin == 0 and arr[1].tile_begin == 2
+    arr[1].k = 100
+    assert w4._lib.w4_gemv_batched_plan(0, 1, 0, arr, 2, ctypes.byref(total)) == 2
+    assert w4._lib.w4_gemv_batched_plan(0, 17, 0, arr, 2, ctypes.byref(total)) == 2
+    assert w4._lib.w4_gemv_batched(0, 1, 0, ctypes.c_void_p(8), 2, 5, None) == 3
+    assert w4._lib.w4_gemv_batched(0, 1, 0, None, 0, 0, None) == 0

@@ -1,0 +1,276 @@
+"""GPU parity: the HIP library against the CPU oracle, through the C ABI.
+
+Bit-exact for scales, packed bytes and dequantized values; GEMV / GEMM within
+|y - y_ref| <= 1e-3 * sum|x w_hat| + 1e-6 of the fp64 oracle on the same
+dequantized weights (plus one bf16 output rounding for bf16 outputs).  Sizes
+span several tiles and a ragged tail; the full-size workloads are covered in
+test_gpu_fullsize.py.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synthetic
+from oracle import bits, dyadic, lut16, matmul, native, packing, signmag8
+from tests.gpu_util import dev_bf16, dev_f16, dev_u8, host_bits, host_f32, host_u8, report
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def w4():
+    import weight_only_bit_unpack_amd as m
+    return m
+
+
+def _edge_weight(n, k, seed, huge=True):
+    """Gaussian weight with planted edge cases: an all-zero group, -0.0,
+    subnormal-scale and huge-scale groups, exact code midpoints, +-absmax.
+    huge=False keeps every scale below 2**110 so that fp32 sums of products
+    with N(0, 1) activations cannot overflow."""
+    w = synthetic.normal_bf16((n, k), 0.02, seed)
+    g = np.random.default_rng(seed)
+    if n >= 6 and k >= 128:
+        w[0, :64] = 0
+        w[0, 64:128] = 0x8000
+        w[1, :64] = (g.integers(0, 0x7F, 64) | (g.integers(0, 2, 64) << 15)).astype(np.uint16)
+        w[2, :64] = (g.integers(0x7E00, 0x7F7F, 64)).astype(np.uint16)     # scale ~ 2^125
+        if not huge:
+            w[2, :64] = (g.integers(0x7600, 0x7700, 64)).astype(np.uint16)
+        w[2, 64:128] = (g.integers(0x7600, 0x7700, 64)).astype(np.uint16)  # scale ~ 2^109
+        w[3, :64] = np.tile(np.array([0x3F80, 0xBF80, 0x3F00, 0x3E80], np.uint16), 16)
+        # midpoints (2t-15)/16 of scale 1.0, all exactly representable
+        mids = bits.rne_bf16((2 * np.arange(15) - 15) / 16.0)
+        w[4, :15] = mids
+        w[4, 15] = 0x3F80
+        w[5, 64:128] = (g.integers(0x0080, 0x0400, 64)).astype(np.uint16)  # tiny normal scale
+    return w
+
+
+# ------------------------------------------------------------------ DYADIC
+@pytest.mark.parametrize("n,k", [(2048, 2048), (37, 320), (6, 128), (1, 64)])
+def test_dyadic_quantize_pack_bitexact(w4, n, k):
+    report("dyadic_quantize", n=n, k=k)
+    w = _edge_weight(n, k, 100 + n)
+    p, s = w4.w4_quantize_pack(dev_bf16(w), w4.W4_DYADIC)
+    torch.cuda.synchronize()
+    idx_o, s_o = native.dyadic_quantize(w)
+    assert np.array_equal(host_bits(s), s_o)
+    assert np.array_equal(host_u8(p), packing.pack(idx_o))
+    if n * k <= 1 << 16:   # the numpy oracle itself on the small ones
+        p2, s2 = dyadic.quantize_pack(w)
+        assert np.array_equal(host_u8(p), p2) and np.array_equal(host_bits(s), s2)
+
+
+@pytest.mark.parametrize("n,k", [(2048, 2048), (37, 320), (6, 128)])
+def test_dyadic_dequant_bitexact(w4, n, k):
+    report("dyadic_dequant", n=n, k=k)
+    w = _edge_weight(n, k, 200 + n)
+    p_o, s_o = dyadic.quantize_pack(w) if n * k <= 1 << 16 else (None, None)
+    if p_o is None:
+        idx, s_o = native.dyadic_quantize(w)
+        p_o = packing.pack(idx)
+    out = w4.w4_unpack_dequant(dev_u8(p_o), w4.W4_DYADIC, scales=dev_bf16(s_o))
+    torch.cuda.synchronize()
+    want = native.dyadic_dequant(packing.unpack(p_o), s_o)
+    assert np.array_equal(host_bits(out), want)
+
+
+def test_dyadic_dequant_exhaustive_scales(w4):
+    """Every finite non-negative bf16 scale x every index, on the GPU."""
+    allb = bits.all_finite_bf16()
+    pos = allb[(allb & 0x8000) == 0]
+    n = len(pos)
+    idx = np.tile(np.arange(16, dtype=np.uint8), (n, 4))
+    report("dyadic_dequant_exhaustive", n=n)
+    out = w4.w4_unpack_dequant(dev_u8(packing.pack(idx)), w4.W4_DYADIC, scales=dev_bf16(pos[:, None]))
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(out), dyadic.dequant_from_indices(idx, pos[:, None]))
+
+
+def _gemv_check(y, x_bits, w_hat, bf16_out):
+    y_ref, bound = matmul.gemm_ref(x_bits, w_hat)
+    ok = matmul.within_tolerance(host_f32(y), y_ref, bound, bf16_out=bf16_out)
+    if not ok.all():
+        bad = np.argwhere(~ok)[:5]
+        raise AssertionError(f"{(~ok).sum()} outside tolerance, e.g. {bad.tolist()} "
+                             f"got {host_f32(y)[tuple(bad[0])]} want {y_ref[tuple(bad[0])]}")
+
+
+@pytest.mark.parametrize("n,k,m", [(2048, 2048, 1), (37, 320, 1), (37, 320, 3), (300, 1024, 4),
+                                   (300, 1024, 16), (64, 4096, 16), (40000, 128, 2),
+                                   (70000, 64, 1)])
+@pytest.mark.parametrize("ybf16", [False, True])
+def test_dyadic_gemv(w4, n, k, m, ybf16):
+    report("dyadic_gemv", n=n, k=k, m=m, ybf16=ybf16)
+    w = _edge_weight(n, k, 300 + n + k, huge=False)
+    idx, s = native.dyadic_quantize(w)
+    p = packing.pack(idx)
+    x = synthetic.normal_bf16((m, k), 1.0, 301 + m)
+    y = w4.w4_gemv(dev_u8(p), dev_bf16(x), w4.W4_DYADIC, scales=dev_bf16(s),
+                   y_dtype=torch.bfloat16 if ybf16 else torch.float32)
+    torch.cuda.synchronize()
+    w_hat = bits.bf16_to_f64(native.dyadic_dequant(idx, s))
+    _gemv_check(y, x, w_hat, ybf16)
+
+
+def test_dyadic_gemv_unit_vectors_exact(w4):
+    n, k = 96, 512
+    report("dyadic_gemv_unit", n=n, k=k)
+    w = _edge_weight(n, k, 401, huge=False)
+    idx, s = native.dyadic_quantize(w)
+    p = dev_u8(packing.pack(idx))
+    sd = dev_bf16(s)
+    w_hat = bits.bf16_to_f64(native.dyadic_dequant(idx, s))
+    w_hat[~np.isfinite(w_hat)] = 0
+    for col in [0, 1, 63, 64, 255, 256, 511]:
+        x = np.zeros((1, k), np.uint16)
+        x[0, col] = 0x3F80
+        y = host_f32(w4.w4_gemv(p, dev_bf16(x), w4.W4_DYADIC, scales=sd))
+        assert np.array_equal(y[0], w_hat[:, col]), col
+    # all-index-8 weights give exactly zero
+    z = w4.w4_gemv(dev_u8(np.full((n, k // 2), 0x88, np.uint8)), dev_bf16(x), w4.W4_DYADIC, scales=sd)
+    assert torch.count_nonzero(z).item() == 0
+
+
+@pytest.mark.parametrize("op", ["gemv", "gemm"])
+def test_dyadic_wide_scales(w4, op):
+    """Scales >= 2**120 take the wide rebuild; activations ~2**-20 keep the
+    fp32 sums finite."""
+    n, k = 64, 256
+    report("dyadic_wide", op=op)
+    w = _edge_weight(n, k, 402)
+    w[10:20, :] = (np.random.default_rng(3).integers(0x7C00, 0x7F7F, (10, k))
+                   | (np.random.default_rng(4).integers(0, 2, (10, k)) << 15)).astype(np.uint16)
+    idx, s = native.dyadic_quantize(w)
+    x = bits.rne_bf16(bits.bf16_to_f64(synthetic.normal_bf16((2, k), 1.0, 403)) * 2.0 ** -20)
+    fn = w4.w4_gemv if op == "gemv" else w4.w4_gemm
+    y = fn(dev_u8(packing.pack(idx)), dev_bf16(x), w4.W4_DYADIC, scales=dev_bf16(s))
+    torch.cuda.synchronize()
+    _gemv_check(y, x, bits.bf16_to_f64(native.dyadic_dequant(idx, s)), False)
+
+
+def test_dyadic_gemv_deterministic(w4):
+    n, k = 4096, 2048
+    w = synthetic.normal_bf16((n, k), 0.02, 402)
+    x = dev_bf16(synthetic.normal_bf16((1, k), 1.0, 403))
+    p, s = w4.w4_quantize_pack(dev_bf16(w), w4.W4_DYADIC)
+    a = w4.w4_gemv(p, x, w4.W4_DYADIC, scales=s)
+    b = w4.w4_gemv(p, x, w4.W4_DYADIC, scales=s)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_dyadic_gemv_batched(w4):
+    shapes = [(2048, 2048), (5632, 2048), (2048, 5632), (100, 320), (64, 64)]
+    report("dyadic_gemv_batched", count=len(shapes))
+    probs, refs = [], []
+    for i, (n, k) in enumerate(shapes):
+        w = synthetic.student_t_bf16((n, k), 4, 0.02, 500 + i)
+        x = synthetic.normal_bf16((1, k), 1.0, 600 + i)
+        idx, s = native.dyadic_quantize(w)
+        p = packing.pack(idx)
+        y = torch.full((1, n), float("nan"), device="cuda")
+        probs.append({"packed": dev_u8(p), "scales": dev_bf16(s), "x": dev_bf16(x), "y": y})
+        refs.append((x, bits.bf16_to_f64(native.dyadic_dequant(idx, s))))
+    batch = w4.w4_gemv_batched_plan(probs, w4.W4_DYADIC)
+    batch()
+    batch()
+    torch.cuda.synchronize()
+    for pr, (x, w_hat) in zip(probs, refs):
+        _gemv_check(pr["y"], x, w_hat, False)
+
+
+@pytest.mark.parametrize("n,k,m", [(200, 576, 1), (200, 576, 130), (1024, 2048, 256), (64, 64, 128)])
+def test_dyadic_gemm(w4, n, k, m):
+    report("dyadic_gemm", n=n, k=k, m=m)
+    w = _edge_weight(n, k, 700 + n, huge=False)
+    idx, s = native.dyadic_quantize(w)
+    x = synthetic.normal_bf16((m, k), 1.0, 701 + m)
+    y = w4.w4_gemm(dev_u8(packing.pack(idx)), dev_bf16(x), w4.W4_DYADIC, scales=dev_bf16(s))
+    torch.cuda.synchronize()
+    _gemv_check(y, x, bits.bf16_to_f64(native.dyadic_dequant(idx, s)), False)
+
+
+# ------------------------------------------------------------------ LUT16
+def _lut_case(n, k, seed):
+    w = synthetic.normal_outliers_bf16((n, k), 0.015, 0.001, 0.15, seed)
+    if n >= 2:
+        w[1, :64] = 0
+    s, L = native.lut16_fit(w)
+    return w, s, L
+
+
+@pytest.mark.parametrize("n,k", [(512, 1024), (37, 320)])
+def test_lut16_quantize_dequant_bitexact(w4, n, k):
+    report("lut16_quant_dequant", n=n, k=k)
+    w, s, L = _lut_case(n, k, 800 + n)
+    p, _ = w4.w4_quantize_pack(dev_bf16(w), w4.W4_LUT16, scales=dev_bf16(s), codebook=dev_bf16(L))
+    torch.cuda.synchronize()
+    idx = native.lut16_indices(w, s, L)
+    assert np.array_equal(host_u8(p), packing.pack(idx))
+    if n * k <= 1 << 16:
+        assert np.array_equal(host_u8(p), lut16.quantize_pack(w, s, L))
+    out = w4.w4_unpack_dequant(dev_u8(packing.pack(idx)), w4.W4_LUT16, scales=dev_bf16(s),
+                               codebook=dev_bf16(L))
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(out), lut16.dequant_from_indices(idx, s, L))
+
+
+@pytest.mark.parametrize("m", [1, 4, 16])
+def test_lut16_gemv_and_gemm(w4, m):
+    n, k = 300, 1024
+    report("lut16_gemv", n=n, k=k, m=m)
+    w, s, L = _lut_case(n, k, 900 + m)
+    idx = native.lut16_indices(w, s, L)
+    w_hat = bits.bf16_to_f64(lut16.dequant_from_indices(idx, s, L))
+    x = synthetic.normal_bf16((m, k), 1.0, 901 + m)
+    args = dict(scales=dev_bf16(s), codebook=dev_bf16(L))
+    y = w4.w4_gemv(dev_u8(packing.pack(idx)), dev_bf16(x), w4.W4_LUT16, **args)
+    torch.cuda.synchronize()
+    _gemv_check(y, x, w_hat, False)
+    y2 = w4.w4_gemm(dev_u8(packing.pack(idx)), dev_bf16(x), w4.W4_LUT16, **args)
+    torch.cuda.synchronize()
+    _gemv_check(y2, x, w_hat, False)
+
+
+# ------------------------------------------------------------------ SIGNMAG8
+def _sm_case(n, k, seed):
+    w = synthetic.student_t_bf16((n, k), 5, 0.02, seed)
+    w[0, 0] = 0x8000
+    cb = native.signmag8_fit(w)
+    cb[0, 1, 0] = 0
+    return w, cb
+
+
+@pytest.mark.parametrize("n,k", [(512, 1024), (37, 320)])
+def test_signmag8_quantize_dequant_bitexact(w4, n, k):
+    report("signmag8_quant_dequant", n=n, k=k)
+    w, cb = _sm_case(n, k, 1000 + n)
+    p, _ = w4.w4_quantize_pack(dev_bf16(w), w4.W4_SIGNMAG8, codebook=dev_f16(cb))
+    torch.cuda.synchronize()
+    nib = native.signmag8_indices(w, cb)
+    assert np.array_equal(host_u8(p), packing.pack(nib))
+    if n * k <= 1 << 16:
+        assert np.array_equal(host_u8(p), signmag8.quantize_pack(w, cb))
+    out = w4.w4_unpack_dequant(dev_u8(packing.pack(nib)), w4.W4_SIGNMAG8, codebook=dev_f16(cb))
+    torch.cuda.synchronize()
+    assert out.dtype == torch.float16
+    assert np.array_equal(host_bits(out), signmag8.dequant_from_indices(nib, cb))
+
+
+@pytest.mark.parametrize("m", [1, 5])
+def test_signmag8_gemv_and_gemm(w4, m):
+    n, k = 300, 1024
+    report("signmag8_gemv", n=n, k=k, m=m)
+    w, cb = _sm_case(n, k, 1100 + m)
+    nib = native.signmag8_indices(w, cb)
+    w_hat = signmag8.dequant_values(cb, nib)
+    x = synthetic.normal_bf16((m, k), 1.0, 1101 + m)
+    y = w4.w4_gemv(dev_u8(packing.pack(nib)), dev_bf16(x), w4.W4_SIGNMAG8, codebook=dev_f16(cb))
+    torch.cuda.synchronize()
+    _gemv_check(y, x, w_hat, False)
+    y2 = w4.w4_gemm(dev_u8(packing.pack(nib)), dev_bf16(x), w4.W4_SIGNMAG8, codebook=dev_f16(cb))
+    torch.cuda.synchronize()
+    _gemv_check(y2, x, w_hat, False)

@@ -1,0 +1,221 @@
+"""Python binding of libw4, the gfx950 group-wise 4-bit weight library.
+
+Argument marshalling only: every call checks device / dtype / shape of the
+torch tensors, allocates outputs with torch when the caller passes none, and
+forwards raw device pointers and the current HIP stream to the C ABI
+(``include/w4.h``), whose functions carry the same names.  All computation
+happens in the HIP kernels; there is no fallback of any kind, and importing
+this package fails if ``libw4.so`` has not been built
+(``python -m weight_only_bit_unpack_amd.build``).
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libw4.so")
+
+W4_DYADIC, W4_LUT16, W4_SIGNMAG8 = 0, 1, 2
+W4_F32, W4_BF16, W4_F16 = 0, 1, 2
+GROUP = {W4_DYADIC: 64, W4_LUT16: 64, W4_SIGNMAG8: 32}
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m weight_only_bit_unpack_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_P, _I32, _I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+
+
+class W4Problem(ctypes.Structure):
+    """Mirror of ``w4_gemv_problem``."""
+    _fields_ = [("packed", _P), ("scales", _P), ("codebook", _P), ("x", _P), ("y", _P),
+                ("n", _I64), ("k", _I64), ("tile_begin", _I64)]
+
+
+_SIGS = {
+    "w4_status_str": ([_I32], ctypes.c_char_p),
+    "w4_group_size": ([_I32], _I32),
+    "w4_quantize_pack": ([_I32, _I64, _I64, _P, _P, _P, _P, _P], _I32),
+    "w4_unpack_dequant": ([_I32, _I64, _I64, _P, _P, _P, _P, _P], _I32),
+    "w4_gemv": ([_I32, _I64, _I64, _P, _P, _P, _P, _I32, _P, _I32, _P], _I32),
+    "w4_gemm": ([_I32, _I64, _I64, _P, _P, _P, _P, _I32, _P, _I32, _P], _I32),
+    "w4_gemv_batched_plan": ([_I32, _I32, _I32, ctypes.POINTER(W4Problem), _I32,
+                              ctypes.POINTER(_I64)], _I32),
+    "w4_gemv_batched": ([_I32, _I32, _I32, _P, _I32, _I64, _P], _I32),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _res
+
+EXPORTED = tuple(_SIGS)
+
+
+class W4Error(RuntimeError):
+    def __init__(self, status):
+        self.status = status
+        super().__init__(_lib.w4_status_str(status).decode())
+
+
+def _check(status):
+    if status != 0:
+        raise W4Error(status)
+
+
+def w4_status_str(status):
+    return _lib.w4_status_str(status).decode()
+
+
+def w4_group_size(codec):
+    return _lib.w4_group_size(codec)
+
+
+# ------------------------------------------------------------------ marshalling
+_U16 = (torch.bfloat16, torch.float16, torch.int16, torch.uint16)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, name, dtypes, shape=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def _side_tables(codec, n, k, scales, codebook):
+    g = GROUP[codec]
+    if codec in (W4_DYADIC, W4_LUT16):
+        _need(scales, "scales", _U16, (n, k // 64))
+    if codec == W4_LUT16:
+        _need(codebook, "codebook", _U16, (n, k // 64, 16))
+    if codec == W4_SIGNMAG8:
+        _need(codebook, "codebook", _U16, (n, k // g, 8))
+
+
+def w4_quantize_pack(w, codec=W4_DYADIC, *, scales=None, codebook=None, packed=None,
+                     stream=None):
+    """Quantize a bf16 weight [n, k] and pack two 4-bit indices per byte.
+
+    DYADIC writes ``scales`` (allocated if None); LUT16 reads ``scales`` and
+    ``codebook``; SIGNMAG8 reads ``codebook``.  Returns (packed, scales)."""
+    _need(w, "w", _U16)
+    n, k = w.shape
+    if packed is None:
+        packed = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
+    _need(packed, "packed", (torch.uint8,), (n, k // 2))
+    if codec == W4_DYADIC and scales is None:
+        scales = torch.empty((n, k // 64), dtype=torch.bfloat16, device=w.device)
+    _side_tables(codec, n, k, scales, codebook)
+    _check(_lib.w4_quantize_pack(codec, n, k, _ptr(w), _ptr(packed), _ptr(scales),
+                                 _ptr(codebook), _stream(stream)))
+    return packed, scales
+
+
+def w4_unpack_dequant(packed, codec=W4_DYADIC, *, scales=None, codebook=None, out=None,
+                      stream=None):
+    """Dense rebuilt weight: bf16 [n, k] (DYADIC, LUT16) or fp16 (SIGNMAG8)."""
+    _need(packed, "packed", (torch.uint8,))
+    n, k2 = packed.shape
+    k = 2 * k2
+    _side_tables(codec, n, k, scales, codebook)
+    dt = torch.float16 if codec == W4_SIGNMAG8 else torch.bfloat16
+    if out is None:
+        out = torch.empty((n, k), dtype=dt, device=packed.device)
+    _need(out, "out", _U16, (n, k))
+    _check(_lib.w4_unpack_dequant(codec, n, k, _ptr(packed), _ptr(scales), _ptr(codebook),
+                                  _ptr(out), _stream(stream)))
+    return out
+
+
+def _matmul(fn, packed, x, codec, scales, codebook, y, y_dtype, stream):
+    _need(packed, "packed", (torch.uint8,))
+    n, k2 = packed.shape
+    k = 2 * k2
+    _side_tables(codec, n, k, scales, codebook)
+    _need(x, "x", _U16)
+    if x.dim() != 2 or x.shape[1] != k:
+        raise ValueError(f"x must be [m, {k}]")
+    m = x.shape[0]
+    code = W4_BF16 if y_dtype == torch.bfloat16 else W4_F32
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.bfloat16 if code == W4_BF16 else torch.float32,
+                        device=packed.device)
+    _need(y, "y", (torch.float32,) if code == W4_F32 else _U16, (m, n))
+    _check(fn(codec, n, k, _ptr(packed), _ptr(scales), _ptr(codebook), _ptr(x), m, _ptr(y),
+              code, _stream(stream)))
+    return y
+
+
+def w4_gemv(packed, x, codec=W4_DYADIC, *, scales=None, codebook=None, y=None,
+            y_dtype=torch.float32, stream=None):
+    """y[m, n] = x[m, k] @ w_hat[n, k]^T for 1 <= m <= 16 (fused dequant)."""
+    return _matmul(_lib.w4_gemv, packed, x, codec, scales, codebook, y, y_dtype, stream)
+
+
+def w4_gemm(packed, x, codec=W4_DYADIC, *, scales=None, codebook=None, y=None,
+            y_dtype=torch.float32, stream=None):
+    """Y[m, n] = X[m, k] @ w_hat[n, k]^T, bf16 MFMA (fused dequant), any m >= 1."""
+    return _matmul(_lib.w4_gemm, packed, x, codec, scales, codebook, y, y_dtype, stream)
+
+
+class W4GemvBatch:
+    """A planned batch of independent GEMVs (``w4_gemv_batched_plan``), with
+    its descriptor table already in device memory.  Call it to launch."""
+
+    def __init__(self, codec, m, y_dtype, table_dev, count, total_tiles, keepalive):
+        self.codec, self.m, self.y_dtype = codec, m, y_dtype
+        self.table, self.count, self.total_tiles = table_dev, count, total_tiles
+        self._keep = keepalive
+
+    def __call__(self, stream=None):
+        _check(_lib.w4_gemv_batched(self.codec, self.m, self.y_dtype,
+                                    ctypes.c_void_p(self.table.data_ptr()), self.count,
+                                    self.total_tiles, _stream(stream)))
+
+
+def w4_gemv_batched_plan(problems, codec=W4_DYADIC, y_dtype=torch.float32):
+    """problems: list of dicts with packed, x, y and scales / codebook as the
+    codec needs.  Validates all of them, uploads the descriptor table and
+    returns a W4GemvBatch."""
+    code = W4_BF16 if y_dtype == torch.bfloat16 else W4_F32
+    arr = (W4Problem * len(problems))()
+    m = None
+    keep = []
+    for i, p in enumerate(problems):
+        packed, x, y = p["packed"], p["x"], p["y"]
+        _need(packed, "packed", (torch.uint8,))
+        n, k = packed.shape[0], 2 * packed.shape[1]
+        _side_tables(codec, n, k, p.get("scales"), p.get("codebook"))
+        _need(x, "x", _U16, (x.shape[0], k))
+        _need(y, "y", (torch.float32,) if code == W4_F32 else _U16, (x.shape[0], n))
+        if m is None:
+            m = x.shape[0]
+        elif x.shape[0] != m:
+            raise ValueError("all problems of a batch share m")
+        arr[i] = W4Problem(packed.data_ptr(), _ptr(p.get("scales")), _ptr(p.get("codebook")),
+                           x.data_ptr(), y.data_ptr(), n, k, 0)
+        keep.append(p)
+    total = _I64(0)
+    _check(_lib.w4_gemv_batched_plan(codec, m or 1, code, arr, len(problems), ctypes.byref(total)))
+    raw = bytes(arr)
+    dev = problems[0]["packed"].device if problems else torch.device("cuda")
+    table = torch.frombuffer(bytearray(raw), dtype=torch.uint8).to(dev)
+    return W4GemvBatch(codec, m or 1, code, table, len(problems), total.value, keep)

@@ -1,0 +1,182 @@
+// C ABI of libw4 (declared in include/w4.h): argument validation on the host,
+// then one kernel launch on the caller's stream.  Nothing is allocated,
+// nothing is synchronised, and an error return leaves every buffer untouched.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "w4.h"
+#include "w4_launch.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool valid_codec(int32_t c) { return c == W4_DYADIC || c == W4_LUT16 || c == W4_SIGNMAG8; }
+
+// Checks the quantized-weight triple of a codec for an [n][k] weight.
+w4_status check_weight(int32_t codec, int64_t n, int64_t k, const void* packed, const void* scales,
+                       const void* codebook) {
+  if (!valid_codec(codec)) return W4_EINVAL;
+  if (n < 0 || k < 0) return W4_EINVAL;
+  if (k % 64) return W4_ESHAPE;
+  if (n == 0 || k == 0) return W4_OK;
+  if (!packed) return W4_EINVAL;
+  if (!aligned(packed, 16)) return W4_EALIGN;
+  if (codec == W4_DYADIC || codec == W4_LUT16) {
+    if (!scales) return W4_EINVAL;
+    if (!aligned(scales, 2)) return W4_EALIGN;
+  }
+  if (codec == W4_LUT16 || codec == W4_SIGNMAG8) {
+    if (!codebook) return W4_EINVAL;
+    if (!aligned(codebook, 16)) return W4_EALIGN;
+  }
+  return W4_OK;
+}
+
+w4_status check_matmul(int32_t codec, int64_t n, int64_t k, const uint8_t* packed,
+                       const uint16_t* scales, const uint16_t* codebook, const uint16_t* x,
+                       int32_t m, void* y, int32_t y_dtype, int32_t m_max) {
+  w4_status st = check_weight(codec, n, k, packed, scales, codebook);
+  if (st != W4_OK) return st;
+  if (m < 0) return W4_EINVAL;
+  if (m > m_max) return W4_ESHAPE;
+  if (y_dtype != W4_F32 && y_dtype != W4_BF16) return W4_EUNSUPPORTED;
+  if (m == 0 || n == 0) return W4_OK;
+  if (!y) return W4_EINVAL;
+  if (!aligned(y, y_dtype == W4_F32 ? 4 : 2)) return W4_EALIGN;
+  if (k > 0) {
+    if (!x) return W4_EINVAL;
+    if (!aligned(x, 16)) return W4_EALIGN;
+  }
+  return W4_OK;
+}
+
+w4_status launched(hipError_t e) { return e == hipSuccess ? W4_OK : W4_EHIP; }
+
+w4::GemvProblem problem(int64_t n, int64_t k, const uint8_t* packed, const uint16_t* scales,
+                        const uint16_t* codebook, const uint16_t* x, void* y) {
+  w4::GemvProblem p;
+  p.packed = packed;
+  p.scales = scales;
+  p.codebook = codebook;
+  p.x = x;
+  p.y = y;
+  p.n = n;
+  p.k = k;
+  p.tile_begin = 0;
+  return p;
+}
+
+constexpr int32_t kGemvMaxM = 16;
+constexpr int32_t kGemmMaxM = 65535 * 128;
+
+}  // namespace
+
+static_assert(sizeof(w4_gemv_problem) == sizeof(w4::GemvProblem), "problem layout");
+
+extern "C" {
+
+const char* w4_status_str(int32_t status) {
+  switch (status) {
+    case W4_OK: return "W4_OK";
+    case W4_EINVAL: return "W4_EINVAL: null pointer, bad enum or negative size";
+    case W4_ESHAPE: return "W4_ESHAPE: k not a multiple of 64 or m out of range";
+    case W4_EALIGN: return "W4_EALIGN: pointer not aligned as required";
+    case W4_EUNSUPPORTED: return "W4_EUNSUPPORTED: codec / dtype combination not provided";
+    case W4_EHIP: return "W4_EHIP: kernel launch failed";
+    default: return "unknown w4 status";
+  }
+}
+
+int32_t w4_group_size(int32_t codec) {
+  switch (codec) {
+    case W4_DYADIC: return 64;
+    case W4_LUT16: return 64;
+    case W4_SIGNMAG8: return 32;
+    default: return -1;
+  }
+}
+
+w4_status w4_quantize_pack(int32_t codec, int64_t n, int64_t k, const uint16_t* w,
+                           uint8_t* packed, uint16_t* scales, const uint16_t* codebook,
+                           void* stream) {
+  w4_status st = check_weight(codec, n, k, packed, scales, codebook);
+  if (st != W4_OK) return st;
+  if (n == 0 || k == 0) return W4_OK;
+  if (!w) return W4_EINVAL;
+  if (!aligned(w, 16)) return W4_EALIGN;
+  return launched(w4::launch_quantize(codec, n, k, w, packed, scales, codebook,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+w4_status w4_unpack_dequant(int32_t codec, int64_t n, int64_t k, const uint8_t* packed,
+                            const uint16_t* scales, const uint16_t* codebook, void* out,
+                            void* stream) {
+  w4_status st = check_weight(codec, n, k, packed, scales, codebook);
+  if (st != W4_OK) return st;
+  if (n == 0 || k == 0) return W4_OK;
+  if (!out) return W4_EINVAL;
+  if (!aligned(out, 16)) return W4_EALIGN;
+  return launched(w4::launch_dequant(codec, n, k, packed, scales, codebook, out,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+w4_status w4_gemv(int32_t codec, int64_t n, int64_t k, const uint8_t* packed,
+                  const uint16_t* scales, const uint16_t* codebook, const uint16_t* x,
+                  int32_t m, void* y, int32_t y_dtype, void* stream) {
+  w4_status st = check_matmul(codec, n, k, packed, scales, codebook, x, m, y, y_dtype, kGemvMaxM);
+  if (st != W4_OK) return st;
+  if (m == 0 || n == 0) return W4_OK;
+  return launched(w4::launch_gemv(codec, problem(n, k, packed, scales, codebook, x, y), m,
+                                  y_dtype == W4_BF16, static_cast<hipStream_t>(stream)));
+}
+
+w4_status w4_gemm(int32_t codec, int64_t n, int64_t k, const uint8_t* packed,
+                  const uint16_t* scales, const uint16_t* codebook, const uint16_t* x,
+                  int32_t m, void* y, int32_t y_dtype, void* stream) {
+  w4_status st = check_matmul(codec, n, k, packed, scales, codebook, x, m, y, y_dtype, kGemmMaxM);
+  if (st != W4_OK) return st;
+  if (m == 0 || n == 0) return W4_OK;
+  return launched(w4::launch_gemm(codec, problem(n, k, packed, scales, codebook, x, y), m,
+                                  y_dtype == W4_BF16, static_cast<hipStream_t>(stream)));
+}
+
+w4_status w4_gemv_batched_plan(int32_t codec, int32_t m, int32_t y_dtype,
+                               w4_gemv_problem* problems, int32_t count, int64_t* total_tiles) {
+  if (!total_tiles || count < 0 || (count > 0 && !problems)) return W4_EINVAL;
+  if (!valid_codec(codec)) return W4_EINVAL;
+  if (m < 1) return m < 0 ? W4_EINVAL : W4_ESHAPE;
+  const int64_t rows = w4::gemv_rows_per_block(1);
+  int64_t total = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    const w4_gemv_problem& p = problems[i];
+    w4_status st = check_matmul(codec, p.n, p.k, p.packed, p.scales, p.codebook, p.x, m, p.y,
+                                y_dtype, kGemvMaxM);
+    if (st != W4_OK) return st;
+  }
+  for (int32_t i = 0; i < count; ++i) {
+    problems[i].tile_begin = total;
+    total += (problems[i].n + rows - 1) / rows;
+  }
+  if (total > 0x7FFFFFFF) return W4_ESHAPE;
+  *total_tiles = total;
+  return W4_OK;
+}
+
+w4_status w4_gemv_batched(int32_t codec, int32_t m, int32_t y_dtype,
+                          const w4_gemv_problem* problems_device, int32_t count,
+                          int64_t total_tiles, void* stream) {
+  if (!valid_codec(codec) || count < 0 || total_tiles < 0) return W4_EINVAL;
+  if (m < 1) return m < 0 ? W4_EINVAL : W4_ESHAPE;
+  if (m > kGemvMaxM) return W4_ESHAPE;
+  if (y_dtype != W4_F32 && y_dtype != W4_BF16) return W4_EUNSUPPORTED;
+  if (count == 0 || total_tiles == 0) return W4_OK;
+  if (!problems_device) return W4_EINVAL;
+  if (!aligned(problems_device, 16)) return W4_EALIGN;
+  if (total_tiles > 0x7FFFFFFF) return W4_ESHAPE;
+  return launched(w4::launch_gemv_batched(
+      codec, reinterpret_cast<const w4::GemvProblem*>(problems_device), count, total_tiles, m,
+      y_dtype == W4_BF16, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,41 @@
+// Host-side launchers of the gfx950 kernels (internal to libw4; the public
+// ABI is include/w4.h).  Arguments are validated by w4_api.cpp before any of
+// these is called; each launcher only enqueues on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4 {
+
+// Same layout as w4_gemv_problem in include/w4.h.
+struct GemvProblem {
+  const uint8_t* packed;
+  const uint16_t* scales;
+  const uint16_t* codebook;
+  const uint16_t* x;
+  void* y;
+  int64_t n;
+  int64_t k;
+  int64_t tile_begin;
+};
+
+hipError_t launch_quantize(int codec, int64_t n, int64_t k, const uint16_t* w, uint8_t* packed,
+                           uint16_t* scales, const uint16_t* codebook, hipStream_t stream);
+
+hipError_t launch_dequant(int codec, int64_t n, int64_t k, const uint8_t* packed,
+                          const uint16_t* scales, const uint16_t* codebook, void* out,
+                          hipStream_t stream);
+
+// rows of one GEMV block for a given k-split (the batched plan uses it too)
+int gemv_rows_per_block(int ksplit);
+int gemv_pick_ksplit(int64_t n, int64_t k, int m);
+
+hipError_t launch_gemv(int codec, const GemvProblem& p, int m, int y_bf16, hipStream_t stream);
+
+hipError_t launch_gemv_batched(int codec, const GemvProblem* probs_dev, int count,
+                               int64_t total_blocks, int m, int y_bf16, hipStream_t stream);
+
+hipError_t launch_gemm(int codec, const GemvProblem& p, int m, int y_bf16, hipStream_t stream);
+
+}  // namespace w4

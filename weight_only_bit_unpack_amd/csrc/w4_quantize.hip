@@ -1,0 +1,200 @@
+// Quantize + pack kernels (gfx950).
+//
+// DyadicGumbel page, sections 2.1-2.3 and 2.5: per group of 64 weights a bf16
+// scale (the group absmax here) and for each weight the hard argmin over the
+// 16 codes (scale/8)*(j-8); two 4-bit indices per byte, low nibble first.
+// k-means page, section 1.2: nearest of the group's 16 LUT levels.
+// int4-g32 page, sections 1.3 and 2: sign bit + nearest of 8 magnitudes.
+//
+// One thread handles 8 consecutive weights (one 16-byte load, one 4-byte
+// packed store); a 64-weight group is 8 adjacent lanes, so the group absmax
+// is three DPP steps inside the lane octet.  Rows hold whole groups (k is a
+// multiple of 64), so the weight is processed as a flat array.
+#include "w4_device.h"
+#include "w4_launch.h"
+
+namespace w4 {
+namespace {
+
+// DPP lane moves (all lanes of an octet are active whenever these run).
+__device__ __forceinline__ float dpp_quad_xor1(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_quad_xor2(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                0x4E, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_half_mirror(float v) {  // lane i <-> 7 - i within 8 lanes
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                0x141, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ void unpack8(const u32x4& v, float f[8]) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+    f[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xFFFF0000u);
+  }
+}
+
+// idx = #{t in 0..14 : w > (2t - 15) * s/16}: the number of midpoints between
+// adjacent codes that lie strictly below w (ties go to the lower index).
+// Every (2t-15)*s/16 is exact in fp32 (<= 12 significant bits, no overflow
+// since it is below s), so each comparison is exact.
+__device__ __forceinline__ uint32_t dyadic_idx_exact(float w, float s16) {
+  uint32_t c = 0;
+#pragma unroll
+  for (int t = 0; t < 15; ++t) c += (w > (float)(2 * t - 15) * s16) ? 1u : 0u;
+  return c;
+}
+
+// Same count, found from an estimate that is off by at most one and then
+// checked against the two exact midpoints around it.
+__device__ __forceinline__ uint32_t dyadic_idx_fast(float w, float inv8, float s8, float s16) {
+  const float z = w * inv8;  // ~ 8 w / s, relative error ~2^-23
+  int i0 = (int)__builtin_ceilf(z + 7.5f);
+  i0 = i0 < 0 ? 0 : (i0 > 15 ? 15 : i0);
+  const float mlo = (float)(2 * i0 - 17) * s16;  // midpoint below code i0
+  const float mhi = mlo + s8;                    // midpoint above code i0 (exact)
+  int i = i0 - (w <= mlo ? 1 : 0) + (w > mhi ? 1 : 0);
+  return (uint32_t)(i > 15 ? 15 : i);
+}
+
+__global__ __launch_bounds__(256) void quantize_dyadic_kernel(const u32x4* __restrict__ w,
+                                                              uint32_t* __restrict__ packed,
+                                                              uint16_t* __restrict__ scales,
+                                                              int64_t nchunks) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const bool live = c < nchunks;
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (live) v = __builtin_nontemporal_load(&w[c]);
+  float f[8];
+  unpack8(v, f);
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a = __builtin_fmaxf(a, __builtin_fabsf(f[i]));
+  a = __builtin_fmaxf(a, dpp_quad_xor1(a));
+  a = __builtin_fmaxf(a, dpp_quad_xor2(a));
+  a = __builtin_fmaxf(a, dpp_half_mirror(a));
+  const float s = a;  // group absmax: a bf16 value, exact in fp32
+  const float s8 = s * 0.125f, s16 = s * 0.0625f;
+  uint32_t word = 0x88888888u;  // all-zero group: index 8 everywhere
+  const bool tiny = s < 0x1p-120f;  // 8/s would overflow: use the direct count
+  if (__builtin_expect(__any(tiny && s != 0.0f), 0)) {
+    if (s != 0.0f) {
+      word = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) word |= dyadic_idx_exact(f[i], s16) << (4 * i);
+    }
+  } else if (s != 0.0f) {
+    const float inv8 = 8.0f / s;
+    word = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) word |= dyadic_idx_fast(f[i], inv8, s8, s16) << (4 * i);
+  }
+  if (live) {
+    packed[c] = word;
+    if ((c & 7) == 0) scales[c >> 3] = (uint16_t)(__builtin_bit_cast(uint32_t, s) >> 16);
+  }
+}
+
+// LUT16: levels v_j = s * L_j (exact in fp32); index = lowest j minimising
+// |fl32(w - v_j)|.
+__global__ __launch_bounds__(256) void quantize_lut16_kernel(const u32x4* __restrict__ w,
+                                                             uint32_t* __restrict__ packed,
+                                                             const uint16_t* __restrict__ scales,
+                                                             const u32x4* __restrict__ lut,
+                                                             int64_t nchunks) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= nchunks) return;
+  const int64_t g = c >> 3;
+  const u32x4 v = __builtin_nontemporal_load(&w[c]);
+  const float s = bf16_bits_to_f32(scales[g]);
+  const u32x4 l0 = lut[2 * g], l1 = lut[2 * g + 1];
+  const uint32_t lw[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+  float lv[16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    lv[2 * i] = bf16_bits_to_f32(lw[i] & 0xFFFFu) * s;
+    lv[2 * i + 1] = __builtin_bit_cast(float, lw[i] & 0xFFFF0000u) * s;
+  }
+  float f[8];
+  unpack8(v, f);
+  uint32_t word = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float best = __builtin_fabsf(f[i] - lv[0]);
+    uint32_t bi = 0;
+#pragma unroll
+    for (int j = 1; j < 16; ++j) {
+      const float d = __builtin_fabsf(f[i] - lv[j]);
+      if (d < best) {
+        best = d;
+        bi = (uint32_t)j;
+      }
+    }
+    word |= bi << (4 * i);
+  }
+  packed[c] = word;
+}
+
+// SIGNMAG8: nibble = (w < 0) << 3 | lowest j minimising |fl32(|w| - M_j)|.
+__global__ __launch_bounds__(256) void quantize_signmag8_kernel(const u32x4* __restrict__ w,
+                                                                uint32_t* __restrict__ packed,
+                                                                const u32x4* __restrict__ cb,
+                                                                int64_t nchunks) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= nchunks) return;
+  const u32x4 v = __builtin_nontemporal_load(&w[c]);
+  const u32x4 m = cb[c >> 2];  // group of 32 = 4 chunks
+  const uint32_t mw[4] = {m.x, m.y, m.z, m.w};
+  float mv[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f16x2 h = __builtin_bit_cast(f16x2, mw[i]);
+    mv[2 * i] = (float)h.x;
+    mv[2 * i + 1] = (float)h.y;
+  }
+  float f[8];
+  unpack8(v, f);
+  uint32_t word = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float a = __builtin_fabsf(f[i]);
+    float best = __builtin_fabsf(a - mv[0]);
+    uint32_t bi = 0;
+#pragma unroll
+    for (int j = 1; j < 8; ++j) {
+      const float d = __builtin_fabsf(a - mv[j]);
+      if (d < best) {
+        best = d;
+        bi = (uint32_t)j;
+      }
+    }
+    word |= ((f[i] < 0.0f ? 8u : 0u) | bi) << (4 * i);
+  }
+  packed[c] = word;
+}
+
+}  // namespace
+
+hipError_t launch_quantize(int codec, int64_t n, int64_t k, const uint16_t* w, uint8_t* packed,
+                           uint16_t* scales, const uint16_t* codebook, hipStream_t stream) {
+  const int64_t nchunks = n * k / 8;
+  const int64_t blocks = (nchunks + 255) / 256;
+  const auto* wv = reinterpret_cast<const u32x4*>(w);
+  auto* pk = reinterpret_cast<uint32_t*>(packed);
+  if (codec == 0)
+    quantize_dyadic_kernel<<<dim3((uint32_t)blocks), dim3(256), 0, stream>>>(wv, pk, scales, nchunks);
+  else if (codec == 1)
+    quantize_lut16_kernel<<<dim3((uint32_t)blocks), dim3(256), 0, stream>>>(
+        wv, pk, scales, reinterpret_cast<const u32x4*>(codebook), nchunks);
+  else
+    quantize_signmag8_kernel<<<dim3((uint32_t)blocks), dim3(256), 0, stream>>>(
+        wv, pk, reinterpret_cast<const u32x4*>(codebook), nchunks);
+  return hipGetLastError();
+}
+
+}  // namespace w4

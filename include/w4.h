@@ -132,10 +132,12 @@ w4_status w4_gemm(int32_t codec, int64_t n, int64_t k, const uint8_t* packed,
  *
  * 1. Fill a HOST array of w4_gemv_problem (tile_begin is ignored) and call
  *    w4_gemv_batched_plan: it validates every problem exactly as w4_gemv would
- *    and writes tile_begin (an opaque work offset) and *total_tiles.
+ *    and writes tile_begin (an opaque work offset), *total_tiles and *k_max
+ *    (the largest k, which sizes the kernel's LDS).
  * 2. Copy the planned array byte for byte into device memory (16-byte aligned).
- * 3. Call w4_gemv_batched with that device array, any number of times.  The
- *    kernel trusts the device copy: it must equal an array the plan accepted.
+ * 3. Call w4_gemv_batched with that device array, total_tiles and k_max, any
+ *    number of times.  The kernel trusts the device copy: it must equal an
+ *    array the plan accepted.
  */
 typedef struct {
   const uint8_t* packed;
@@ -150,11 +152,11 @@ typedef struct {
 
 w4_status w4_gemv_batched_plan(int32_t codec, int32_t m, int32_t y_dtype,
                                w4_gemv_problem* problems_host, int32_t count,
-                               int64_t* total_tiles);
+                               int64_t* total_tiles, int64_t* k_max);
 
 w4_status w4_gemv_batched(int32_t codec, int32_t m, int32_t y_dtype,
                           const w4_gemv_problem* problems_device, int32_t count,
-                          int64_t total_tiles, void* stream);
+                          int64_t total_tiles, int64_t k_max, void* stream);
 
 #ifdef __cplusplus
 }

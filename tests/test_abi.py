@@ -90,11 +90,15 @@ def test_batched_plan_validation(w4):
     arr = (w4.W4Problem * 2)()
     for i in range(2):
         arr[i] = w4.W4Problem(16, 16, None, 16, 16, 100 + 64 * i, 128, 0)
-    total = ctypes.c_int64(-1)
-    assert w4._lib.w4_gemv_batched_plan(0, 1, 0, arr, 2, ctypes.byref(total)) == 0
+    total, kmax = ctypes.c_int64(-1), ctypes.c_int64(-1)
+    plan = lambda m: w4._lib.w4_gemv_batched_plan(0, m, 0, arr, 2, ctypes.byref(total),
+                                                   ctypes.byref(kmax))
+    assert plan(1) == 0
     assert total.value == 2 + 3 and arr[0].tile_begin == 0 and arr[1].tile_begin == 2
+    assert kmax.value == 128
     arr[1].k = 100
-    assert w4._lib.w4_gemv_batched_plan(0, 1, 0, arr, 2, ctypes.byref(total)) == 2
-    assert w4._lib.w4_gemv_batched_plan(0, 17, 0, arr, 2, ctypes.byref(total)) == 2
-    assert w4._lib.w4_gemv_batched(0, 1, 0, ctypes.c_void_p(8), 2, 5, None) == 3
-    assert w4._lib.w4_gemv_batched(0, 1, 0, None, 0, 0, None) == 0
+    assert plan(1) == 2
+    assert plan(17) == 2
+    assert w4._lib.w4_gemv_batched(0, 1, 0, ctypes.c_void_p(8), 2, 5, 128, None) == 3
+    assert w4._lib.w4_gemv_batched(0, 1, 0, ctypes.c_void_p(16), 2, 5, -1, None) == 1
+    assert w4._lib.w4_gemv_batched(0, 1, 0, None, 0, 0, 0, None) == 0

@@ -43,8 +43,8 @@ _SIGS = {
     "w4_gemv": ([_I32, _I64, _I64, _P, _P, _P, _P, _I32, _P, _I32, _P], _I32),
     "w4_gemm": ([_I32, _I64, _I64, _P, _P, _P, _P, _I32, _P, _I32, _P], _I32),
     "w4_gemv_batched_plan": ([_I32, _I32, _I32, ctypes.POINTER(W4Problem), _I32,
-                              ctypes.POINTER(_I64)], _I32),
-    "w4_gemv_batched": ([_I32, _I32, _I32, _P, _I32, _I64, _P], _I32),
+                              ctypes.POINTER(_I64), ctypes.POINTER(_I64)], _I32),
+    "w4_gemv_batched": ([_I32, _I32, _I32, _P, _I32, _I64, _I64, _P], _I32),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -180,15 +180,16 @@ class W4GemvBatch:
     """A planned batch of independent GEMVs (``w4_gemv_batched_plan``), with
     its descriptor table already in device memory.  Call it to launch."""
 
-    def __init__(self, codec, m, y_dtype, table_dev, count, total_tiles, keepalive):
+    def __init__(self, codec, m, y_dtype, table_dev, count, total_tiles, k_max, keepalive):
         self.codec, self.m, self.y_dtype = codec, m, y_dtype
         self.table, self.count, self.total_tiles = table_dev, count, total_tiles
+        self.k_max = k_max
         self._keep = keepalive
 
     def __call__(self, stream=None):
         _check(_lib.w4_gemv_batched(self.codec, self.m, self.y_dtype,
                                     ctypes.c_void_p(self.table.data_ptr()), self.count,
-                                    self.total_tiles, _stream(stream)))
+                                    self.total_tiles, self.k_max, _stream(stream)))
 
 
 def w4_gemv_batched_plan(problems, codec=W4_DYADIC, y_dtype=torch.float32):
@@ -213,9 +214,10 @@ def w4_gemv_batched_plan(problems, codec=W4_DYADIC, y_dtype=torch.float32):
         arr[i] = W4Problem(packed.data_ptr(), _ptr(p.get("scales")), _ptr(p.get("codebook")),
                            x.data_ptr(), y.data_ptr(), n, k, 0)
         keep.append(p)
-    total = _I64(0)
-    _check(_lib.w4_gemv_batched_plan(codec, m or 1, code, arr, len(problems), ctypes.byref(total)))
+    total, kmax = _I64(0), _I64(0)
+    _check(_lib.w4_gemv_batched_plan(codec, m or 1, code, arr, len(problems), ctypes.byref(total),
+                                     ctypes.byref(kmax)))
     raw = bytes(arr)
     dev = problems[0]["packed"].device if problems else torch.device("cuda")
     table = torch.frombuffer(bytearray(raw), dtype=torch.uint8).to(dev)
-    return W4GemvBatch(codec, m or 1, code, table, len(problems), total.value, keep)
+    return W4GemvBatch(codec, m or 1, code, table, len(problems), total.value, kmax.value, keep)

@@ -142,8 +142,9 @@ w4_status w4_gemm(int32_t codec, int64_t n, int64_t k, const uint8_t* packed,
 }
 
 w4_status w4_gemv_batched_plan(int32_t codec, int32_t m, int32_t y_dtype,
-                               w4_gemv_problem* problems, int32_t count, int64_t* total_tiles) {
-  if (!total_tiles || count < 0 || (count > 0 && !problems)) return W4_EINVAL;
+                               w4_gemv_problem* problems, int32_t count, int64_t* total_tiles,
+                               int64_t* k_max) {
+  if (!total_tiles || !k_max || count < 0 || (count > 0 && !problems)) return W4_EINVAL;
   if (!valid_codec(codec)) return W4_EINVAL;
   if (m < 1) return m < 0 ? W4_EINVAL : W4_ESHAPE;
   const int64_t rows = w4::gemv_rows_per_block(1);
@@ -154,19 +155,26 @@ w4_status w4_gemv_batched_plan(int32_t codec, int32_t m, int32_t y_dtype,
                                 y_dtype, kGemvMaxM);
     if (st != W4_OK) return st;
   }
+  int64_t kmax = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    if (problems[i].k > kmax) kmax = problems[i].k;
+    total += (problems[i].n + rows - 1) / rows;
+  }
+  if (total > 0x7FFFFFFF) return W4_ESHAPE;
+  total = 0;
   for (int32_t i = 0; i < count; ++i) {
     problems[i].tile_begin = total;
     total += (problems[i].n + rows - 1) / rows;
   }
-  if (total > 0x7FFFFFFF) return W4_ESHAPE;
   *total_tiles = total;
+  *k_max = kmax;
   return W4_OK;
 }
 
 w4_status w4_gemv_batched(int32_t codec, int32_t m, int32_t y_dtype,
                           const w4_gemv_problem* problems_device, int32_t count,
-                          int64_t total_tiles, void* stream) {
-  if (!valid_codec(codec) || count < 0 || total_tiles < 0) return W4_EINVAL;
+                          int64_t total_tiles, int64_t k_max, void* stream) {
+  if (!valid_codec(codec) || count < 0 || total_tiles < 0 || k_max < 0) return W4_EINVAL;
   if (m < 1) return m < 0 ? W4_EINVAL : W4_ESHAPE;
   if (m > kGemvMaxM) return W4_ESHAPE;
   if (y_dtype != W4_F32 && y_dtype != W4_BF16) return W4_EUNSUPPORTED;
@@ -175,8 +183,8 @@ w4_status w4_gemv_batched(int32_t codec, int32_t m, int32_t y_dtype,
   if (!aligned(problems_device, 16)) return W4_EALIGN;
   if (total_tiles > 0x7FFFFFFF) return W4_ESHAPE;
   return launched(w4::launch_gemv_batched(
-      codec, reinterpret_cast<const w4::GemvProblem*>(problems_device), count, total_tiles, m,
-      y_dtype == W4_BF16, static_cast<hipStream_t>(stream)));
+      codec, reinterpret_cast<const w4::GemvProblem*>(problems_device), count, total_tiles,
+      k_max, m, y_dtype == W4_BF16, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -28,21 +28,61 @@
 namespace w4 {
 namespace {
 
-constexpr int kXsUnits = 2048;  // 32 KiB of LDS for staged activations (16-byte units)
+constexpr int kXsUnitsMax = 2048;  // at most 32 KiB of LDS for staged activations (16-byte units)
 
+// Buffer resources (V#) over one block's slice of an array: loads at an
+// offset outside [0, num_records) return zero without touching memory, so
+// rows past n and k past the end need no branches, and the compiler can
+// keep prefetched loads in flight across the loop (vmcnt stays exact).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+constexpr uint32_t kOOB = 0x80000000u;  // an offset past every slice
+
+// Offsets pass through an empty asm so the compiler keeps the select as one
+// v_cndmask instead of splitting the loads into branches (which would make it
+// wait for every outstanding load at the join).
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// Per-block view of one problem: resources rebased at the block's first row.
+struct Slice {
+  __amdgpu_buffer_rsrc_t packed, side, side2, x;
+};
+
+// Per-lane byte offsets of the lane's first step in the current k-chunk.
+// Rows past the slice give offsets past num_records (reads return zero).
+// In a row's last, partial step the lanes past k read the next row's bytes:
+// finite weights that meet zero activations in LDS, so they add nothing.
+struct LaneBase {
+  uint32_t p, s, s2;
+};
+
+// Raw per-step loads of one lane: 32 packed bytes plus the side data of the
+// group(s) they belong to.  `sp` / `ss` are the step's uniform byte offsets
+// into the packed and side arrays, or kOOB for a padding step.
 template <int CODEC>
-struct Rebuild;
+struct Raw;
 
 template <>
-struct Rebuild<0> {  // DYADIC
-  uint32_t sb;
-  DyadicScale d;
-  __device__ __forceinline__ void load(const GemvProblem& P, int64_t row, int64_t kg, bool valid) {
-    sb = valid ? P.scales[row * (P.k >> 6) + (kg >> 6)] : 0u;
-    d = dyadic_scale(sb);
+struct Raw<0> {  // DYADIC: one bf16 scale per 64-group
+  static constexpr uint32_t kSideStep = 8;  // 4 groups x 2 bytes per 256-k step
+  u32x4 a0, a1;
+  uint16_t sb;
+  __device__ __forceinline__ void fetch(const Slice& S, const LaneBase& L, uint32_t sp,
+                                        uint32_t ss) {
+    const uint32_t off = L.p + sp;
+    a0 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, off, 0, 0);
+    a1 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, off + 16, 0, 0);
+    sb = __builtin_amdgcn_raw_buffer_load_b16(S.side, L.s + ss, 0, 0);
   }
   template <typename F>
-  __device__ __forceinline__ void apply(const uint32_t (&pw)[8], F&& mma) const {
+  __device__ __forceinline__ void apply(F&& mma) const {
+    const uint32_t pw[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+    const DyadicScale d = dyadic_scale(sb);
     const uint32_t m0 = 0x000F000Fu, m1 = 0x00F000F0u, mg = kMagic;
     if (__builtin_expect(__any(dyadic_scale_is_wide(sb)), 0)) {
 #pragma unroll
@@ -55,43 +95,47 @@ struct Rebuild<0> {  // DYADIC
 };
 
 template <>
-struct Rebuild<1> {  // LUT16
-  Lut16Table t;
-  __device__ __forceinline__ void load(const GemvProblem& P, int64_t row, int64_t kg, bool valid) {
-    u32x4 l0 = {0u, 0u, 0u, 0u}, l1 = l0;
-    uint32_t sb = 0;
-    if (valid) {
-      const int64_t g = row * (P.k >> 6) + (kg >> 6);
-      const u32x4* lut = reinterpret_cast<const u32x4*>(P.codebook);
-      sb = P.scales[g];
-      l0 = lut[2 * g];
-      l1 = lut[2 * g + 1];
-    }
-    t = lut16_table(sb, l0, l1);
+struct Raw<1> {  // LUT16: 16 bf16 levels (side) + bf16 scale (side2) per 64-group
+  static constexpr uint32_t kSideStep = 128;  // 4 groups x 32 bytes
+  u32x4 a0, a1, l0, l1;
+  uint16_t sb;
+  __device__ __forceinline__ void fetch(const Slice& S, const LaneBase& L, uint32_t sp,
+                                        uint32_t ss) {
+    const uint32_t off = L.p + sp;
+    a0 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, off, 0, 0);
+    a1 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, off + 16, 0, 0);
+    const uint32_t loff = L.s + ss;
+    l0 = __builtin_amdgcn_raw_buffer_load_b128(S.side, loff, 0, 0);
+    l1 = __builtin_amdgcn_raw_buffer_load_b128(S.side, loff + 16, 0, 0);
+    // scale offset = level offset / 16
+    sb = __builtin_amdgcn_raw_buffer_load_b16(S.side2, L.s2 + (ss == kOOB ? kOOB : ss >> 4), 0, 0);
   }
   template <typename F>
-  __device__ __forceinline__ void apply(const uint32_t (&pw)[8], F&& mma) const {
+  __device__ __forceinline__ void apply(F&& mma) const {
+    const uint32_t pw[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+    const Lut16Table t = lut16_table(sb, l0, l1);
 #pragma unroll
     for (int j = 0; j < 8; ++j) mma(j, lut16_rebuild(pw[j], t));
   }
 };
 
 template <>
-struct Rebuild<2> {  // SIGNMAG8: two 32-groups per lane step
-  SignMagTable t0, t1;
-  __device__ __forceinline__ void load(const GemvProblem& P, int64_t row, int64_t kg, bool valid) {
-    u32x4 c0 = {0u, 0u, 0u, 0u}, c1 = c0;
-    if (valid) {
-      const int64_t g = row * (P.k >> 5) + (kg >> 5);
-      const u32x4* cb = reinterpret_cast<const u32x4*>(P.codebook);
-      c0 = cb[g];
-      c1 = cb[g + 1];
-    }
-    t0 = signmag_table(c0);
-    t1 = signmag_table(c1);
+struct Raw<2> {  // SIGNMAG8: two 32-groups, 8 fp16 magnitudes each
+  static constexpr uint32_t kSideStep = 128;  // 8 groups x 16 bytes
+  u32x4 a0, a1, c0, c1;
+  __device__ __forceinline__ void fetch(const Slice& S, const LaneBase& L, uint32_t sp,
+                                        uint32_t ss) {
+    const uint32_t off = L.p + sp;
+    a0 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, off, 0, 0);
+    a1 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, off + 16, 0, 0);
+    const uint32_t coff = L.s + ss;
+    c0 = __builtin_amdgcn_raw_buffer_load_b128(S.side, coff, 0, 0);
+    c1 = __builtin_amdgcn_raw_buffer_load_b128(S.side, coff + 16, 0, 0);
   }
   template <typename F>
-  __device__ __forceinline__ void apply(const uint32_t (&pw)[8], F&& mma) const {
+  __device__ __forceinline__ void apply(F&& mma) const {
+    const uint32_t pw[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+    const SignMagTable t0 = signmag_table(c0), t1 = signmag_table(c1);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       u32x4 h, l;
@@ -102,81 +146,148 @@ struct Rebuild<2> {  // SIGNMAG8: two 32-groups per lane step
   }
 };
 
-__device__ __forceinline__ void locate(const GemvProblem* probs, int count, int64_t b, int& idx) {
-  int lo = 0, hi = count - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (probs[mid].tile_begin <= b)
-      lo = mid;
-    else
-      hi = mid - 1;
-  }
-  idx = lo;
+// k-chunk length staged in LDS for a given m and LDS capacity (16-byte units):
+// rows of kc/8 units plus one pad unit each.
+__host__ __device__ __forceinline__ int64_t gemv_chunk(int m, int xs_units, int64_t K) {
+  int64_t kc = (int64_t)((xs_units / m - 1) / 32) * 256;
+  const int64_t kpad = (K + 255) & ~(int64_t)255;
+  return kc < kpad ? kc : kpad;
 }
+
+constexpr int kXFirst = 4;  // x units per thread loaded ahead of the weight prefetch
 
 template <int CODEC, int KSPLIT, bool BATCHED>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvProblem single, const GemvProblem* probs,
-                                                   int count, int m, int y_bf16) {
+                                                   int count, int m, int y_bf16, int xs_units) {
   constexpr int RW = 4 / KSPLIT;  // row tiles per block
-  __shared__ u32x4 xs[kXsUnits];
+  extern __shared__ u32x4 xs[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   GemvProblem P;
   int64_t blk = blockIdx.x;
   if constexpr (BATCHED) {
-    int pi;
-    locate(probs, count, blk, pi);
-    P = probs[pi];
+    // one round of parallel compares instead of a chain of dependent loads
+    __shared__ int s_prob;
+    if (tid == 0) s_prob = 0;
+    __syncthreads();
+    for (int t0 = 0; t0 < count; t0 += 256) {
+      const int t = t0 + tid;
+      if (t < count) {
+        const int64_t b0 = probs[t].tile_begin;
+        const int64_t b1 = t + 1 < count ? probs[t + 1].tile_begin : 0x7FFFFFFFFFFFFFFFll;
+        if (b0 <= blk && blk < b1) s_prob = t;
+      }
+    }
+    __syncthreads();
+    P = probs[s_prob];
     blk -= P.tile_begin;
   } else {
     P = single;
   }
   const int64_t N = P.n, K = P.k;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kw = wave % KSPLIT, rw = wave / KSPLIT;
   const int r16 = lane & 15, q = lane >> 4;
-  const int64_t row = (blk * RW + rw) * 16 + r16;
-  const bool row_ok = row < N;
+  const int64_t row0 = blk * RW * 16;
+  const int rows_here = (int)((N - row0 < RW * 16) ? N - row0 : RW * 16);
+  const uint32_t rloc = (uint32_t)(rw * 16 + r16);
+  const int64_t row = row0 + rloc;
   const int mr = r16 < m ? r16 : m - 1;  // A row: batch row (padding rows repeat the last)
 
-  // chunk of k staged in LDS: rows of KC/8 units plus one pad unit
-  int64_t kc = (int64_t)((kXsUnits / m - 1) / 32) * 256;
-  const int64_t kpad = (K + 255) & ~(int64_t)255;
-  if (kc > kpad) kc = kpad;
-  const int row_units = (int)(kc / 8) + 1;
+  Slice S;
+  const uint32_t row_bytes = (uint32_t)(K >> 1);
+  const uint32_t g64 = (uint32_t)(K >> 6);  // 64-groups per row
+  S.packed = rsrc(P.packed + row0 * (K >> 1), (uint32_t)rows_here * row_bytes);
+  if constexpr (CODEC == 0) {
+    S.side = rsrc(P.scales + row0 * (K >> 6), (uint32_t)rows_here * g64 * 2);
+  } else if constexpr (CODEC == 1) {
+    S.side = rsrc(P.codebook + row0 * (K >> 6) * 16, (uint32_t)rows_here * g64 * 32);
+    S.side2 = rsrc(P.scales + row0 * (K >> 6), (uint32_t)rows_here * g64 * 2);
+  } else {
+    S.side = rsrc(P.codebook + row0 * (K >> 5) * 8, (uint32_t)rows_here * g64 * 32);
+  }
+  S.x = rsrc(P.x, (uint32_t)(m * K * 2));
 
-  const uint8_t* prow = P.packed + row * (K >> 1);
+  const int64_t kc = gemv_chunk(m, xs_units, K);
+  const int row_units = (int)(kc / 8) + 1;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 
   for (int64_t k0 = 0; k0 < K; k0 += kc) {
     const int64_t klen = (K - k0 < kc) ? K - k0 : kc;
     const int steps = (int)((klen + 255) >> 8);
-    __syncthreads();
-    // stage x[:, k0 : k0 + steps*256] (zero beyond K) in SIGMA order
-    const int units = steps * 32;
-    for (int u = tid; u < m * units; u += 256) {
-      const int mrow = u / units, uu = u - mrow * units;
+    const int units = steps * 32;  // 16-byte units of one x row in this chunk
+    // this wave's steps: st = kw + i * KSPLIT for i < nw; processed three at a
+    // time, a padding step loads zeros (offset kOOB) and is not computed
+    const int nw = steps > kw ? (steps - kw + KSPLIT - 1) / KSPLIT : 0;
+    auto step_of = [&](int i) { return kw + i * KSPLIT; };
+    LaneBase L;
+    {
+      const uint32_t g0 = rloc * g64 + (uint32_t)((k0 >> 6) + q);  // lane's first 64-group
+      L.p = rloc * row_bytes + (uint32_t)(k0 >> 1) + 32u * q;
+      L.s = CODEC == 0 ? g0 * 2 : g0 * 32;
+      L.s2 = g0 * 2;
+    }
+    auto fetch = [&](Raw<CODEC>& r, int i) {
+      const bool in = i < nw;
+      const uint32_t st = (uint32_t)step_of(i);
+      r.fetch(S, L, in ? st * 128u : kOOB, in ? st * Raw<CODEC>::kSideStep : kOOB);
+    };
+    // x staging slots: (row mrow, pass ip) -> unit tid + 256 ip of that row
+    const int ipr = (units + 255) >> 8;
+    const int nslots = m * ipr;
+    auto x_off = [&](int slot, int& mrow, int& uu) -> uint32_t {
+      mrow = slot / ipr;  // uniform
+      uu = tid + 256 * (slot - mrow * ipr);
       const int64_t kk = k0 + 8 * (int64_t)uu;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (kk < K) v = *reinterpret_cast<const u32x4*>(P.x + mrow * K + kk);
-      xs[mrow * row_units + uu] = x_to_sigma(v);
+      return (uu < units && kk < K) ? (uint32_t)((mrow * K + kk) * 2) : kOOB;
+    };
+    __syncthreads();  // the previous chunk's LDS reads are done
+    // activations first, then this wave's first three weight steps
+    u32x4 xv[kXFirst];
+    int xrow[kXFirst], xu[kXFirst];
+#pragma unroll
+    for (int i = 0; i < kXFirst; ++i) {
+      const uint32_t o = x_off(i, xrow[i], xu[i]);
+      xv[i] = __builtin_amdgcn_raw_buffer_load_b128(S.x, i < nslots ? o : kOOB, 0, 0);
+    }
+    // (issue order pinned: the loop's waits assume ra, rb, rc left in this order)
+    Raw<CODEC> ra, rb, rc;
+    __builtin_amdgcn_sched_barrier(0);
+    fetch(ra, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    fetch(rb, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    fetch(rc, 2);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < kXFirst; ++i)
+      if (i < nslots && xu[i] < units) xs[xrow[i] * row_units + xu[i]] = x_to_sigma(xv[i]);
+    for (int slot = kXFirst; slot < nslots; ++slot) {
+      int mrow, uu;
+      const uint32_t o = x_off(slot, mrow, uu);
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(S.x, o, 0, 0);
+      if (uu < units) xs[mrow * row_units + uu] = x_to_sigma(v);
     }
     __syncthreads();
 
-    for (int s = kw; s < steps; s += KSPLIT) {
-      const int64_t kg = k0 + 256 * (int64_t)s + 64 * q;
-      const bool ok = row_ok && kg < K;
-      u32x4 a0 = {0u, 0u, 0u, 0u}, a1 = a0;
-      if (ok) {
-        const u32x4* src = reinterpret_cast<const u32x4*>(prow + (kg >> 1));
-        a0 = __builtin_nontemporal_load(src);
-        a1 = __builtin_nontemporal_load(src + 1);
-      }
-      Rebuild<CODEC> rb;
-      rb.load(P, row, kg, ok);
-      const uint32_t pw[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-      const u32x4* xa = &xs[mr * row_units + 32 * s + 8 * q];
-      rb.apply(pw, [&](int j, const u32x4& b) { acc = mfma16x16x32(xa[j], b, acc); });
+    auto compute = [&](const Raw<CODEC>& r, int i) {
+      const u32x4* xa = &xs[mr * row_units + 32 * step_of(i) + 8 * q];
+      r.apply([&](int j, const u32x4& b) { acc = mfma16x16x32(xa[j], b, acc); });
+    };
+    // three buffers in rotation: a buffer is refilled right after it is used,
+    // so two steps stay in flight while one is computed and no live buffer is
+    // ever copied (a copy would have to wait for its load)
+    int i = 0;
+    for (; i + 3 <= nw; i += 3) {
+      compute(ra, i);
+      fetch(ra, i + 3);
+      compute(rb, i + 1);
+      fetch(rb, i + 4);
+      compute(rc, i + 2);
+      fetch(rc, i + 5);
     }
+    // the last one or two steps, after the loop so its body stays branch-free
+    if (i < nw) compute(ra, i);
+    if (i + 1 < nw) compute(rb, i + 1);
   }
 
   if constexpr (KSPLIT > 1) {
@@ -195,7 +306,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvProblem single, const Gem
     }
   }
 
-  if (!row_ok) return;
+  if ((int)rloc >= rows_here) return;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int mrow = 4 * q + i;
@@ -208,12 +319,23 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvProblem single, const Gem
   }
 }
 
+// LDS units for a launch: the whole padded k of the largest problem if it
+// fits, else the cap; never less than the 4 KiB the k-split reduction needs.
+int xs_units_for(int m, int64_t k_max) {
+  const int64_t kpad = (k_max + 255) & ~(int64_t)255;
+  int64_t u = (int64_t)m * (kpad / 8 + 1);
+  if (u > kXsUnitsMax) u = kXsUnitsMax;
+  if (u < 256) u = 256;
+  return (int)u;
+}
+
 template <int CODEC, int KSPLIT>
 hipError_t launch_one(const GemvProblem& p, int m, int y_bf16, hipStream_t stream) {
   const int rows = 16 * (4 / KSPLIT);
   const int64_t blocks = (p.n + rows - 1) / rows;
-  gemv_kernel<CODEC, KSPLIT, false><<<dim3((uint32_t)blocks), dim3(256), 0, stream>>>(
-      p, nullptr, 0, m, y_bf16);
+  const int xu = xs_units_for(m, p.k);
+  gemv_kernel<CODEC, KSPLIT, false><<<dim3((uint32_t)blocks), dim3(256), xu * 16, stream>>>(
+      p, nullptr, 0, m, y_bf16, xu);
   return hipGetLastError();
 }
 
@@ -246,15 +368,18 @@ hipError_t launch_gemv(int codec, const GemvProblem& p, int m, int y_bf16, hipSt
 }
 
 hipError_t launch_gemv_batched(int codec, const GemvProblem* probs_dev, int count,
-                               int64_t total_blocks, int m, int y_bf16, hipStream_t stream) {
+                               int64_t total_blocks, int64_t k_max, int m, int y_bf16,
+                               hipStream_t stream) {
   GemvProblem none{};
   const dim3 grid((uint32_t)total_blocks), block(256);
+  const int xu = xs_units_for(m, k_max);
+  const size_t lds = (size_t)xu * 16;
   if (codec == 0)
-    gemv_kernel<0, 1, true><<<grid, block, 0, stream>>>(none, probs_dev, count, m, y_bf16);
+    gemv_kernel<0, 1, true><<<grid, block, lds, stream>>>(none, probs_dev, count, m, y_bf16, xu);
   else if (codec == 1)
-    gemv_kernel<1, 1, true><<<grid, block, 0, stream>>>(none, probs_dev, count, m, y_bf16);
+    gemv_kernel<1, 1, true><<<grid, block, lds, stream>>>(none, probs_dev, count, m, y_bf16, xu);
   else
-    gemv_kernel<2, 1, true><<<grid, block, 0, stream>>>(none, probs_dev, count, m, y_bf16);
+    gemv_kernel<2, 1, true><<<grid, block, lds, stream>>>(none, probs_dev, count, m, y_bf16, xu);
   return hipGetLastError();
 }
 

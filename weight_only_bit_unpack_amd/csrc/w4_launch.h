@@ -34,7 +34,8 @@ int gemv_pick_ksplit(int64_t n, int64_t k, int m);
 hipError_t launch_gemv(int codec, const GemvProblem& p, int m, int y_bf16, hipStream_t stream);
 
 hipError_t launch_gemv_batched(int codec, const GemvProblem* probs_dev, int count,
-                               int64_t total_blocks, int m, int y_bf16, hipStream_t stream);
+                               int64_t total_blocks, int64_t k_max, int m, int y_bf16,
+                               hipStream_t stream);
 
 hipError_t launch_gemm(int codec, const GemvProblem& p, int m, int y_bf16, hipStream_t stream);
 

@@ -132,8 +132,9 @@ w4_status w4_gemm(int32_t codec, int64_t n, int64_t k, const uint8_t* packed,
  *
  * 1. Fill a HOST array of w4_gemv_problem (tile_begin is ignored) and call
  *    w4_gemv_batched_plan: it validates every problem exactly as w4_gemv would
- *    and writes tile_begin (an opaque work offset), *total_tiles and *k_max
- *    (the largest k, which sizes the kernel's LDS).
+ *    and writes tile_begin (an opaque work offset; problems with larger k get
+ *    earlier work), *total_tiles and *k_max (the largest k, which sizes the
+ *    kernel's LDS).
  * 2. Copy the planned array byte for byte into device memory (16-byte aligned).
  * 3. Call w4_gemv_batched with that device array, total_tiles and k_max, any
  *    number of times.  The kernel trusts the device copy: it must equal an

@@ -4,6 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <vector>
+
 #include "w4.h"
 #include "w4_launch.h"
 
@@ -161,8 +164,14 @@ w4_status w4_gemv_batched_plan(int32_t codec, int32_t m, int32_t y_dtype,
     total += (problems[i].n + rows - 1) / rows;
   }
   if (total > 0x7FFFFFFF) return W4_ESHAPE;
+  // Blocks are dispatched in index order; giving the longest rows (largest k)
+  // the first block indices leaves short blocks for the end of the launch.
   total = 0;
-  for (int32_t i = 0; i < count; ++i) {
+  std::vector<int32_t> order((size_t)count);
+  for (int32_t i = 0; i < count; ++i) order[(size_t)i] = i;
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int32_t a, int32_t b) { return problems[a].k > problems[b].k; });
+  for (int32_t i : order) {
     problems[i].tile_begin = total;
     total += (problems[i].n + rows - 1) / rows;
   }

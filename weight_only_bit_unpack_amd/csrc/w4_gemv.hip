@@ -58,7 +58,25 @@ struct Slice {
 // In a row's last, partial step the lanes past k read the next row's bytes:
 // finite weights that meet zero activations in LDS, so they add nothing.
 struct LaneBase {
-  uint32_t p, s, s2;
+  uint32_t pa, pb, s, s2;
+};
+
+// The packed bytes of a wave's 16 rows are loaded with whole 128-byte lines
+// per row (8 lanes x 16 bytes, rows 0-7 then rows 8-15), which streams HBM far
+// better than giving each MFMA lane its own 32 bytes straight from memory, and
+// then moved into MFMA lane order (lane = row + 16 g holds bytes 32g..32g+31 of
+// its row) through a 2 KiB per-wave LDS area.  Inside a row the 16-byte chunks
+// are stored XOR-swizzled by (row >> 1) & 7 so the reads are bank-conflict free.
+struct Shuffle {
+  u32x4* stage;  // this wave's 128 x 16-byte area
+  int wr, rd0, rd1;
+  __device__ __forceinline__ void operator()(const u32x4& a0, const u32x4& a1, u32x4& p0,
+                                             u32x4& p1) const {
+    stage[wr] = a0;
+    stage[64 + wr] = a1;
+    p0 = stage[rd0];
+    p1 = stage[rd1];
+  }
 };
 
 // Raw per-step loads of one lane: 32 packed bytes plus the side data of the
@@ -74,14 +92,15 @@ struct Raw<0> {  // DYADIC: one bf16 scale per 64-group
   uint16_t sb;
   __device__ __forceinline__ void fetch(const Slice& S, const LaneBase& L, uint32_t sp,
                                         uint32_t ss) {
-    const uint32_t off = L.p + sp;
-    a0 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, off, 0, 0);
-    a1 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, off + 16, 0, 0);
+    a0 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, L.pa + sp, 0, 0);
+    a1 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, L.pb + sp, 0, 0);
     sb = __builtin_amdgcn_raw_buffer_load_b16(S.side, L.s + ss, 0, 0);
   }
   template <typename F>
-  __device__ __forceinline__ void apply(F&& mma) const {
-    const uint32_t pw[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+  __device__ __forceinline__ void apply(const Shuffle& sh, F&& mma) const {
+    u32x4 p0, p1;
+    sh(a0, a1, p0, p1);
+    const uint32_t pw[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
     const DyadicScale d = dyadic_scale(sb);
     const uint32_t m0 = 0x000F000Fu, m1 = 0x00F000F0u, mg = kMagic;
     if (__builtin_expect(__any(dyadic_scale_is_wide(sb)), 0)) {
@@ -101,9 +120,8 @@ struct Raw<1> {  // LUT16: 16 bf16 levels (side) + bf16 scale (side2) per 64-gro
   uint16_t sb;
   __device__ __forceinline__ void fetch(const Slice& S, const LaneBase& L, uint32_t sp,
                                         uint32_t ss) {
-    const uint32_t off = L.p + sp;
-    a0 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, off, 0, 0);
-    a1 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, off + 16, 0, 0);
+    a0 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, L.pa + sp, 0, 0);
+    a1 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, L.pb + sp, 0, 0);
     const uint32_t loff = L.s + ss;
     l0 = __builtin_amdgcn_raw_buffer_load_b128(S.side, loff, 0, 0);
     l1 = __builtin_amdgcn_raw_buffer_load_b128(S.side, loff + 16, 0, 0);
@@ -111,8 +129,10 @@ struct Raw<1> {  // LUT16: 16 bf16 levels (side) + bf16 scale (side2) per 64-gro
     sb = __builtin_amdgcn_raw_buffer_load_b16(S.side2, L.s2 + (ss == kOOB ? kOOB : ss >> 4), 0, 0);
   }
   template <typename F>
-  __device__ __forceinline__ void apply(F&& mma) const {
-    const uint32_t pw[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+  __device__ __forceinline__ void apply(const Shuffle& sh, F&& mma) const {
+    u32x4 p0, p1;
+    sh(a0, a1, p0, p1);
+    const uint32_t pw[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
     const Lut16Table t = lut16_table(sb, l0, l1);
 #pragma unroll
     for (int j = 0; j < 8; ++j) mma(j, lut16_rebuild(pw[j], t));
@@ -125,16 +145,17 @@ struct Raw<2> {  // SIGNMAG8: two 32-groups, 8 fp16 magnitudes each
   u32x4 a0, a1, c0, c1;
   __device__ __forceinline__ void fetch(const Slice& S, const LaneBase& L, uint32_t sp,
                                         uint32_t ss) {
-    const uint32_t off = L.p + sp;
-    a0 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, off, 0, 0);
-    a1 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, off + 16, 0, 0);
+    a0 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, L.pa + sp, 0, 0);
+    a1 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, L.pb + sp, 0, 0);
     const uint32_t coff = L.s + ss;
     c0 = __builtin_amdgcn_raw_buffer_load_b128(S.side, coff, 0, 0);
     c1 = __builtin_amdgcn_raw_buffer_load_b128(S.side, coff + 16, 0, 0);
   }
   template <typename F>
-  __device__ __forceinline__ void apply(F&& mma) const {
-    const uint32_t pw[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+  __device__ __forceinline__ void apply(const Shuffle& sh, F&& mma) const {
+    u32x4 p0, p1;
+    sh(a0, a1, p0, p1);
+    const uint32_t pw[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
     const SignMagTable t0 = signmag_table(c0), t1 = signmag_table(c1);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -174,7 +195,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvProblem single, const Gem
       const int t = t0 + tid;
       if (t < count) {
         const int64_t b0 = probs[t].tile_begin;
-        const int64_t b1 = t + 1 < count ? probs[t + 1].tile_begin : 0x7FFFFFFFFFFFFFFFll;
+        const int64_t b1 = b0 + (probs[t].n + RW * 16 - 1) / (RW * 16);
         if (b0 <= blk && blk < b1) s_prob = t;
       }
     }
@@ -192,6 +213,19 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvProblem single, const Gem
   const uint32_t rloc = (uint32_t)(rw * 16 + r16);
   const int64_t row = row0 + rloc;
   const int mr = r16 < m ? r16 : m - 1;  // A row: batch row (padding rows repeat the last)
+  // whole-line loads: lane = (row i of 8, chunk position cp); see Shuffle
+  const int li = lane >> 3, cp = lane & 7;
+  const uint32_t rowA = (uint32_t)(rw * 16 + li);
+  const uint32_t chA = 16u * (uint32_t)(cp ^ ((li >> 1) & 7));
+  const uint32_t chB = 16u * (uint32_t)(cp ^ (((li + 8) >> 1) & 7));
+  Shuffle sh;
+  sh.stage = xs + xs_units + 128 * wave;
+  sh.wr = lane;
+  {
+    const int sw = (r16 >> 1) & 7;
+    sh.rd0 = r16 * 8 + ((2 * q) ^ sw);
+    sh.rd1 = r16 * 8 + ((2 * q + 1) ^ sw);
+  }
 
   Slice S;
   const uint32_t row_bytes = (uint32_t)(K >> 1);
@@ -222,7 +256,8 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvProblem single, const Gem
     LaneBase L;
     {
       const uint32_t g0 = rloc * g64 + (uint32_t)((k0 >> 6) + q);  // lane's first 64-group
-      L.p = rloc * row_bytes + (uint32_t)(k0 >> 1) + 32u * q;
+      L.pa = rowA * row_bytes + (uint32_t)(k0 >> 1) + chA;
+      L.pb = (rowA + 8) * row_bytes + (uint32_t)(k0 >> 1) + chB;
       L.s = CODEC == 0 ? g0 * 2 : g0 * 32;
       L.s2 = g0 * 2;
     }
@@ -241,7 +276,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvProblem single, const Gem
       return (uu < units && kk < K) ? (uint32_t)((mrow * K + kk) * 2) : kOOB;
     };
     __syncthreads();  // the previous chunk's LDS reads are done
-    // activations first, then this wave's first three weight steps
+    // activations first, then this wave's first four weight steps
     u32x4 xv[kXFirst];
     int xrow[kXFirst], xu[kXFirst];
 #pragma unroll
@@ -249,14 +284,16 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvProblem single, const Gem
       const uint32_t o = x_off(i, xrow[i], xu[i]);
       xv[i] = __builtin_amdgcn_raw_buffer_load_b128(S.x, i < nslots ? o : kOOB, 0, 0);
     }
-    // (issue order pinned: the loop's waits assume ra, rb, rc left in this order)
-    Raw<CODEC> ra, rb, rc;
+    // (issue order pinned: the loop's waits assume the buffers left in this order)
+    Raw<CODEC> ra, rb, rc, rd;
     __builtin_amdgcn_sched_barrier(0);
     fetch(ra, 0);
     __builtin_amdgcn_sched_barrier(0);
     fetch(rb, 1);
     __builtin_amdgcn_sched_barrier(0);
     fetch(rc, 2);
+    __builtin_amdgcn_sched_barrier(0);
+    fetch(rd, 3);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < kXFirst; ++i)
@@ -271,23 +308,26 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvProblem single, const Gem
 
     auto compute = [&](const Raw<CODEC>& r, int i) {
       const u32x4* xa = &xs[mr * row_units + 32 * step_of(i) + 8 * q];
-      r.apply([&](int j, const u32x4& b) { acc = mfma16x16x32(xa[j], b, acc); });
+      r.apply(sh, [&](int j, const u32x4& b) { acc = mfma16x16x32(xa[j], b, acc); });
     };
-    // three buffers in rotation: a buffer is refilled right after it is used,
-    // so two steps stay in flight while one is computed and no live buffer is
-    // ever copied (a copy would have to wait for its load)
+    // four buffers in rotation: a buffer is refilled right after it is used,
+    // so three steps stay in flight while one is computed and no live buffer
+    // is ever copied (a copy would have to wait for its load)
     int i = 0;
-    for (; i + 3 <= nw; i += 3) {
+    for (; i + 4 <= nw; i += 4) {
       compute(ra, i);
-      fetch(ra, i + 3);
+      fetch(ra, i + 4);
       compute(rb, i + 1);
-      fetch(rb, i + 4);
+      fetch(rb, i + 5);
       compute(rc, i + 2);
-      fetch(rc, i + 5);
+      fetch(rc, i + 6);
+      compute(rd, i + 3);
+      fetch(rd, i + 7);
     }
-    // the last one or two steps, after the loop so its body stays branch-free
+    // the last one to three steps, after the loop so its body stays branch-free
     if (i < nw) compute(ra, i);
     if (i + 1 < nw) compute(rb, i + 1);
+    if (i + 2 < nw) compute(rc, i + 2);
   }
 
   if constexpr (KSPLIT > 1) {
@@ -334,7 +374,7 @@ hipError_t launch_one(const GemvProblem& p, int m, int y_bf16, hipStream_t strea
   const int rows = 16 * (4 / KSPLIT);
   const int64_t blocks = (p.n + rows - 1) / rows;
   const int xu = xs_units_for(m, p.k);
-  gemv_kernel<CODEC, KSPLIT, false><<<dim3((uint32_t)blocks), dim3(256), xu * 16, stream>>>(
+  gemv_kernel<CODEC, KSPLIT, false><<<dim3((uint32_t)blocks), dim3(256), (xu + 512) * 16, stream>>>(
       p, nullptr, 0, m, y_bf16, xu);
   return hipGetLastError();
 }
@@ -373,7 +413,7 @@ hipError_t launch_gemv_batched(int codec, const GemvProblem* probs_dev, int coun
   GemvProblem none{};
   const dim3 grid((uint32_t)total_blocks), block(256);
   const int xu = xs_units_for(m, k_max);
-  const size_t lds = (size_t)xu * 16;
+  const size_t lds = (size_t)(xu + 512) * 16;  // activations + 4 x 2 KiB shuffle areas
   if (codec == 0)
     gemv_kernel<0, 1, true><<<grid, block, lds, stream>>>(none, probs_dev, count, m, y_bf16, xu);
   else if (codec == 1)

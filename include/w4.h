@@ -130,15 +130,18 @@ w4_status w4_gemm(int32_t codec, int64_t n, int64_t k, const uint8_t* packed,
  * [DG] sec. 2.5 runs one unpack launch per layer, 168 per forward; one launch
  * for all of them removes the per-launch ramp.
  *
- * 1. Fill a HOST array of w4_gemv_problem (tile_begin is ignored) and call
- *    w4_gemv_batched_plan: it validates every problem exactly as w4_gemv would
- *    and writes tile_begin (an opaque work offset; problems with larger k get
- *    earlier work), *total_tiles and *k_max (the largest k, which sizes the
- *    kernel's LDS).
- * 2. Copy the planned array byte for byte into device memory (16-byte aligned).
- * 3. Call w4_gemv_batched with that device array, total_tiles and k_max, any
- *    number of times.  The kernel trusts the device copy: it must equal an
- *    array the plan accepted.
+ * 1. Fill a HOST array of count w4_gemv_problem records (tile_begin is
+ *    ignored) and call w4_gemv_batched_plan: it validates every problem
+ *    exactly as w4_gemv would, writes each tile_begin (an opaque work offset;
+ *    problems with larger k get earlier work) and fills *info.
+ * 2. Copy the count records byte for byte into device memory (16-byte
+ *    aligned).  The table is only read, so it can be launched any number of
+ *    times, also concurrently.
+ * 3. Call w4_gemv_batched with that device table and the plan's info.  The
+ *    kernel trusts the device copy: it must equal an array the plan accepted.
+ * Errors: W4_EINVAL / W4_ESHAPE / W4_EALIGN / W4_EUNSUPPORTED as for w4_gemv
+ * (the plan reports the first failing problem's status and writes nothing to
+ * *info); W4_ESHAPE when the problems need more than 2^31 - 1 tiles.
  */
 typedef struct {
   const uint8_t* packed;
@@ -151,13 +154,21 @@ typedef struct {
   int64_t tile_begin; /* written by w4_gemv_batched_plan */
 } w4_gemv_problem;
 
+typedef struct {
+  int64_t total_tiles; /* 64-row work tiles over all problems */
+  int64_t k_min;       /* smallest k */
+  int64_t k_max;       /* largest k (sizes the kernel's LDS) */
+  int32_t count;       /* number of problems */
+  int32_t reserved;
+} w4_gemv_batch_info;
+
 w4_status w4_gemv_batched_plan(int32_t codec, int32_t m, int32_t y_dtype,
                                w4_gemv_problem* problems_host, int32_t count,
-                               int64_t* total_tiles, int64_t* k_max);
+                               w4_gemv_batch_info* info);
 
 w4_status w4_gemv_batched(int32_t codec, int32_t m, int32_t y_dtype,
-                          const w4_gemv_problem* problems_device, int32_t count,
-                          int64_t total_tiles, int64_t k_max, void* stream);
+                          w4_gemv_problem* problems_device, const w4_gemv_batch_info* info,
+                          void* stream);
 
 #ifdef __cplusplus
 }

@@ -86,19 +86,22 @@ def test_quantize_dequant_validation(w4):
 
 
 def test_batched_plan_validation(w4):
-    import torch
-    arr = (w4.W4Problem * 2)()
+    arr = (w4.W4Problem * 3)()
     for i in range(2):
-        arr[i] = w4.W4Problem(16, 16, None, 16, 16, 100 + 64 * i, 128, 0)
-    total, kmax = ctypes.c_int64(-1), ctypes.c_int64(-1)
-    plan = lambda m: w4._lib.w4_gemv_batched_plan(0, m, 0, arr, 2, ctypes.byref(total),
-                                                   ctypes.byref(kmax))
+        arr[i] = w4.W4Problem(16, 16, None, 16, 16, 100 + 64 * i, 128 + 64 * i, 0)
+    arr[2] = w4.W4Problem(8, 8, 8, 8, 8, 7, 7, 7)   # past count: never touched
+    info = w4.W4BatchInfo()
+    plan = lambda m: w4._lib.w4_gemv_batched_plan(0, m, 0, arr, 2, ctypes.byref(info))
     assert plan(1) == 0
-    assert total.value == 2 + 3 and arr[0].tile_begin == 0 and arr[1].tile_begin == 2
-    assert kmax.value == 128
+    # largest k first: problem 1 (k = 192, 3 tiles) gets tiles 0..2, problem 0 tiles 3..4
+    assert info.total_tiles == 2 + 3 and arr[1].tile_begin == 0 and arr[0].tile_begin == 3
+    assert (info.k_min, info.k_max, info.count) == (128, 192, 2)
+    assert (arr[2].n, arr[2].k, arr[2].tile_begin) == (7, 7, 7)
     arr[1].k = 100
     assert plan(1) == 2
     assert plan(17) == 2
-    assert w4._lib.w4_gemv_batched(0, 1, 0, ctypes.c_void_p(8), 2, 5, 128, None) == 3
-    assert w4._lib.w4_gemv_batched(0, 1, 0, ctypes.c_void_p(16), 2, 5, -1, None) == 1
-    assert w4._lib.w4_gemv_batched(0, 1, 0, None, 0, 0, 0, None) == 0
+    assert w4._lib.w4_gemv_batched(0, 1, 0, ctypes.c_void_p(8), ctypes.byref(info), None) == 3
+    bad = w4.W4BatchInfo(5, -1, 128, 2, 0)
+    assert w4._lib.w4_gemv_batched(0, 1, 0, ctypes.c_void_p(16), ctypes.byref(bad), None) == 1
+    empty = w4.W4BatchInfo(0, 0, 0, 0, 0)
+    assert w4._lib.w4_gemv_batched(0, 1, 0, None, ctypes.byref(empty), None) == 0

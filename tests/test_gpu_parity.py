@@ -274,3 +274,45 @@ def test_signmag8_gemv_and_gemm(w4, m):
     y2 = w4.w4_gemm(dev_u8(packing.pack(nib)), dev_bf16(x), w4.W4_SIGNMAG8, codebook=dev_f16(cb))
     torch.cuda.synchronize()
     _gemv_check(y2, x, w_hat, False)
+
+
+def _batched_case(codec, n, k, seed):
+    """(packed, side tables, fp64 dequantized weight) of one batched problem."""
+    if codec == 0:
+        w = synthetic.student_t_bf16((n, k), 4, 0.02, seed)
+        idx, s = native.dyadic_quantize(w)
+        return packing.pack(idx), dict(scales=dev_bf16(s)), bits.bf16_to_f64(native.dyadic_dequant(idx, s))
+    if codec == 1:
+        w, s, L = _lut_case(n, k, seed)
+        idx = native.lut16_indices(w, s, L)
+        w_hat = bits.bf16_to_f64(lut16.dequant_from_indices(idx, s, L))
+        return packing.pack(idx), dict(scales=dev_bf16(s), codebook=dev_bf16(L)), w_hat
+    w, cb = _sm_case(n, k, seed)
+    nib = native.signmag8_indices(w, cb)
+    return packing.pack(nib), dict(codebook=dev_f16(cb)), signmag8.dequant_values(cb, nib)
+
+
+# every codec through the batched launch, ragged n, m > 1, repeated launches
+@pytest.mark.parametrize("codec,m,shapes", [
+    (0, 1, [(2048, 2048), (5632, 2048), (2048, 5632), (100, 1024), (70, 832)]),
+    (0, 4, [(1000, 2048), (64, 1024), (333, 832)]),
+    (1, 1, [(300, 1024), (129, 2048)]),
+    (2, 3, [(300, 1024), (65, 2048)]),
+])
+def test_gemv_batched_codecs(w4, codec, m, shapes):
+    report("gemv_batched_codecs", codec=codec, m=m, count=len(shapes))
+    probs, refs = [], []
+    for i, (n, k) in enumerate(shapes):
+        p, side, w_hat = _batched_case(codec, n, k, 1200 + 10 * codec + i)
+        x = synthetic.normal_bf16((m, k), 1.0, 1300 + 10 * codec + i)
+        y = torch.full((m, n), float("nan"), device="cuda")
+        probs.append(dict(packed=dev_u8(p), x=dev_bf16(x), y=y, **side))
+        refs.append((x, w_hat))
+    batch = w4.w4_gemv_batched_plan(probs, codec)
+    for rep in range(3):
+        for pr in probs:
+            pr["y"].fill_(float("nan"))
+        batch()
+        torch.cuda.synchronize()
+        for pr, (x, w_hat) in zip(probs, refs):
+            _gemv_check(pr["y"], x, w_hat, False)

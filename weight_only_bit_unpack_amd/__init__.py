@@ -35,6 +35,12 @@ class W4Problem(ctypes.Structure):
                 ("n", _I64), ("k", _I64), ("tile_begin", _I64)]
 
 
+class W4BatchInfo(ctypes.Structure):
+    """Mirror of ``w4_gemv_batch_info``."""
+    _fields_ = [("total_tiles", _I64), ("k_min", _I64), ("k_max", _I64), ("count", _I32),
+                ("reserved", _I32)]
+
+
 _SIGS = {
     "w4_status_str": ([_I32], ctypes.c_char_p),
     "w4_group_size": ([_I32], _I32),
@@ -43,8 +49,8 @@ _SIGS = {
     "w4_gemv": ([_I32, _I64, _I64, _P, _P, _P, _P, _I32, _P, _I32, _P], _I32),
     "w4_gemm": ([_I32, _I64, _I64, _P, _P, _P, _P, _I32, _P, _I32, _P], _I32),
     "w4_gemv_batched_plan": ([_I32, _I32, _I32, ctypes.POINTER(W4Problem), _I32,
-                              ctypes.POINTER(_I64), ctypes.POINTER(_I64)], _I32),
-    "w4_gemv_batched": ([_I32, _I32, _I32, _P, _I32, _I64, _I64, _P], _I32),
+                              ctypes.POINTER(W4BatchInfo)], _I32),
+    "w4_gemv_batched": ([_I32, _I32, _I32, _P, ctypes.POINTER(W4BatchInfo), _P], _I32),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -180,16 +186,19 @@ class W4GemvBatch:
     """A planned batch of independent GEMVs (``w4_gemv_batched_plan``), with
     its descriptor table already in device memory.  Call it to launch."""
 
-    def __init__(self, codec, m, y_dtype, table_dev, count, total_tiles, k_max, keepalive):
+    def __init__(self, codec, m, y_dtype, table_dev, info, keepalive):
         self.codec, self.m, self.y_dtype = codec, m, y_dtype
-        self.table, self.count, self.total_tiles = table_dev, count, total_tiles
-        self.k_max = k_max
+        self.table, self.info = table_dev, info
         self._keep = keepalive
+
+    @property
+    def total_tiles(self):
+        return self.info.total_tiles
 
     def __call__(self, stream=None):
         _check(_lib.w4_gemv_batched(self.codec, self.m, self.y_dtype,
-                                    ctypes.c_void_p(self.table.data_ptr()), self.count,
-                                    self.total_tiles, self.k_max, _stream(stream)))
+                                    ctypes.c_void_p(self.table.data_ptr()),
+                                    ctypes.byref(self.info), _stream(stream)))
 
 
 def w4_gemv_batched_plan(problems, codec=W4_DYADIC, y_dtype=torch.float32):
@@ -214,10 +223,9 @@ def w4_gemv_batched_plan(problems, codec=W4_DYADIC, y_dtype=torch.float32):
         arr[i] = W4Problem(packed.data_ptr(), _ptr(p.get("scales")), _ptr(p.get("codebook")),
                            x.data_ptr(), y.data_ptr(), n, k, 0)
         keep.append(p)
-    total, kmax = _I64(0), _I64(0)
-    _check(_lib.w4_gemv_batched_plan(codec, m or 1, code, arr, len(problems), ctypes.byref(total),
-                                     ctypes.byref(kmax)))
-    raw = bytes(arr)
+    info = W4BatchInfo()
+    _check(_lib.w4_gemv_batched_plan(codec, m or 1, code, arr, len(problems),
+                                     ctypes.byref(info)))
     dev = problems[0]["packed"].device if problems else torch.device("cuda")
-    table = torch.frombuffer(bytearray(raw), dtype=torch.uint8).to(dev)
-    return W4GemvBatch(codec, m or 1, code, table, len(problems), total.value, kmax.value, keep)
+    table = torch.frombuffer(bytearray(bytes(arr)), dtype=torch.uint8).to(dev)
+    return W4GemvBatch(codec, m or 1, code, table, info, keep)

@@ -145,55 +145,61 @@ w4_status w4_gemm(int32_t codec, int64_t n, int64_t k, const uint8_t* packed,
 }
 
 w4_status w4_gemv_batched_plan(int32_t codec, int32_t m, int32_t y_dtype,
-                               w4_gemv_problem* problems, int32_t count, int64_t* total_tiles,
-                               int64_t* k_max) {
-  if (!total_tiles || !k_max || count < 0 || (count > 0 && !problems)) return W4_EINVAL;
+                               w4_gemv_problem* problems, int32_t count,
+                               w4_gemv_batch_info* info) {
+  if (!info || count < 0 || !problems) return W4_EINVAL;
   if (!valid_codec(codec)) return W4_EINVAL;
   if (m < 1) return m < 0 ? W4_EINVAL : W4_ESHAPE;
   const int64_t rows = w4::gemv_rows_per_block(1);
-  int64_t total = 0;
   for (int32_t i = 0; i < count; ++i) {
     const w4_gemv_problem& p = problems[i];
     w4_status st = check_matmul(codec, p.n, p.k, p.packed, p.scales, p.codebook, p.x, m, p.y,
                                 y_dtype, kGemvMaxM);
     if (st != W4_OK) return st;
   }
-  int64_t kmax = 0;
+  int64_t total = 0, kmax = 0, kmin = count > 0 ? problems[0].k : 0;
   for (int32_t i = 0; i < count; ++i) {
     if (problems[i].k > kmax) kmax = problems[i].k;
+    if (problems[i].k < kmin) kmin = problems[i].k;
     total += (problems[i].n + rows - 1) / rows;
   }
   if (total > 0x7FFFFFFF) return W4_ESHAPE;
-  // Blocks are dispatched in index order; giving the longest rows (largest k)
-  // the first block indices leaves short blocks for the end of the launch.
-  total = 0;
+  // Work is handed out in tile order; giving the longest rows (largest k) the
+  // first tiles leaves short tiles for the end of the launch.
   std::vector<int32_t> order((size_t)count);
   for (int32_t i = 0; i < count; ++i) order[(size_t)i] = i;
   std::stable_sort(order.begin(), order.end(),
                    [&](int32_t a, int32_t b) { return problems[a].k > problems[b].k; });
+  total = 0;
   for (int32_t i : order) {
     problems[i].tile_begin = total;
     total += (problems[i].n + rows - 1) / rows;
   }
-  *total_tiles = total;
-  *k_max = kmax;
+  info->total_tiles = total;
+  info->k_min = kmin;
+  info->k_max = kmax;
+  info->count = count;
+  info->reserved = 0;
   return W4_OK;
 }
 
 w4_status w4_gemv_batched(int32_t codec, int32_t m, int32_t y_dtype,
-                          const w4_gemv_problem* problems_device, int32_t count,
-                          int64_t total_tiles, int64_t k_max, void* stream) {
-  if (!valid_codec(codec) || count < 0 || total_tiles < 0 || k_max < 0) return W4_EINVAL;
+                          w4_gemv_problem* problems_device, const w4_gemv_batch_info* info,
+                          void* stream) {
+  if (!info || !valid_codec(codec)) return W4_EINVAL;
+  if (info->count < 0 || info->total_tiles < 0 || info->k_max < 0 || info->k_min < 0)
+    return W4_EINVAL;
   if (m < 1) return m < 0 ? W4_EINVAL : W4_ESHAPE;
   if (m > kGemvMaxM) return W4_ESHAPE;
   if (y_dtype != W4_F32 && y_dtype != W4_BF16) return W4_EUNSUPPORTED;
-  if (count == 0 || total_tiles == 0) return W4_OK;
+  if (info->count == 0 || info->total_tiles == 0) return W4_OK;
   if (!problems_device) return W4_EINVAL;
   if (!aligned(problems_device, 16)) return W4_EALIGN;
-  if (total_tiles > 0x7FFFFFFF) return W4_ESHAPE;
+  if (info->total_tiles > 0x7FFFFFFF) return W4_ESHAPE;
   return launched(w4::launch_gemv_batched(
-      codec, reinterpret_cast<const w4::GemvProblem*>(problems_device), count, total_tiles,
-      k_max, m, y_dtype == W4_BF16, static_cast<hipStream_t>(stream)));
+      codec, reinterpret_cast<const w4::GemvProblem*>(problems_device), info->count,
+      info->total_tiles, info->k_max, m, y_dtype == W4_BF16,
+      static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -256,6 +256,15 @@ __device__ __forceinline__ u32x4 sigma_to_natural(const u32x4& s) {
   return r;
 }
 
+// Workgroup barrier that orders LDS only.  __syncthreads() also fences global
+// memory, which makes the wave wait for every vector-memory load in flight;
+// here prefetched weight loads stay in flight across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);

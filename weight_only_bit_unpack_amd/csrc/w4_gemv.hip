@@ -6,17 +6,18 @@
 // int4-g32 page, section 5.2: a fused int4 kernel with the group codebook in
 // registers.
 //
-// Work unit: a 16-row x 256-k step.  Lane l = (r = l % 16, q = l / 16) loads
-// the 32 packed bytes of row r covering k = 256 s + 64 q .. + 63 (one group
-// for the 64-groups, two for SIGNMAG8), so the four q-lanes of a row read one
-// full 128-byte line.  Each of the lane's 8 packed dwords is rebuilt into one
-// bf16 MFMA B operand (8 values), and v_mfma_f32_16x16x32_bf16 multiplies it
-// by the activation operand: A row = batch row m (rows >= m repeat row m-1 and
-// are never stored), D[m][r] lands in lane r + 16 (m / 4), register m % 4.
-// For m = 1 the matrix core does 16x the necessary multiplies, which is free:
-// the kernel is bound by HBM and by the VALU work of the rebuild (about 17
-// VALU instructions per 8 weights), and the MFMA takes the multiply-adds off
-// the VALU.
+// Work unit: a 16-row x 256-k step of one wave.  The wave loads its rows'
+// packed bytes as whole 128-byte lines (Shuffle below) and moves them through
+// LDS into MFMA lane order: lane l = (r = l % 16, q = l / 16) then holds the
+// 32 packed bytes of row r covering k = 256 s + 64 q .. + 63 (one 64-group, or
+// two 32-groups for SIGNMAG8).  Each of the lane's 8 packed dwords is rebuilt
+// into one bf16 MFMA B operand (8 values), and v_mfma_f32_16x16x32_bf16
+// multiplies it by the activation operand: A row = batch row m (rows >= m
+// repeat row m-1 and are never stored), D[m][r] lands in lane r + 16 (m / 4),
+// register m % 4.  For m = 1 the matrix core does 16x the necessary
+// multiplies, which costs nothing here: the kernel is bound by HBM and by the
+// VALU work of the rebuild (about 17 VALU instructions per 8 weights), and the
+// MFMA takes the multiply-adds off the VALU.
 //
 // The activations are staged once per block into LDS in the rebuild's slot
 // order (w4_device.h, SIGMA), in k-chunks when m * k does not fit.
@@ -24,6 +25,7 @@
 // With KSPLIT > 1 the waves' partial sums are added in LDS in a fixed order.
 #include "w4_device.h"
 #include "w4_launch.h"
+
 
 namespace w4 {
 namespace {
@@ -275,7 +277,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvProblem single, const Gem
       const int64_t kk = k0 + 8 * (int64_t)uu;
       return (uu < units && kk < K) ? (uint32_t)((mrow * K + kk) * 2) : kOOB;
     };
-    __syncthreads();  // the previous chunk's LDS reads are done
+    lds_barrier();  // the previous chunk's LDS reads are done
     // activations first, then this wave's first four weight steps
     u32x4 xv[kXFirst];
     int xrow[kXFirst], xu[kXFirst];
@@ -304,7 +306,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvProblem single, const Gem
       const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(S.x, o, 0, 0);
       if (uu < units) xs[mrow * row_units + uu] = x_to_sigma(v);
     }
-    __syncthreads();
+    lds_barrier();
 
     auto compute = [&](const Raw<CODEC>& r, int i) {
       const u32x4* xa = &xs[mr * row_units + 32 * step_of(i) + 8 * q];
@@ -408,12 +410,12 @@ hipError_t launch_gemv(int codec, const GemvProblem& p, int m, int y_bf16, hipSt
 }
 
 hipError_t launch_gemv_batched(int codec, const GemvProblem* probs_dev, int count,
-                               int64_t total_blocks, int64_t k_max, int m, int y_bf16,
+                               int64_t total_tiles, int64_t k_max, int m, int y_bf16,
                                hipStream_t stream) {
-  GemvProblem none{};
-  const dim3 grid((uint32_t)total_blocks), block(256);
+  const dim3 block(256), grid((uint32_t)total_tiles);
   const int xu = xs_units_for(m, k_max);
   const size_t lds = (size_t)(xu + 512) * 16;  // activations + 4 x 2 KiB shuffle areas
+  GemvProblem none{};
   if (codec == 0)
     gemv_kernel<0, 1, true><<<grid, block, lds, stream>>>(none, probs_dev, count, m, y_bf16, xu);
   else if (codec == 1)

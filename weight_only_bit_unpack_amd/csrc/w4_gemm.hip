@@ -2,158 +2,485 @@
 //
 // k-means page, section 4.1: batches above the LUT-kernel range go to a mixed
 // 4-bit x bf16 kernel.  Y[M][N] = X[M][K] * W_hat[N][K]^T, bf16 MFMA with fp32
-// accumulation; the 4-bit weight tile is rebuilt (w4_device.h) straight into
-// LDS once per block and k-step, next to the staged activation tile.
+// accumulation; each 4-bit weight is rebuilt (w4_device.h) once per block into
+// LDS and multiplied there against every batch row of the block.
 //
-// Block tile 128 (batch rows) x 64 (weight rows), k-step 64 (one 64-group per
-// weight row).  4 waves in a 2 x 2 grid, each 64 x 32 = 4 x 2 tiles of
-// v_mfma_f32_16x16x32_bf16.  Both LDS tiles hold each 8-k block in the
-// rebuild's slot order, so an MFMA operand is one 16-byte LDS read.
+// Block tile 256 (batch rows) x 128 (weight rows), k-step 64 (one 64-group per
+// weight row), one block per CU with eight waves, two per SIMD.  Wave w owns
+// batch rows 64 (w % 4) .. + 63 against all 128 weight rows = 2 x 4 tiles of
+// v_mfma_f32_32x32x16_bf16 (128 fp32 accumulators per lane), for half of each
+// k-step (w / 4); the two halves are added through LDS after the k loop.  Two
+// waves per SIMD let one wave's MFMAs run while the other waits on memory,
+// LDS or the rebuild, which a single wave cannot overlap.
+//
+// A wave owns its batch rows, so its activation operands come straight from
+// global memory into registers, from a copy of x rewritten once per call into
+// MFMA operand order (pack_activations); only the rebuilt weights (natural k
+// order) go through LDS: 16 KB of writes and 64 KB of reads per k-step against
+// 4.2 MFLOP of MFMA work.
+//
+// The k range is split over S blocks when the output tiles alone cannot fill
+// the GPU (256 x 8192 outputs are only 64 tiles); each split writes an fp32
+// partial in the MFMA register layout and a second kernel adds the partials in
+// split order, so results do not depend on timing.
+//
+// Software pipeline per k-step u: issue the loads of step u+3 (packed weights
+// and their side data) and u+1 (activations), rebuild step u+1 into the other
+// LDS buffer, run the 16 MFMAs of step u, then one LDS-only barrier.  Loads
+// past the block's k range use offsets past the buffer resource and return
+// zero, so the loop runs whole rounds of four steps without branches.
 #include "w4_device.h"
 #include "w4_launch.h"
+
+#include <map>
+#include <mutex>
+#include <utility>
 
 namespace w4 {
 namespace {
 
-constexpr int BM = 128, BN = 64, BK = 64;
-constexpr int STR = BK / 8 + 1;  // 16-byte units per LDS row (+1 pad against bank conflicts)
+constexpr int BM = 256, BN = 128, BK = 64;
+constexpr int STR = BK / 8 + 1;  // 16-byte units per LDS weight row (+1 pad: conflict-free reads)
+constexpr uint32_t kOOB = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// Packed bytes and side data one thread rebuilds per k-step: weight row
+// tid / 4, k = 16 (tid % 4) .. + 15 of the step (8 packed bytes).  The rebuilt
+// values go to LDS in natural k order (the activations stay as loaded).
+template <int CODEC>
+struct WRaw;
+
+template <>
+struct WRaw<0> {  // DYADIC: bf16 scale of the row's 64-group
+  uint32_t p0, p1;
+  uint16_t sb;
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t pk, __amdgpu_buffer_rsrc_t s0,
+                                       __amdgpu_buffer_rsrc_t, uint32_t po, uint32_t so,
+                                       uint32_t) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(pk, po, 0, 0);
+    p0 = v[0];
+    p1 = v[1];
+    sb = __builtin_amdgcn_raw_buffer_load_b16(s0, so, 0, 0);
+  }
+  __device__ __forceinline__ void rebuild(u32x4* dst, u32x4*) const {
+    const DyadicScale d = dyadic_scale(sb);
+    const uint32_t m0 = 0x000F000Fu, m1 = 0x00F000F0u, mg = kMagic;
+    if (__builtin_expect(__any(dyadic_scale_is_wide(sb)), 0)) {
+      dst[0] = sigma_to_natural(dyadic_rebuild_wide(p0, d, m0, m1, mg));
+      dst[1] = sigma_to_natural(dyadic_rebuild_wide(p1, d, m0, m1, mg));
+    } else {
+      dst[0] = sigma_to_natural(dyadic_rebuild(p0, d, m0, m1, mg));
+      dst[1] = sigma_to_natural(dyadic_rebuild(p1, d, m0, m1, mg));
+    }
+  }
+};
+
+template <>
+struct WRaw<1> {  // LUT16: 16 bf16 levels + bf16 scale of the row's 64-group
+  uint32_t p0, p1;
+  u32x4 l0, l1;
+  uint16_t sb;
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t pk, __amdgpu_buffer_rsrc_t s0,
+                                       __amdgpu_buffer_rsrc_t s1, uint32_t po, uint32_t so,
+                                       uint32_t co) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(pk, po, 0, 0);
+    p0 = v[0];
+    p1 = v[1];
+    l0 = __builtin_amdgcn_raw_buffer_load_b128(s1, co, 0, 0);
+    l1 = __builtin_amdgcn_raw_buffer_load_b128(s1, co + 16, 0, 0);
+    sb = __builtin_amdgcn_raw_buffer_load_b16(s0, so, 0, 0);
+  }
+  __device__ __forceinline__ void rebuild(u32x4* dst, u32x4*) const {
+    const Lut16Table t = lut16_table(sb, l0, l1);
+    dst[0] = sigma_to_natural(lut16_rebuild(p0, t));
+    dst[1] = sigma_to_natural(lut16_rebuild(p1, t));
+  }
+};
+
+template <>
+struct WRaw<2> {  // SIGNMAG8: 8 fp16 magnitudes of the row's 32-group
+  uint32_t p0, p1;
+  u32x4 c;
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t pk, __amdgpu_buffer_rsrc_t,
+                                       __amdgpu_buffer_rsrc_t s1, uint32_t po, uint32_t,
+                                       uint32_t co) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(pk, po, 0, 0);
+    p0 = v[0];
+    p1 = v[1];
+    c = __builtin_amdgcn_raw_buffer_load_b128(s1, co, 0, 0);
+  }
+  __device__ __forceinline__ void rebuild(u32x4* hi, u32x4* lo) const {
+    const SignMagTable t = signmag_table(c);
+    u32x4 h, l;
+    signmag_rebuild(p0, t, h, l);
+    hi[0] = sigma_to_natural(h);
+    lo[0] = sigma_to_natural(l);
+    signmag_rebuild(p1, t, h, l);
+    hi[1] = sigma_to_natural(h);
+    lo[1] = sigma_to_natural(l);
+  }
+};
+
+// LDS: two rebuilt weight tiles during the k loop; after it, the same bytes
+// hold the k-half partial sums that the waves of one row group exchange.
+constexpr int kWsUnits = BN * STR;                  // 16-byte units per weight tile plane
+constexpr size_t kRedBytes = 4 * 32 * 64 * 16;      // 4 row groups x 128 floats x 64 lanes
+template <int CODEC>
+constexpr size_t gemm_lds_bytes() {
+  const size_t w = (size_t)2 * (CODEC == 2 ? 2 : 1) * kWsUnits * 16;
+  return w > kRedBytes ? w : kRedBytes;
+}
 
 template <int CODEC>
-__global__ __launch_bounds__(256) void gemm_kernel(GemvProblem P, int M, int y_bf16) {
-  constexpr int NPLANES = CODEC == 2 ? 2 : 1;
-  __shared__ u32x4 xs[BM * STR];
-  __shared__ u32x4 ws[NPLANES][BN * STR];
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_kernel(
+    GemvProblem P, int M, int y_bf16, const u32x4* __restrict__ xpk, float* __restrict__ partial) {
+  constexpr int NPL = CODEC == 2 ? 2 : 1;  // SIGNMAG8: high and low bf16 planes
+  extern __shared__ u32x4 lds[];
+  auto wtile = [&](int buf, int pl) { return lds + (buf * NPL + pl) * kWsUnits; };
 
   const int64_t N = P.n, K = P.k;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int64_t n0 = (int64_t)blockIdx.x * BN, m0 = (int64_t)blockIdx.y * BM;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int mw = wave & 3, kh = wave >> 2;  // row group, k half
+  // Block -> (split, m tile, n tile).  Blocks are dealt to the 8 XCDs round
+  // robin; renumbering them so that each XCD gets a contiguous range of the
+  // split-major order keeps one split's activations (256 x k / S bf16) in that
+  // XCD's L2 instead of all of them.
+  const uint32_t G = gridDim.x, b = blockIdx.x;
+  const uint32_t L = (G & 7u) == 0 ? (b & 7u) * (G >> 3) + (b >> 3) : b;
+  const uint32_t tiles_n = (uint32_t)((P.n + BN - 1) / BN), tiles_m = (uint32_t)((M + BM - 1) / BM);
+  const uint32_t tile = L % (tiles_n * tiles_m);
+  const uint32_t nt = tile % tiles_n, mt = tile / tiles_n;
+  const int s = (int)(L / (tiles_n * tiles_m));
+  const int64_t n0 = (int64_t)nt * BN, m0 = (int64_t)mt * BM;
+  const int rows_n = (int)(N - n0 < BN ? N - n0 : BN);
+  const int rows_m = (int)(M - m0 < BM ? M - m0 : BM);
 
-  // weight-rebuild role of this thread: row wr, packed dwords 2*wq, 2*wq + 1
+  // k range of this split, in 64-k steps
+  const int T = (int)(K / BK), S = (int)(G / (tiles_n * tiles_m));
+  const int ks0 = (int)((int64_t)s * T / S), ks1 = (int)((int64_t)(s + 1) * T / S);
+  const int nsteps = ks1 - ks0;
+
+  // weight rebuild role: row wr, quarter wq of the 64-k step
   const int wr = tid >> 2, wq = tid & 3;
-  const int64_t wrow = n0 + wr;
-  const bool wrow_ok = wrow < N;
+  const uint32_t row_bytes = (uint32_t)(K >> 1);
+  const __amdgpu_buffer_rsrc_t pk = rsrc(P.packed + n0 * (K >> 1), (uint32_t)rows_n * row_bytes);
+  __amdgpu_buffer_rsrc_t s0 = pk, s1 = pk;
+  if constexpr (CODEC == 0) {
+    s0 = rsrc(P.scales + n0 * (K >> 6), (uint32_t)(rows_n * (K >> 6) * 2));
+  } else if constexpr (CODEC == 1) {
+    s0 = rsrc(P.scales + n0 * (K >> 6), (uint32_t)(rows_n * (K >> 6) * 2));
+    s1 = rsrc(P.codebook + n0 * (K >> 6) * 16, (uint32_t)(rows_n * (K >> 6) * 32));
+  } else {
+    s1 = rsrc(P.codebook + n0 * (K >> 5) * 8, (uint32_t)(rows_n * (K >> 5) * 16));
+  }
+  const uint32_t p_lane = (uint32_t)wr * row_bytes + 8u * (uint32_t)wq;
+  const uint32_t g64_lane = (uint32_t)wr * (uint32_t)(K >> 6);
+  const uint32_t g32_lane = (uint32_t)wr * (uint32_t)(K >> 5) + (uint32_t)(wq >> 1);
 
-  f32x4 acc[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  // activation role: the block's 8 row tiles of 32 in the packed layout
+  // (pack_activations); wave (mw, kh) takes row tiles 2 mw + i and, within a
+  // step, 16-k blocks kb = 2 kh + kk
+  const int r32 = lane & 31, h = lane >> 5;
+  const uint32_t kblocks = (uint32_t)(K >> 4);
+  const __amdgpu_buffer_rsrc_t xr = rsrc(xpk + (size_t)(m0 >> 5) * kblocks * 64, 8u * kblocks * 1024u);
+  const uint32_t x_lane = ((uint32_t)(2 * mw) * kblocks + 2u * (uint32_t)kh) * 1024u + 16u * (uint32_t)lane;
+  const uint32_t x_i = kblocks * 1024u;  // next row tile
 
-  for (int64_t k0 = 0; k0 < K; k0 += BK) {
-    __syncthreads();
-    // activation tile: 128 rows x 8 units
+  WRaw<CODEC> wqr[4];
+  u32x4 xq[2][2][2];
+  // Offsets of a step past the split are kOOB plus at most 2^31 - 1: still
+  // past every resource (num_records <= 2^31 since k <= 2^22), so those loads
+  // return zero without a branch.
+  auto load_w = [&](WRaw<CODEC>& r, int u) {
+    const bool in = u < nsteps;
+    const uint32_t ks = (uint32_t)(ks0 + u);
+    // byte offsets: packed, 64-group scale, codebook (LUT16 levels / SIGNMAG8 magnitudes)
+    const uint32_t co = CODEC == 1 ? 32u * (g64_lane + ks) : 16u * (g32_lane + 2u * ks);
+    r.load(pk, s0, s1, opaque(in ? p_lane + ks * 32u : kOOB),
+           opaque(in ? 2u * (g64_lane + ks) : kOOB), opaque(in ? co : kOOB));
+  };
+  auto load_x = [&](u32x4 (&xv)[2][2], int u) {
+    const bool in = u < nsteps;
+    const uint32_t base = opaque(in ? x_lane + (uint32_t)(ks0 + u) * 4096u : kOOB);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int u = tid + 256 * i;
-      const int r = u >> 3, uu = u & 7;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (m0 + r < M) v = *reinterpret_cast<const u32x4*>(P.x + (m0 + r) * K + k0 + 8 * uu);
-      xs[r * STR + uu] = x_to_sigma(v);
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+        xv[i][kk] = __builtin_amdgcn_raw_buffer_load_b128(
+            xr, base + (uint32_t)i * x_i + (uint32_t)kk * 1024u, 0, 0);
+  };
+  auto rebuild = [&](const WRaw<CODEC>& r, int buf) {
+    u32x4 hi[2], lo[2];
+    r.rebuild(hi, lo);
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      wtile(buf, 0)[wr * STR + 2 * wq + d] = hi[d];
+      if constexpr (NPL == 2) wtile(buf, 1)[wr * STR + 2 * wq + d] = lo[d];
     }
-    // weight tile: 64 rows x 8 units, rebuilt from 32 packed bytes per row
-    {
-      uint32_t p0 = 0x88888888u, p1 = 0x88888888u;
-      if (wrow_ok) {
-        const uint32_t* src = reinterpret_cast<const uint32_t*>(P.packed + wrow * (K >> 1) + (k0 >> 1));
-        p0 = src[2 * wq];
-        p1 = src[2 * wq + 1];
-      }
-      u32x4 o0, o1;
-      if constexpr (CODEC == 0) {
-        const uint32_t sb = wrow_ok ? P.scales[wrow * (K >> 6) + (k0 >> 6)] : 0u;
-        const DyadicScale d = dyadic_scale(sb);
-        const uint32_t m0c = 0x000F000Fu, m1c = 0x00F000F0u, mg = kMagic;
-        if (__builtin_expect(__any(dyadic_scale_is_wide(sb)), 0)) {
-          o0 = dyadic_rebuild_wide(p0, d, m0c, m1c, mg);
-          o1 = dyadic_rebuild_wide(p1, d, m0c, m1c, mg);
-        } else {
-          o0 = dyadic_rebuild(p0, d, m0c, m1c, mg);
-          o1 = dyadic_rebuild(p1, d, m0c, m1c, mg);
-        }
-        ws[0][wr * STR + 2 * wq] = o0;
-        ws[0][wr * STR + 2 * wq + 1] = o1;
-      } else if constexpr (CODEC == 1) {
-        u32x4 l0 = {0u, 0u, 0u, 0u}, l1 = l0;
-        uint32_t sb = 0;
-        if (wrow_ok) {
-          const int64_t g = wrow * (K >> 6) + (k0 >> 6);
-          const u32x4* lut = reinterpret_cast<const u32x4*>(P.codebook);
-          sb = P.scales[g];
-          l0 = lut[2 * g];
-          l1 = lut[2 * g + 1];
-        }
-        const Lut16Table t = lut16_table(sb, l0, l1);
-        ws[0][wr * STR + 2 * wq] = lut16_rebuild(p0, t);
-        ws[0][wr * STR + 2 * wq + 1] = lut16_rebuild(p1, t);
-      } else {
-        u32x4 c = {0u, 0u, 0u, 0u};
-        if (wrow_ok) {
-          // dwords 2wq, 2wq+1 cover k 16wq .. 16wq+15: group (k0 + 16 wq) / 32
-          const int64_t g = wrow * (K >> 5) + ((k0 + 16 * wq) >> 5);
-          c = reinterpret_cast<const u32x4*>(P.codebook)[g];
-        }
-        const SignMagTable t = signmag_table(c);
-        u32x4 h0, l0, h1, l1;
-        signmag_rebuild(p0, t, h0, l0);
-        signmag_rebuild(p1, t, h1, l1);
-        ws[0][wr * STR + 2 * wq] = h0;
-        ws[0][wr * STR + 2 * wq + 1] = h1;
-        ws[NPLANES - 1][wr * STR + 2 * wq] = l0;
-        ws[NPLANES - 1][wr * STR + 2 * wq + 1] = l1;
+  };
+
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  auto mma_step = [&](const u32x4 (&xv)[2][2], int buf) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int kb = 2 * kh + kk;
+#pragma unroll
+      for (int pl = 0; pl < NPL; ++pl) {
+        u32x4 bq[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bq[j] = wtile(buf, pl)[(32 * j + r32) * STR + 2 * kb + h];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(xv[i][kk], bq[j], acc[i][j]);
       }
     }
-    __syncthreads();
+  };
 
+  // prologue: weights of steps 0..2, activations of step 0, step 0 rebuilt
+  load_w(wqr[0], 0);
+  load_w(wqr[1], 1);
+  load_w(wqr[2], 2);
+  load_x(xq[0], 0);
+  rebuild(wqr[0], 0);
+  lds_barrier();
+
+  for (int u = 0; u < nsteps; u += 4) {
 #pragma unroll
-    for (int kb = 0; kb < BK / 32; ++kb) {
-      u32x4 a[4], b[NPLANES][2];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = xs[(wm * 64 + i * 16 + (lane & 15)) * STR + kb * 4 + (lane >> 4)];
-#pragma unroll
-      for (int pl = 0; pl < NPLANES; ++pl)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          b[pl][j] = ws[pl][(wn * 32 + j * 16 + (lane & 15)) * STR + kb * 4 + (lane >> 4)];
-#pragma unroll
-      for (int pl = 0; pl < NPLANES; ++pl)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j) acc[i][j] = mfma16x16x32(a[i], b[pl][j], acc[i][j]);
+    for (int v = 0; v < 4; ++v) {
+      load_w(wqr[(v + 3) & 3], u + v + 3);
+      load_x(xq[(v + 1) & 1], u + v + 1);
+      rebuild(wqr[(v + 1) & 3], (v + 1) & 1);
+      mma_step(xq[v & 1], v & 1);
+      lds_barrier();
     }
   }
 
-  // D[m][n] of tile (i, j) sits in lane n + 16 (m / 4), register m % 4
+  // the two k halves of a row group meet in LDS (the weight tiles are dead)
+  f32x4* const red = reinterpret_cast<f32x4*>(lds) + mw * 32 * 64 + lane;
+  if (kh == 1) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t col = n0 + wn * 32 + j * 16 + (lane & 15);
-      if (col >= N) continue;
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t r = m0 + wm * 64 + i * 16 + 4 * (lane >> 4) + e;
-        if (r < M) {
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x16& a = acc[i][j];
+          red[((i * 4 + j) * 4 + r4) * 64] =
+              (f32x4){a[4 * r4], a[4 * r4 + 1], a[4 * r4 + 2], a[4 * r4 + 3]};
+        }
+  }
+  lds_barrier();
+  if (kh == 1) return;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 o = red[((i * 4 + j) * 4 + r4) * 64];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i][j][4 * r4 + e] += o[e];
+      }
+
+  if (partial) {
+    // split partial in the MFMA register layout: 16-byte stores, 1 KB per
+    // instruction; the reduction kernel maps it back to rows and columns
+    f32x4* dst = reinterpret_cast<f32x4*>(partial) +
+                 (((size_t)s * tiles_m * tiles_n + tile) * 4 + mw) * 32 * 64 + lane;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x16& a = acc[i][j];
+          dst[((i * 4 + j) * 4 + r4) * 64] =
+              (f32x4){a[4 * r4], a[4 * r4 + 1], a[4 * r4 + 2], a[4 * r4 + 3]};
+        }
+    return;
+  }
+  // D[m][n] of tile (i, j) sits in lane n + 32 ((m / 4) % 2), register
+  // 4 (m / 8) + m % 4
+  float* const yf = reinterpret_cast<float*>(P.y);
+  uint16_t* const yh = reinterpret_cast<uint16_t*>(P.y);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int cn = 32 * j + r32;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rm = 64 * mw + 32 * i + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (cn < rows_n && rm < rows_m) {
+          const int64_t o = (m0 + rm) * N + n0 + cn;
           if (y_bf16)
-            reinterpret_cast<uint16_t*>(P.y)[r * N + col] = (uint16_t)f32_to_bf16_bits(acc[i][j][e]);
+            yh[o] = (uint16_t)f32_to_bf16_bits(acc[i][j][r]);
           else
-            reinterpret_cast<float*>(P.y)[r * N + col] = acc[i][j][e];
+            yf[o] = acc[i][j][r];
         }
       }
+  }
+}
+
+// Activations in MFMA operand order: for each 32-row tile R and 16-k block B
+// a 1 KB record whose lane l holds x[32 R + l % 32][16 B + 8 (l / 32) .. + 7]
+// (rows past M are zero).  The GEMM then reads every operand as 1 KB of
+// contiguous memory; read straight from x, each operand load would touch 32
+// rows and the L1 would stall the address path.
+__global__ __launch_bounds__(256) void pack_activations(const u32x4* __restrict__ x,
+                                                        u32x4* __restrict__ xpk, int64_t M,
+                                                        int64_t K, int64_t units) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;  // one 16-byte unit
+  if (t >= units) return;
+  const int lane = (int)(t & 63);
+  const int64_t rec = t >> 6, kblocks = K >> 4;
+  const int64_t row = (rec / kblocks) * 32 + (lane & 31);
+  const int64_t kb = rec % kblocks;
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (row < M) v = x[(row * K + kb * 16 + 8 * (lane >> 5)) >> 3];
+  xpk[t] = v;
+}
+
+// y = sum of the S split partials, added in split order.  One thread per
+// (tile, row group, 4-register group, lane) of the GEMM's register layout.
+__global__ __launch_bounds__(256) void splitk_reduce(const f32x4* __restrict__ partial, int S,
+                                                     uint32_t tiles_n, uint32_t tiles,
+                                                     int64_t M, int64_t N, void* y, int y_bf16) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;  // < tiles * 4 * 32 * 64
+  const int64_t per_split = (int64_t)tiles * 4 * 32 * 64;
+  if (t >= per_split) return;
+  f32x4 v = partial[t];
+  for (int s = 1; s < S; ++s) {
+    const f32x4 w = partial[(int64_t)s * per_split + t];
+    v += w;
+  }
+  const int lane = (int)(t & 63), r4g = (int)((t >> 6) & 31), mw = (int)((t >> 11) & 3);
+  const uint32_t tile = (uint32_t)(t >> 13);
+  const int r32 = lane & 31, h = lane >> 5;
+  const int i = r4g >> 4, j = (r4g >> 2) & 3, r4 = r4g & 3;
+  const int64_t row0 = (int64_t)(tile / tiles_n) * BM + 64 * mw + 32 * i + 8 * r4 + 4 * h;
+  const int64_t col = (int64_t)(tile % tiles_n) * BN + 32 * j + r32;
+  if (col >= N) return;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int64_t row = row0 + e;
+    if (row < M) {
+      if (y_bf16)
+        reinterpret_cast<uint16_t*>(y)[row * N + col] = (uint16_t)f32_to_bf16_bits(v[e]);
+      else
+        reinterpret_cast<float*>(y)[row * N + col] = v[e];
     }
+  }
 }
 
 }  // namespace
 
+// Splits of the k range: enough blocks for about one per CU, at least eight
+// k-steps per split, at most eight splits.
+int gemm_splits(int64_t n, int64_t k, int m, int cus) {
+  const int64_t tiles = ((n + BN - 1) / BN) * ((m + BM - 1) / BM);
+  const int64_t steps = k / BK;
+  int64_t s = tiles > 0 ? (cus + tiles - 1) / tiles : 1;
+  if (s > 8) s = 8;
+  if (s > steps / 8) s = steps / 8;
+  return s < 1 ? 1 : (int)s;
+}
+
+template <int CODEC>
+hipError_t launch_codec(const GemvProblem& p, int m, int y_bf16, const u32x4* xpk, float* partial,
+                        uint32_t blocks, hipStream_t stream) {
+  constexpr size_t lds = gemm_lds_bytes<CODEC>();
+  static bool configured = false;  // benign race: every caller sets the same value
+  if (!configured) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<CODEC>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  gemm_kernel<CODEC><<<dim3(blocks), dim3(512), lds, stream>>>(p, m, y_bf16, xpk, partial);
+  return hipGetLastError();
+}
+
+// Workspace of a (device, stream): grown on demand, kept for the process, so a
+// call only enqueues kernels.  Calls on one stream are ordered, so they may
+// share it; calls on different streams get different workspaces.
+hipError_t stream_workspace(hipStream_t stream, size_t bytes, char** out) {
+  static std::mutex mu;
+  static std::map<std::pair<int, hipStream_t>, std::pair<char*, size_t>> cache;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> g(mu);
+  auto& slot = cache[{dev, stream}];
+  if (slot.second < bytes) {
+    if (slot.first) {
+      // the stream may still be using the old buffer
+      e = hipStreamSynchronize(stream);
+      if (e != hipSuccess) return e;
+      e = hipFree(slot.first);
+      if (e != hipSuccess) return e;
+      slot = {nullptr, 0};
+    }
+    e = hipMalloc(reinterpret_cast<void**>(&slot.first), bytes);
+    if (e != hipSuccess) return e;
+    slot.second = bytes;
+  }
+  *out = slot.first;
+  return hipSuccess;
+}
+
 hipError_t launch_gemm(int codec, const GemvProblem& p, int m, int y_bf16, hipStream_t stream) {
-  const dim3 grid((uint32_t)((p.n + BN - 1) / BN), (uint32_t)((m + BM - 1) / BM));
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
+  const int S = gemm_splits(p.n, p.k, m, cus);
+  const uint32_t tiles_n = (uint32_t)((p.n + BN - 1) / BN), tiles_m = (uint32_t)((m + BM - 1) / BM);
+  const uint32_t tiles = tiles_n * tiles_m;
+  // workspace: packed activations of tiles_m * 256 rows, then S fp32 partials
+  // of tiles * 256 * 128 when the k range is split
+  const size_t xpk_bytes = (size_t)tiles_m * BM * p.k * 2;
+  const size_t per_split = (size_t)tiles * BM * BN;  // floats
+  const size_t bytes = xpk_bytes + (S > 1 ? (size_t)S * per_split * sizeof(float) : 0);
+  char* ws = nullptr;
+  hipError_t e = stream_workspace(stream, bytes, &ws);
+  if (e != hipSuccess) return e;
+  u32x4* xpk = reinterpret_cast<u32x4*>(ws);
+  float* partial = S > 1 ? reinterpret_cast<float*>(ws + xpk_bytes) : nullptr;
+  const int64_t units = (int64_t)(xpk_bytes / 16);
+  pack_activations<<<dim3((uint32_t)((units + 255) / 256)), dim3(256), 0, stream>>>(
+      reinterpret_cast<const u32x4*>(p.x), xpk, m, p.k, units);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const uint32_t blocks = tiles * (uint32_t)S;
   if (codec == 0)
-    gemm_kernel<0><<<grid, dim3(256), 0, stream>>>(p, m, y_bf16);
+    e = launch_codec<0>(p, m, y_bf16, xpk, partial, blocks, stream);
   else if (codec == 1)
-    gemm_kernel<1><<<grid, dim3(256), 0, stream>>>(p, m, y_bf16);
+    e = launch_codec<1>(p, m, y_bf16, xpk, partial, blocks, stream);
   else
-    gemm_kernel<2><<<grid, dim3(256), 0, stream>>>(p, m, y_bf16);
+    e = launch_codec<2>(p, m, y_bf16, xpk, partial, blocks, stream);
+  if (e != hipSuccess || S == 1) return e;
+  const size_t threads = per_split / 4;
+  splitk_reduce<<<dim3((uint32_t)((threads + 255) / 256)), dim3(256), 0, stream>>>(
+      reinterpret_cast<const f32x4*>(partial), S, tiles_n, tiles, m, p.n, p.y, y_bf16);
   return hipGetLastError();
 }
 

@@ -347,16 +347,23 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // rows and the L1 would stall the address path.
 __global__ __launch_bounds__(256) void pack_activations(const u32x4* __restrict__ x,
                                                         u32x4* __restrict__ xpk, int64_t M,
-                                                        int64_t K, int64_t units) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;  // one 16-byte unit
-  if (t >= units) return;
-  const int lane = (int)(t & 63);
-  const int64_t rec = t >> 6, kblocks = K >> 4;
-  const int64_t row = (rec / kblocks) * 32 + (lane & 31);
-  const int64_t kb = rec % kblocks;
-  u32x4 v = {0u, 0u, 0u, 0u};
-  if (row < M) v = x[(row * K + kb * 16 + 8 * (lane >> 5)) >> 3];
-  xpk[t] = v;
+                                                        int64_t K) {
+  // block = (row tile R, 64-k slab c): 32 rows x 128 bytes read row-contiguous
+  // into LDS, written out as the slab's four 1 KB records
+  __shared__ u32x4 t[32][9];
+  const int tid = threadIdx.x;
+  const int64_t kblocks = K >> 4, slabs = K >> 6;
+  const int64_t R = (int64_t)blockIdx.x / slabs, c = (int64_t)blockIdx.x % slabs;
+  {
+    const int r = tid >> 3, u = tid & 7;
+    const int64_t row = R * 32 + r;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (row < M) v = x[(row * K + c * 64) / 8 + u];
+    t[r][u] = v;
+  }
+  __syncthreads();
+  const int rec = tid >> 6, lane = tid & 63;  // record rec = 16-k block 4c + rec
+  xpk[(R * kblocks + 4 * c + rec) * 64 + lane] = t[lane & 31][2 * rec + (lane >> 5)];
 }
 
 // y = sum of the S split partials, added in split order.  One thread per
@@ -465,9 +472,8 @@ hipError_t launch_gemm(int codec, const GemvProblem& p, int m, int y_bf16, hipSt
   if (e != hipSuccess) return e;
   u32x4* xpk = reinterpret_cast<u32x4*>(ws);
   float* partial = S > 1 ? reinterpret_cast<float*>(ws + xpk_bytes) : nullptr;
-  const int64_t units = (int64_t)(xpk_bytes / 16);
-  pack_activations<<<dim3((uint32_t)((units + 255) / 256)), dim3(256), 0, stream>>>(
-      reinterpret_cast<const u32x4*>(p.x), xpk, m, p.k, units);
+  pack_activations<<<dim3((uint32_t)(tiles_m * 8 * (p.k / 64))), dim3(256), 0, stream>>>(
+      reinterpret_cast<const u32x4*>(p.x), xpk, m, p.k);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const uint32_t blocks = tiles * (uint32_t)S;

@@ -39,9 +39,14 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only-headline", action="store_true",
-                    help="time only the batched decode pass (for profiler runs)")
-    return ap.parse_args()
+    ap.add_argument("--only", choices=["headline", "gemm", "copy"], default=None,
+                    help="run one target only (for profiler runs): the batched decode pass, "
+                         "the M=256 GEMM, or a 1 GiB device copy that calibrates HBM counters")
+    ap.add_argument("--only-headline", action="store_true", help="same as --only headline")
+    a = ap.parse_args()
+    if a.only_headline:
+        a.only = "headline"
+    return a
 
 
 def log(msg):
@@ -85,6 +90,20 @@ def timed(fn, stream, steps, warmup):
     return e0.elapsed_time(e1) / steps  # ms per step
 
 
+def time_gemm(w4, synthetic, torch, dev, stream, args):
+    """Prefill GEMM, M = 256, K = N = 8192, dyadic weights N(0, 0.02^2): ms per
+    call (pack + GEMM + split-k reduction) and TFLOP/s."""
+    log("prefill GEMM M=256, K=N=8192")
+    W = synthetic.normal_bf16_device((8192, 8192), 0.02, synthetic.seed(5, 0, 0), dev)
+    X = synthetic.normal_bf16_device((256, 8192), 1.0, synthetic.seed(5, 0, 1), dev)
+    P, S = w4.w4_quantize_pack(W, w4.W4_DYADIC)
+    del W
+    Y = torch.empty((256, 8192), dtype=torch.float32, device=dev)
+    ms_g = timed(lambda: w4.w4_gemm(P, X, w4.W4_DYADIC, scales=S, y=Y, stream=stream),
+                 stream, args.steps, args.warmup)
+    return ms_g, 2 * 256 * 8192 * 8192 / (ms_g * 1e-3) / 1e12
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -99,6 +118,20 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
+
+    if args.only == "copy":
+        # plain device copy of a known size: what FETCH_SIZE / WRITE_SIZE read
+        # for it calibrates the counters (bytes per reported KiB)
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        ms_c = timed(lambda: dst.copy_(src), stream, args.steps, args.warmup)
+        print(json.dumps({"target": "copy", "bytes_read": 1 << 30, "bytes_written": 1 << 30,
+                          "ms": ms_c, "GB/s": 2 * (1 << 30) / (ms_c * 1e-3) / 1e9}), flush=True)
+        return
+    if args.only == "gemm":
+        ms_g, tf = time_gemm(w4, synthetic, torch, dev, stream, args)
+        print(json.dumps({"target": "gemm", "ms": ms_g, "TFLOP/s": tf}), flush=True)
+        return
 
     # ---------------------------------------------------------- config 2 stack
     shapes = synthetic.llama1b_stack_shapes()
@@ -123,7 +156,7 @@ def main():
     rows = {}
     traffic = stored_traffic("gemv_batched_dyadic_m1_llama1b_stack", gemv_bytes)
 
-    if not args.only_headline:
+    if args.only is None:
         # the same pass as 168 separate calls
         def per_call():
             for m in mats:
@@ -159,19 +192,15 @@ def main():
         del m["w"]
     torch.cuda.empty_cache()
 
-    if not args.only_headline:
+    if args.only is None:
         # ------------------------------------------------------ config 5 GEMM
-        log("prefill GEMM M=256, K=N=8192")
+        ms_g, tf = time_gemm(w4, synthetic, torch, dev, stream, args)
+        rows["gemm_m256_k8192_n8192"] = {"ms": ms_g, "TFLOP/s": tf,
+                                         "frac_of_bf16_peak": tf / BF16_MFMA_PEAK_TFLOPS}
         W = synthetic.normal_bf16_device((8192, 8192), 0.02, synthetic.seed(5, 0, 0), dev)
         X = synthetic.normal_bf16_device((256, 8192), 1.0, synthetic.seed(5, 0, 1), dev)
         P, S = w4.w4_quantize_pack(W, w4.W4_DYADIC)
         Y = torch.empty((256, 8192), dtype=torch.float32, device=dev)
-        ms_g = timed(lambda: w4.w4_gemm(P, X, w4.W4_DYADIC, scales=S, y=Y, stream=stream),
-                     stream, args.steps, args.warmup)
-        flops = 2 * 256 * 8192 * 8192
-        tf = flops / (ms_g * 1e-3) / 1e12
-        rows["gemm_m256_k8192_n8192"] = {"ms": ms_g, "TFLOP/s": tf,
-                                         "frac_of_bf16_peak": tf / BF16_MFMA_PEAK_TFLOPS}
         ms_q5 = timed(lambda: w4.w4_quantize_pack(W, w4.W4_DYADIC, packed=P, scales=S,
                                                   stream=stream), stream, 10, 2)
         qb = 2 * 8192 * 8192 + 8192 * 4096 + 2 * 8192 * 128
@@ -186,7 +215,7 @@ def main():
 
     # ---------------------------------------------------------- CPU baseline
     cpu = None
-    if not args.no_cpu_baseline and not args.only_headline:
+    if not args.no_cpu_baseline and args.only is None:
         cpu = cpu_baseline(mats, shapes)
 
     out = {
@@ -214,39 +243,42 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+CPU_BLOCKS = 8  # decoder blocks of the stack timed on the CPU (about 10-15 s of work)
+
+
 def cpu_baseline(mats, shapes):
-    """The oracle (numpy dequant + fp64 matmul, one thread) on the first block
-    of the stack (7 matrices, 51.4 M weights).  Its input is the same bf16
-    weight quantized by the oracle itself on the host."""
+    """The oracle (numpy dequant + fp64 GEMV, one thread) on the first
+    CPU_BLOCKS decoder blocks of the stack.  Each weight is regenerated on the
+    device, copied to the host and quantized by the oracle's own C routine
+    (untimed); the timed part is the oracle's dequant + matmul per matrix."""
     import numpy as np
     import torch
+    import synthetic
     from threadpoolctl import threadpool_limits
     from oracle import dyadic, matmul, native, packing
+    from oracle.bits import bf16_to_f64
 
-    log("cpu baseline: oracle on the first block")
-    sample = list(range(7))
-    host = []
+    sample = list(range(7 * CPU_BLOCKS))
+    log(f"cpu baseline: oracle on {len(sample)} matrices")
+    nbytes, weights, dt = 0, 0, 0.0
     for i in sample:
         n, k = shapes[i]
-        # regenerate the same bf16 weight on the device and copy it back
-        import synthetic
         w = synthetic.student_t_bf16_device((n, k), 4, 0.02, synthetic.seed(2, i, 0), "cuda")
         wb = w.view(torch.int16).cpu().numpy().view(np.uint16)
+        del w
         xb = mats[i]["x"].view(torch.int16).cpu().numpy().view(np.uint16)
         idx, s = native.dyadic_quantize(wb)
-        host.append((packing.pack(idx), s, xb))
-        del w
-    nbytes = sum(n * k // 2 + 2 * n * (k // 64) + 2 * k + 4 * n for n, k in (shapes[i] for i in sample))
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        for p, s, xb in host:
-            w_hat = dyadic.dequant(p, s)
-            from oracle.bits import bf16_to_f64
-            matmul.gemm_ref(xb, bf16_to_f64(w_hat))
-        dt = time.perf_counter() - t0
+        p = packing.pack(idx)
+        del wb, idx
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            matmul.gemm_ref(xb, bf16_to_f64(dyadic.dequant(p, s)))
+            dt += time.perf_counter() - t0
+        nbytes += n * k // 2 + 2 * n * (k // 64) + 2 * k + 4 * n
+        weights += n * k
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "first decoder block of the stack (7 matrices, 51,380,224 weights): "
-                      "numpy dequant + fp64 GEMV, one thread",
+            "sample": f"first {CPU_BLOCKS} decoder blocks of the stack ({len(sample)} matrices, "
+                      f"{weights:,} weights): numpy dequant + fp64 GEMV, one thread",
             "seconds": round(dt, 2)}
 
 

@@ -104,6 +104,84 @@ def time_gemm(w4, synthetic, torch, dev, stream, args):
     return ms_g, 2 * 256 * 8192 * 8192 / (ms_g * 1e-3) / 1e12
 
 
+def quantile_levels(w, group, n_levels, magnitude):
+    """Per-group levels for timing runs: the k-means starting point (sorted
+    values at 4k + 2, as normalised values for LUT16 or magnitudes for
+    SIGNMAG8), built with torch on the device.  Throughput does not depend on
+    the levels' values; parity of fitted levels is checked in the tests."""
+    import torch
+    n, k = w.shape
+    g = w.float().reshape(n, k // group, group)
+    if magnitude:
+        v = torch.sort(g.abs(), dim=-1).values
+        return v[..., 2::4][..., :n_levels].to(torch.float16).contiguous()
+    s = g.abs().amax(dim=-1, keepdim=True)
+    u = torch.where(s > 0, g / torch.where(s > 0, s, torch.ones_like(s)), torch.zeros_like(g))
+    v = torch.sort(u, dim=-1).values
+    return (s.squeeze(-1).to(torch.bfloat16).contiguous(),
+            v[..., 2::4][..., :n_levels].to(torch.bfloat16).contiguous())
+
+
+def other_configs(w4, synthetic, torch, dev, stream, args):
+    """Rows for the 2048^2 single GEMV, the 3.9B-sized LUT16 GEMVs and the 2B
+    SIGNMAG8 dequant + batched GEMV."""
+    rows = {}
+    # single 2048^2 DYADIC weight, N(0, 0.02^2), m = 1: one call's latency
+    W = synthetic.normal_bf16_device((2048, 2048), 0.02, synthetic.seed(0, 0, 0), dev)
+    x = synthetic.normal_bf16_device((1, 2048), 1.0, synthetic.seed(0, 0, 1), dev)
+    P, S = w4.w4_quantize_pack(W, w4.W4_DYADIC)
+    y = torch.empty((1, 2048), device=dev)
+    ms = timed(lambda: w4.w4_gemv(P, x, w4.W4_DYADIC, scales=S, y=y, stream=stream), stream,
+               args.steps, args.warmup)
+    b = 2048 * 1024 + 2 * 2048 * 32 + 2 * 2048 + 4 * 2048
+    rows["gemv_m1_2048x2048_single_call"] = {"ms": ms, "GB/s": b / (ms * 1e-3) / 1e9}
+    del W, P, S
+
+    # LUT16 on the 3.9B-sized shapes, m = 1, 4, 16
+    log("LUT16 3.9B-sized GEMVs")
+    for i, (n, k) in enumerate([(4096, 4096), (11008, 4096), (4096, 11008)]):
+        W = synthetic.normal_outliers_bf16_device((n, k), 0.015, 0.001, 0.15,
+                                                  synthetic.seed(3, i, 0), dev)
+        sc, L = quantile_levels(W, 64, 16, magnitude=False)
+        P, _ = w4.w4_quantize_pack(W, w4.W4_LUT16, scales=sc, codebook=L)
+        del W
+        for m in (1, 4, 16):
+            x = synthetic.normal_bf16_device((m, k), 1.0, synthetic.seed(3, i, 1), dev)
+            y = torch.empty((m, n), device=dev)
+            ms = timed(lambda: w4.w4_gemv(P, x, w4.W4_LUT16, scales=sc, codebook=L, y=y,
+                                          stream=stream), stream, args.steps, args.warmup)
+            b = n * k // 2 + n * (k // 64) * 34 + 2 * m * k + 4 * m * n
+            rows[f"lut16_gemv_m{m}_{n}x{k}"] = {"ms": ms, "GB/s": b / (ms * 1e-3) / 1e9}
+        del P, sc, L
+
+    # SIGNMAG8: 224 x 2048^2, Student-t nu = 5; dense dequant + one batched m = 1 GEMV
+    log("SIGNMAG8 2B stack")
+    probs, total = [], 0
+    for i in range(224):
+        W = synthetic.student_t_bf16_device((2048, 2048), 5, 0.02, synthetic.seed(4, i, 0), dev)
+        cb = quantile_levels(W, 32, 8, magnitude=True)
+        P, _ = w4.w4_quantize_pack(W, w4.W4_SIGNMAG8, codebook=cb)
+        del W
+        x = synthetic.normal_bf16_device((1, 2048), 1.0, synthetic.seed(4, i, 1), dev)
+        probs.append({"packed": P, "codebook": cb, "x": x, "y": torch.empty((1, 2048), device=dev)})
+        total += 2048 * 1024 + 2048 * 64 * 16 + 2 * 2048 + 4 * 2048
+    batch = w4.w4_gemv_batched_plan(probs, w4.W4_SIGNMAG8)
+    ms = timed(lambda: batch(stream), stream, args.steps, args.warmup)
+    nominal = 224 * (2048 * 2048 * 4.25 / 8 + 2 * 2048 + 4 * 2048)
+    rows["signmag8_gemv_m1_224x2048x2048"] = {
+        "ms": ms, "GB/s": total / (ms * 1e-3) / 1e9,
+        "GB/s_at_nominal_4.25_bits": nominal / (ms * 1e-3) / 1e9}
+    out = torch.empty((2048, 2048), dtype=torch.float16, device=dev)
+    p0 = probs[0]
+    ms = timed(lambda: w4.w4_unpack_dequant(p0["packed"], w4.W4_SIGNMAG8, codebook=p0["codebook"],
+                                            out=out, stream=stream), stream, args.steps, args.warmup)
+    b = 2048 * 1024 + 2048 * 64 * 16 + 2 * 2048 * 2048
+    rows["signmag8_dequant_2048x2048"] = {"ms": ms, "GB/s": b / (ms * 1e-3) / 1e9}
+    del probs, batch, out
+    torch.cuda.empty_cache()
+    return rows
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -212,6 +290,9 @@ def main():
         vb = 8192 * 4096 + 2 * 8192 * 128 + 2 * 8192 + 4 * 8192
         rows["gemv_m1_8192x8192"] = {"ms": ms_v5, "GB/s": vb / (ms_v5 * 1e-3) / 1e9}
         del W, X, P, S, Y
+
+    if args.only is None:
+        rows.update(other_configs(w4, synthetic, torch, dev, stream, args))
 
     # ---------------------------------------------------------- CPU baseline
     cpu = None

@@ -20,7 +20,9 @@
  * Conventions shared by every call
  * --------------------------------
  *  - Pointers are DEVICE pointers owned by the caller; the library keeps none
- *    of them after returning and allocates no memory.
+ *    of them after returning.  It allocates no memory, except w4_gemm, which
+ *    keeps one device workspace per (device, stream) for the process's life
+ *    (see there).
  *  - `stream` is a hipStream_t (NULL = the null stream).  A call only enqueues
  *    work on it; it never synchronises the stream or the device.
  *  - All validation happens on the host before anything is enqueued.  On any
@@ -57,13 +59,18 @@ extern "C" {
 typedef enum {
   W4_OK = 0,
   W4_EINVAL = 1,       /* NULL pointer for a non-empty buffer, bad enum, negative size */
-  W4_ESHAPE = 2,       /* k not a multiple of 64, m outside the call's range           */
+  W4_ESHAPE = 2,       /* k not a multiple of 64, m outside the call's range, k above
+                          W4_MAX_MATMUL_K for w4_gemv / w4_gemm / the batched GEMV     */
   W4_EALIGN = 3,       /* a pointer not aligned as the call states                      */
   W4_EUNSUPPORTED = 4, /* a codec / dtype combination the call does not provide         */
   W4_EHIP = 5          /* the kernel launch failed (hipGetLastError)                    */
 } w4_status;
 
 typedef enum { W4_DYADIC = 0, W4_LUT16 = 1, W4_SIGNMAG8 = 2 } w4_codec;
+
+/* Largest k of a matrix product call: keeps every per-block byte offset of the
+ * kernels within 32 bits. */
+#define W4_MAX_MATMUL_K 4194304
 typedef enum { W4_F32 = 0, W4_BF16 = 1, W4_F16 = 2 } w4_dtype;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -119,6 +126,14 @@ w4_status w4_gemv(int32_t codec, int64_t n, int64_t k, const uint8_t* packed,
  * Y[i][r] = sum_c X[i][c] * w_hat[r][c] with bf16 MFMA and fp32 accumulation;
  * the weight tiles are rebuilt into LDS.  [KM] sec. 4.1 (the 4-bit mixed kernel
  * band, m up to 256).  Same arguments as w4_gemv; m >= 1 (tuned for m >= 128).
+ * Workspace: the call enqueues up to three kernels (an activation re-layout,
+ * the product, and an in-order sum of the k-split partials) that use a device
+ * buffer of ceil(m/256) * 256 * k * 2 bytes plus, when k is split S ways,
+ * S * ceil(m/256) * 256 * ceil(n/128) * 128 * 4 bytes.  The library keeps one
+ * such buffer per (device, stream), grown on demand with hipMalloc (growing
+ * waits for the stream and frees the old buffer) and never freed, so calls on
+ * one stream are ordered and calls on different streams never share it.
+ * Additional error: W4_EHIP when the workspace cannot be allocated.
  */
 w4_status w4_gemm(int32_t codec, int64_t n, int64_t k, const uint8_t* packed,
                   const uint16_t* scales, const uint16_t* codebook, const uint16_t* x,

@@ -44,9 +44,10 @@ def test_group_sizes_and_status_strings(w4):
         assert w4.w4_status_str(s).startswith("W4_")
 
 
-def _gemv(w4, codec=0, n=16, k=64, packed=16, scales=16, cb=16, x=16, m=1, y=16, yd=0):
+def _gemv(w4, codec=0, n=16, k=64, packed=16, scales=16, cb=16, x=16, m=1, y=16, yd=0,
+          fn="w4_gemv"):
     P = lambda v: None if v is None else ctypes.c_void_p(v)
-    return w4._lib.w4_gemv(codec, n, k, P(packed), P(scales), P(cb), P(x), m, P(y), yd, None)
+    return getattr(w4._lib, fn)(codec, n, k, P(packed), P(scales), P(cb), P(x), m, P(y), yd, None)
 
 
 def test_validation_errors(w4):
@@ -67,6 +68,9 @@ def test_validation_errors(w4):
     assert _gemv(w4, y=None) == E["inval"]
     assert _gemv(w4, y=18) == E["align"]
     assert _gemv(w4, yd=2) == E["unsup"]
+    # k beyond W4_MAX_MATMUL_K (4,194,304) is rejected before any launch
+    assert _gemv(w4, k=4194304 + 64) == E["shape"]
+    assert _gemv(w4, k=4194304 + 64, fn="w4_gemm") == E["shape"]
     # empty problems are accepted without touching anything
     assert _gemv(w4, n=0, packed=None, scales=None, x=None, y=None) == 0
     assert _gemv(w4, m=0, x=None, y=None) == 0

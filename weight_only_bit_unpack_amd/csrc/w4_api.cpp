@@ -44,6 +44,7 @@ w4_status check_matmul(int32_t codec, int64_t n, int64_t k, const uint8_t* packe
   if (m < 0) return W4_EINVAL;
   if (m > m_max) return W4_ESHAPE;
   if (y_dtype != W4_F32 && y_dtype != W4_BF16) return W4_EUNSUPPORTED;
+  if (k > W4_MAX_MATMUL_K) return W4_ESHAPE;
   if (m == 0 || n == 0) return W4_OK;
   if (!y) return W4_EINVAL;
   if (!aligned(y, y_dtype == W4_F32 ? 4 : 2)) return W4_EALIGN;

@@ -156,7 +156,8 @@ w4_status w4_gemm(int32_t codec, int64_t n, int64_t k, const uint8_t* packed,
  *    kernel trusts the device copy: it must equal an array the plan accepted.
  * Errors: W4_EINVAL / W4_ESHAPE / W4_EALIGN / W4_EUNSUPPORTED as for w4_gemv
  * (the plan reports the first failing problem's status and writes nothing to
- * *info); W4_ESHAPE when the problems need more than 2^31 - 1 tiles.
+ * *info); W4_ESHAPE when the problems need more than 2^31 - 1 tiles;
+ * w4_gemv_batched returns W4_EINVAL when m differs from info->m.
  */
 typedef struct {
   const uint8_t* packed;
@@ -174,7 +175,7 @@ typedef struct {
   int64_t k_min;       /* smallest k */
   int64_t k_max;       /* largest k (sizes the kernel's LDS) */
   int32_t count;       /* number of problems */
-  int32_t reserved;
+  int32_t m;           /* the plan's m; w4_gemv_batched must be called with it */
 } w4_gemv_batch_info;
 
 w4_status w4_gemv_batched_plan(int32_t codec, int32_t m, int32_t y_dtype,

@@ -96,16 +96,23 @@ def test_batched_plan_validation(w4):
     arr[2] = w4.W4Problem(8, 8, 8, 8, 8, 7, 7, 7)   # past count: never touched
     info = w4.W4BatchInfo()
     plan = lambda m: w4._lib.w4_gemv_batched_plan(0, m, 0, arr, 2, ctypes.byref(info))
-    assert plan(1) == 0
-    # largest k first: problem 1 (k = 192, 3 tiles) gets tiles 0..2, problem 0 tiles 3..4
+    # m = 16: 64-row blocks; largest k first: problem 1 (k = 192, 3 blocks) gets
+    # blocks 0..2, problem 0 blocks 3..4
+    assert plan(16) == 0
     assert info.total_tiles == 2 + 3 and arr[1].tile_begin == 0 and arr[0].tile_begin == 3
-    assert (info.k_min, info.k_max, info.count) == (128, 192, 2)
+    assert (info.k_min, info.k_max, info.count, info.m) == (128, 192, 2, 16)
     assert (arr[2].n, arr[2].k, arr[2].tile_begin) == (7, 7, 7)
+    # m = 1: blocks of 64 * t rows (t row tiles per wave); the same order
+    assert plan(1) == 0 and info.m == 1
+    rows = next(r for r in (64, 128, 192, 256)
+                if info.total_tiles == -(-100 // r) + -(-164 // r) and arr[0].tile_begin == -(-164 // r))
+    assert arr[1].tile_begin == 0 and rows >= 64
+    assert w4._lib.w4_gemv_batched(0, 2, 0, ctypes.c_void_p(16), ctypes.byref(info), None) == 1
     arr[1].k = 100
     assert plan(1) == 2
     assert plan(17) == 2
     assert w4._lib.w4_gemv_batched(0, 1, 0, ctypes.c_void_p(8), ctypes.byref(info), None) == 3
-    bad = w4.W4BatchInfo(5, -1, 128, 2, 0)
+    bad = w4.W4BatchInfo(5, -1, 128, 2, 1)
     assert w4._lib.w4_gemv_batched(0, 1, 0, ctypes.c_void_p(16), ctypes.byref(bad), None) == 1
-    empty = w4.W4BatchInfo(0, 0, 0, 0, 0)
+    empty = w4.W4BatchInfo(0, 0, 0, 0, 1)
     assert w4._lib.w4_gemv_batched(0, 1, 0, None, ctypes.byref(empty), None) == 0

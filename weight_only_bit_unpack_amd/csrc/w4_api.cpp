@@ -151,7 +151,6 @@ w4_status w4_gemv_batched_plan(int32_t codec, int32_t m, int32_t y_dtype,
   if (!info || count < 0 || !problems) return W4_EINVAL;
   if (!valid_codec(codec)) return W4_EINVAL;
   if (m < 1) return m < 0 ? W4_EINVAL : W4_ESHAPE;
-  const int64_t rows = w4::gemv_rows_per_block(1);
   for (int32_t i = 0; i < count; ++i) {
     const w4_gemv_problem& p = problems[i];
     w4_status st = check_matmul(codec, p.n, p.k, p.packed, p.scales, p.codebook, p.x, m, p.y,
@@ -162,8 +161,9 @@ w4_status w4_gemv_batched_plan(int32_t codec, int32_t m, int32_t y_dtype,
   for (int32_t i = 0; i < count; ++i) {
     if (problems[i].k > kmax) kmax = problems[i].k;
     if (problems[i].k < kmin) kmin = problems[i].k;
-    total += (problems[i].n + rows - 1) / rows;
   }
+  const int64_t rows = w4::gemv_batched_rows(m, kmax);
+  for (int32_t i = 0; i < count; ++i) total += (problems[i].n + rows - 1) / rows;
   if (total > 0x7FFFFFFF) return W4_ESHAPE;
   // Work is handed out in tile order; giving the longest rows (largest k) the
   // first tiles leaves short tiles for the end of the launch.
@@ -180,7 +180,7 @@ w4_status w4_gemv_batched_plan(int32_t codec, int32_t m, int32_t y_dtype,
   info->k_min = kmin;
   info->k_max = kmax;
   info->count = count;
-  info->reserved = 0;
+  info->m = m;
   return W4_OK;
 }
 
@@ -190,6 +190,7 @@ w4_status w4_gemv_batched(int32_t codec, int32_t m, int32_t y_dtype,
   if (!info || !valid_codec(codec)) return W4_EINVAL;
   if (info->count < 0 || info->total_tiles < 0 || info->k_max < 0 || info->k_min < 0)
     return W4_EINVAL;
+  if (info->m != m) return W4_EINVAL;  // the work numbering depends on m
   if (m < 1) return m < 0 ? W4_EINVAL : W4_ESHAPE;
   if (m > kGemvMaxM) return W4_ESHAPE;
   if (y_dtype != W4_F32 && y_dtype != W4_BF16) return W4_EUNSUPPORTED;

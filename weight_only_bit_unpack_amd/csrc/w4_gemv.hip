@@ -409,6 +409,8 @@ hipError_t launch_gemv(int codec, const GemvProblem& p, int m, int y_bf16, hipSt
   return launch_codec<2>(p, m, y_bf16, stream);
 }
 
+int gemv_batched_rows(int, int64_t) { return gemv_rows_per_block(1); }
+
 hipError_t launch_gemv_batched(int codec, const GemvProblem* probs_dev, int count,
                                int64_t total_tiles, int64_t k_max, int m, int y_bf16,
                                hipStream_t stream) {

@@ -33,7 +33,11 @@ int gemv_pick_ksplit(int64_t n, int64_t k, int m);
 
 hipError_t launch_gemv(int codec, const GemvProblem& p, int m, int y_bf16, hipStream_t stream);
 
-// probs_dev: count problems with tile_begin set by the plan (blocks of 64 rows)
+// Rows per block of the batched GEMV for this m and largest k (the plan numbers
+// the blocks with it).
+int gemv_batched_rows(int m, int64_t k_max);
+// probs_dev: count problems with tile_begin set by the plan (blocks of
+// gemv_batched_rows(m, k_max) rows)
 hipError_t launch_gemv_batched(int codec, const GemvProblem* probs_dev, int count,
                                int64_t total_tiles, int64_t k_max, int m, int y_bf16,
                                hipStream_t stream);

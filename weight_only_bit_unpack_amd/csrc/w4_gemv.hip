@@ -177,7 +177,7 @@ __host__ __device__ __forceinline__ int64_t gemv_chunk(int m, int xs_units, int6
   return kc < kpad ? kc : kpad;
 }
 
-constexpr int kXFirst = 4;  // x units per thread loaded ahead of the weight prefetch
+constexpr int kXFirst = 1;  // x units per thread loaded ahead of the weight prefetch
 
 template <int CODEC, int KSPLIT, bool BATCHED>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvProblem single, const GemvProblem* probs,
@@ -278,7 +278,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvProblem single, const Gem
       return (uu < units && kk < K) ? (uint32_t)((mrow * K + kk) * 2) : kOOB;
     };
     lds_barrier();  // the previous chunk's LDS reads are done
-    // activations first, then this wave's first four weight steps
+    // activations first, then this wave's first three weight steps
     u32x4 xv[kXFirst];
     int xrow[kXFirst], xu[kXFirst];
 #pragma unroll
@@ -287,15 +287,13 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvProblem single, const Gem
       xv[i] = __builtin_amdgcn_raw_buffer_load_b128(S.x, i < nslots ? o : kOOB, 0, 0);
     }
     // (issue order pinned: the loop's waits assume the buffers left in this order)
-    Raw<CODEC> ra, rb, rc, rd;
+    Raw<CODEC> ra, rb, rc;
     __builtin_amdgcn_sched_barrier(0);
     fetch(ra, 0);
     __builtin_amdgcn_sched_barrier(0);
     fetch(rb, 1);
     __builtin_amdgcn_sched_barrier(0);
     fetch(rc, 2);
-    __builtin_amdgcn_sched_barrier(0);
-    fetch(rd, 3);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < kXFirst; ++i)
@@ -312,24 +310,20 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvProblem single, const Gem
       const u32x4* xa = &xs[mr * row_units + 32 * step_of(i) + 8 * q];
       r.apply(sh, [&](int j, const u32x4& b) { acc = mfma16x16x32(xa[j], b, acc); });
     };
-    // four buffers in rotation: a buffer is refilled right after it is used,
-    // so three steps stay in flight while one is computed and no live buffer
-    // is ever copied (a copy would have to wait for its load)
+    // three buffers in rotation: a buffer is refilled right after it is used,
+    // so two steps stay in flight while one is computed and no live buffer is
+    // ever copied (a copy would have to wait for its load)
     int i = 0;
-    for (; i + 4 <= nw; i += 4) {
+    for (; i + 3 <= nw; i += 3) {  // the last one or two steps follow the loop
       compute(ra, i);
-      fetch(ra, i + 4);
+      fetch(ra, i + 3);
       compute(rb, i + 1);
-      fetch(rb, i + 5);
+      fetch(rb, i + 4);
       compute(rc, i + 2);
-      fetch(rc, i + 6);
-      compute(rd, i + 3);
-      fetch(rd, i + 7);
+      fetch(rc, i + 5);
     }
-    // the last one to three steps, after the loop so its body stays branch-free
     if (i < nw) compute(ra, i);
     if (i + 1 < nw) compute(rb, i + 1);
-    if (i + 2 < nw) compute(rc, i + 2);
   }
 
   if constexpr (KSPLIT > 1) {

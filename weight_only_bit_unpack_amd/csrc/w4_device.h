@@ -92,6 +92,34 @@ __device__ __forceinline__ uint32_t wide_pair(uint32_t h2, float off, float s) {
   return cvt_pk_bf16((float)d.x * s, (float)d.y * s);
 }
 
+// Branch-free form valid for every scale: d = h - off in fp16 (exact small
+// integers: n - 8, or 16 (n - 8) for the high nibbles), then one fp32
+// product per value (v_fma_mix with a -0 addend leaves the product as is) and
+// the one RNE.  One VALU per pair more than the fast form; used where a
+// uniform branch on the scale would split the instruction stream.
+// The addend nz is -0.0f hidden from the optimiser (see dyadic_rebuild_any):
+// fma(d, s, -0) is d * s for every d and s, and the fma keeps the fp16 operand
+// inside v_fma_mix instead of a separate conversion.
+__device__ __forceinline__ uint32_t sub_mul_pair(uint32_t h2, uint32_t off2, float s, float nz) {
+  const f16x2 d = __builtin_bit_cast(f16x2, h2) - __builtin_bit_cast(f16x2, off2);
+  return cvt_pk_bf16(__builtin_fmaf((float)d.x, s, nz), __builtin_fmaf((float)d.y, s, nz));
+}
+
+// One packed dword -> 8 bf16 values in SIGMA order, any scale.
+// nz: -0.0f passed through an opaque register by the caller.
+__device__ __forceinline__ u32x4 dyadic_rebuild_any(uint32_t p, const DyadicScale& d, uint32_t m0,
+                                                    uint32_t m1, uint32_t mg, float nz) {
+  const uint32_t q = p >> 8;
+  const uint32_t o1 = 0x64086408u;  // fp16 1032 twice
+  const uint32_t o2 = 0x64806480u;  // fp16 1152 twice
+  u32x4 r;
+  r.x = sub_mul_pair(and_or(p, m0, mg), o1, d.s8, nz);
+  r.y = sub_mul_pair(and_or(p, m1, mg), o2, d.s8_16, nz);
+  r.z = sub_mul_pair(and_or(q, m0, mg), o1, d.s8, nz);
+  r.w = sub_mul_pair(and_or(q, m1, mg), o2, d.s8_16, nz);
+  return r;
+}
+
 // One packed dword -> 8 bf16 values in SIGMA order.
 __device__ __forceinline__ u32x4 dyadic_rebuild(uint32_t p, const DyadicScale& d, uint32_t m0,
                                                 uint32_t m1, uint32_t mg) {

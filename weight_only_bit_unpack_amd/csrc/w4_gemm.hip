@@ -74,13 +74,9 @@ struct WRaw<0> {  // DYADIC: bf16 scale of the row's 64-group
   __device__ __forceinline__ void rebuild(u32x4* dst, u32x4*) const {
     const DyadicScale d = dyadic_scale(sb);
     const uint32_t m0 = 0x000F000Fu, m1 = 0x00F000F0u, mg = kMagic;
-    if (__builtin_expect(__any(dyadic_scale_is_wide(sb)), 0)) {
-      dst[0] = sigma_to_natural(dyadic_rebuild_wide(p0, d, m0, m1, mg));
-      dst[1] = sigma_to_natural(dyadic_rebuild_wide(p1, d, m0, m1, mg));
-    } else {
-      dst[0] = sigma_to_natural(dyadic_rebuild(p0, d, m0, m1, mg));
-      dst[1] = sigma_to_natural(dyadic_rebuild(p1, d, m0, m1, mg));
-    }
+    const float nz = __builtin_bit_cast(float, opaque(0x80000000u));
+    dst[0] = sigma_to_natural(dyadic_rebuild_any(p0, d, m0, m1, mg, nz));
+    dst[1] = sigma_to_natural(dyadic_rebuild_any(p1, d, m0, m1, mg, nz));
   }
 };
 

@@ -115,7 +115,14 @@ w4_status w4_unpack_dequant(int32_t codec, int64_t n, int64_t k, const uint8_t* 
  * the codebook in registers).
  * x: bf16 [m][k], 16-byte aligned.  m: 1..16 (m == 0: nothing to do).
  * y: [m][n] of y_dtype W4_F32 (4-byte aligned) or W4_BF16 (RNE, 2-byte aligned).
- * The result is within 1e-3 * sum_c |x w_hat| + 1e-6 of the exact sum.
+ * The result is within 1e-3 * sum_c |x w_hat| + 1e-6 of the exact sum, and the
+ * same inputs always give the same bits.
+ * Workspace: with m >= 2 and n <= 65536 the call may split k into S <= 32
+ * slices across blocks and enqueue a second kernel that adds the slices' fp32
+ * partial sums in slice order; the partials use a device buffer of
+ * S * m * n * 4 bytes that the library keeps per (device, stream) as for
+ * w4_gemm (grown on demand with hipMalloc, never freed).  m == 1 uses none.
+ * Additional error: W4_EHIP when that buffer cannot be allocated.
  */
 w4_status w4_gemv(int32_t codec, int64_t n, int64_t k, const uint8_t* packed,
                   const uint16_t* scales, const uint16_t* codebook, const uint16_t* x,

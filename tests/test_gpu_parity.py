@@ -98,9 +98,13 @@ def _gemv_check(y, x_bits, w_hat, bf16_out):
                              f"got {host_f32(y)[tuple(bad[0])]} want {y_ref[tuple(bad[0])]}")
 
 
+# m > 1 on few row tiles splits k across blocks (k slices, partial sums added
+# in order by a second kernel): (37, 320, 3) has a ragged last slice, (70,
+# 49472, 16) more activations per slice than fit in LDS (chunks inside a
+# slice), (130, 2944, 7) an odd m over uneven slices.
 @pytest.mark.parametrize("n,k,m", [(2048, 2048, 1), (37, 320, 1), (37, 320, 3), (300, 1024, 4),
                                    (300, 1024, 16), (64, 4096, 16), (40000, 128, 2),
-                                   (70000, 64, 1)])
+                                   (70000, 64, 1), (70, 49472, 16), (130, 2944, 7)])
 @pytest.mark.parametrize("ybf16", [False, True])
 def test_dyadic_gemv(w4, n, k, m, ybf16):
     report("dyadic_gemv", n=n, k=k, m=m, ybf16=ybf16)
@@ -151,10 +155,11 @@ def test_dyadic_wide_scales(w4, op):
     _gemv_check(y, x, bits.bf16_to_f64(native.dyadic_dequant(idx, s)), False)
 
 
-def test_dyadic_gemv_deterministic(w4):
+@pytest.mark.parametrize("m", [1, 16])
+def test_dyadic_gemv_deterministic(w4, m):
     n, k = 4096, 2048
     w = synthetic.normal_bf16((n, k), 0.02, 402)
-    x = dev_bf16(synthetic.normal_bf16((1, k), 1.0, 403))
+    x = dev_bf16(synthetic.normal_bf16((m, k), 1.0, 403))
     p, s = w4.w4_quantize_pack(dev_bf16(w), w4.W4_DYADIC)
     a = w4.w4_gemv(p, x, w4.W4_DYADIC, scales=s)
     b = w4.w4_gemv(p, x, w4.W4_DYADIC, scales=s)

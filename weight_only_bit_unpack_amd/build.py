@@ -20,7 +20,8 @@ LIB = os.path.join(PKG, "libw4.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["w4_api.cpp", "w4_quantize.hip", "w4_dequant.hip", "w4_gemv.hip", "w4_gemm.hip"]
+SOURCES = ["w4_api.cpp", "w4_quantize.hip", "w4_dequant.hip", "w4_gemv.hip", "w4_gemm.hip",
+           "w4_workspace.cpp"]
 
 CFLAGS = [
     f"--offload-arch={ARCH}",

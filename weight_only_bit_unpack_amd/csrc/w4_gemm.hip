@@ -32,9 +32,6 @@
 #include "w4_device.h"
 #include "w4_launch.h"
 
-#include <map>
-#include <mutex>
-#include <utility>
 
 namespace w4 {
 namespace {
@@ -422,34 +419,6 @@ hipError_t launch_codec(const GemvProblem& p, int m, int y_bf16, const u32x4* xp
   return hipGetLastError();
 }
 
-// Workspace of a (device, stream): grown on demand, kept for the process, so a
-// call only enqueues kernels.  Calls on one stream are ordered, so they may
-// share it; calls on different streams get different workspaces.
-hipError_t stream_workspace(hipStream_t stream, size_t bytes, char** out) {
-  static std::mutex mu;
-  static std::map<std::pair<int, hipStream_t>, std::pair<char*, size_t>> cache;
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  std::lock_guard<std::mutex> g(mu);
-  auto& slot = cache[{dev, stream}];
-  if (slot.second < bytes) {
-    if (slot.first) {
-      // the stream may still be using the old buffer
-      e = hipStreamSynchronize(stream);
-      if (e != hipSuccess) return e;
-      e = hipFree(slot.first);
-      if (e != hipSuccess) return e;
-      slot = {nullptr, 0};
-    }
-    e = hipMalloc(reinterpret_cast<void**>(&slot.first), bytes);
-    if (e != hipSuccess) return e;
-    slot.second = bytes;
-  }
-  *out = slot.first;
-  return hipSuccess;
-}
-
 hipError_t launch_gemm(int codec, const GemvProblem& p, int m, int y_bf16, hipStream_t stream) {
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) != hipSuccess ||
@@ -464,7 +433,7 @@ hipError_t launch_gemm(int codec, const GemvProblem& p, int m, int y_bf16, hipSt
   const size_t per_split = (size_t)tiles * BM * BN;  // floats
   const size_t bytes = xpk_bytes + (S > 1 ? (size_t)S * per_split * sizeof(float) : 0);
   char* ws = nullptr;
-  hipError_t e = stream_workspace(stream, bytes, &ws);
+  hipError_t e = stream_workspace(kWorkspaceGemm, stream, bytes, &ws);
   if (e != hipSuccess) return e;
   u32x4* xpk = reinterpret_cast<u32x4*>(ws);
   float* partial = S > 1 ? reinterpret_cast<float*>(ws + xpk_bytes) : nullptr;

@@ -30,7 +30,10 @@
 namespace w4 {
 namespace {
 
-constexpr int kXsUnitsMax = 2048;  // at most 32 KiB of LDS for staged activations (16-byte units)
+// Staged activations: at most 3584 16-byte units (56 KiB), so that with the
+// four 2 KiB shuffle areas a block stays within 64 KiB of LDS and two blocks
+// share a CU.
+constexpr int kXsUnitsMax = 3584;
 
 // Buffer resources (V#) over one block's slice of an array: loads at an
 // offset outside [0, num_records) return zero without touching memory, so
@@ -179,9 +182,25 @@ __host__ __device__ __forceinline__ int64_t gemv_chunk(int m, int xs_units, int6
 
 constexpr int kXFirst = 1;  // x units per thread loaded ahead of the weight prefetch
 
-template <int CODEC, int KSPLIT, bool BATCHED>
+// k slices: for m > 1 a small matrix is also split along k across blocks
+// (blockIdx.y = slice of slice_steps 256-k steps), so that every block stages
+// only its slice's activations and the grid still fills the chip.  Each block
+// then writes its fp32 partial sums to `part` [slice][m][n], and gemv_reduce
+// adds the slices in order 0, 1, ... into y.  (A last-arriving block doing the
+// sum instead would need a device-scope release per block, which on this chip
+// writes back the whole L2 each time.)
+struct Slicing {
+  int kslices, slice_steps;
+  float* part;
+};
+
+// XG: x units per thread kept in flight together while staging (after the
+// first).  The batched m = 1 decode pass stages at most a few units per thread
+// and runs fastest with the fewest registers, XG = 1; elsewhere XG = 4.
+template <int CODEC, int KSPLIT, bool BATCHED, int XG>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvProblem single, const GemvProblem* probs,
-                                                   int count, int m, int y_bf16, int xs_units) {
+                                                   int count, int m, int y_bf16, int xs_units,
+                                                   Slicing sl) {
   constexpr int RW = 4 / KSPLIT;  // row tiles per block
   extern __shared__ u32x4 xs[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -208,6 +227,13 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvProblem single, const Gem
     P = single;
   }
   const int64_t N = P.n, K = P.k;
+  // this block's k range (whole rows unless sliced)
+  int64_t kbeg = 0, kend = K;
+  if constexpr (!BATCHED) {
+    kbeg = (int64_t)blockIdx.y * sl.slice_steps * 256;
+    const int64_t e = kbeg + (int64_t)sl.slice_steps * 256;
+    kend = e < K ? e : K;
+  }
   const int kw = wave % KSPLIT, rw = wave / KSPLIT;
   const int r16 = lane & 15, q = lane >> 4;
   const int64_t row0 = blk * RW * 16;
@@ -243,12 +269,12 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvProblem single, const Gem
   }
   S.x = rsrc(P.x, (uint32_t)(m * K * 2));
 
-  const int64_t kc = gemv_chunk(m, xs_units, K);
+  const int64_t kc = gemv_chunk(m, xs_units, kend - kbeg);
   const int row_units = (int)(kc / 8) + 1;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 
-  for (int64_t k0 = 0; k0 < K; k0 += kc) {
-    const int64_t klen = (K - k0 < kc) ? K - k0 : kc;
+  for (int64_t k0 = kbeg; k0 < kend; k0 += kc) {
+    const int64_t klen = (kend - k0 < kc) ? kend - k0 : kc;
     const int steps = (int)((klen + 255) >> 8);
     const int units = steps * 32;  // 16-byte units of one x row in this chunk
     // this wave's steps: st = kw + i * KSPLIT for i < nw; processed three at a
@@ -275,7 +301,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvProblem single, const Gem
       mrow = slot / ipr;  // uniform
       uu = tid + 256 * (slot - mrow * ipr);
       const int64_t kk = k0 + 8 * (int64_t)uu;
-      return (uu < units && kk < K) ? (uint32_t)((mrow * K + kk) * 2) : kOOB;
+      return (uu < units && kk < kend) ? (uint32_t)((mrow * K + kk) * 2) : kOOB;
     };
     lds_barrier();  // the previous chunk's LDS reads are done
     // activations first, then this wave's first three weight steps
@@ -298,11 +324,18 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvProblem single, const Gem
 #pragma unroll
     for (int i = 0; i < kXFirst; ++i)
       if (i < nslots && xu[i] < units) xs[xrow[i] * row_units + xu[i]] = x_to_sigma(xv[i]);
-    for (int slot = kXFirst; slot < nslots; ++slot) {
-      int mrow, uu;
-      const uint32_t o = x_off(slot, mrow, uu);
-      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(S.x, o, 0, 0);
-      if (uu < units) xs[mrow * row_units + uu] = x_to_sigma(v);
+    // the rest XG slots at a time, so their loads overlap
+    for (int slot = kXFirst; slot < nslots; slot += XG) {
+      u32x4 v[XG];
+      int mrow[XG], uu[XG];
+#pragma unroll
+      for (int j = 0; j < XG; ++j) {
+        const uint32_t o = x_off(slot + j, mrow[j], uu[j]);
+        v[j] = __builtin_amdgcn_raw_buffer_load_b128(S.x, slot + j < nslots ? o : kOOB, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < XG; ++j)
+        if (slot + j < nslots && uu[j] < units) xs[mrow[j] * row_units + uu[j]] = x_to_sigma(v[j]);
     }
     lds_barrier();
 
@@ -342,6 +375,19 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvProblem single, const Gem
     }
   }
 
+  if constexpr (KSPLIT == 1 && !BATCHED) {
+    if (sl.kslices > 1) {
+      if ((int)rloc >= rows_here) return;
+      float* part = sl.part + (int64_t)blockIdx.y * m * N;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int mrow = 4 * q + i;
+        if (mrow < m) part[mrow * N + row] = acc[i];
+      }
+      return;
+    }
+  }
+
   if ((int)rloc >= rows_here) return;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -355,47 +401,105 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvProblem single, const Gem
   }
 }
 
-// LDS units for a launch: the whole padded k of the largest problem if it
-// fits, else the cap; never less than the 4 KiB the k-split reduction needs.
-int xs_units_for(int m, int64_t k_max) {
-  const int64_t kpad = (k_max + 255) & ~(int64_t)255;
+// y[e] = sum over slices s = 0, 1, ... of part[s][e], e < total = m * n.
+constexpr int kMaxSlices = 32;
+
+__global__ __launch_bounds__(256) void gemv_reduce(const float* part, int kslices, int64_t total,
+                                                   void* y, int y_bf16) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= total) return;
+  // every slice's load in flight at once, then the sum in slice order
+  float p[kMaxSlices];
+#pragma unroll
+  for (int s = 0; s < kMaxSlices; ++s) p[s] = s < kslices ? part[s * total + e] : 0.f;
+  float v = 0.f;
+#pragma unroll
+  for (int s = 0; s < kMaxSlices; ++s)
+    if (s < kslices) v += p[s];
+  if (y_bf16)
+    reinterpret_cast<uint16_t*>(y)[e] = (uint16_t)f32_to_bf16_bits(v);
+  else
+    reinterpret_cast<float*>(y)[e] = v;
+}
+
+// LDS units for a launch whose blocks each cover `kspan` of k: the whole
+// padded span if it fits, else the cap; never less than the 4 KiB the in-block
+// k-split reduction needs.
+int xs_units_for(int m, int64_t kspan) {
+  const int64_t kpad = (kspan + 255) & ~(int64_t)255;
   int64_t u = (int64_t)m * (kpad / 8 + 1);
   if (u > kXsUnitsMax) u = kXsUnitsMax;
   if (u < 256) u = 256;
   return (int)u;
 }
 
+constexpr int kMaxSliceTiles = 1024;  // row tiles of a sliced call
+constexpr int64_t kTargetBlocks = 512;  // two blocks per CU
+
+struct GemvShape {
+  int ksplit;       // waves along k inside a block (1, 2, 4)
+  int kslices;      // blocks along k
+  int slice_steps;  // 256-k steps per slice
+};
+
+GemvShape gemv_shape(int64_t n, int64_t k, int m) {
+  const int64_t steps = (k + 255) / 256;
+  const int64_t tiles = (n + 63) / 64;
+  if (m == 1 || tiles > kMaxSliceTiles) {
+    // the activations of m = 1 are small: split k between the waves of a block
+    int ks = 4;
+    if (tiles >= 1024) ks = 1;
+    else if ((n + 31) / 32 >= 1024) ks = 2;
+    if (m > 1) ks = 1;
+    return {ks, 1, (int)steps};
+  }
+  // fewest slices whose activations fit in LDS, at least enough for the grid
+  int64_t fit = 1;
+  while (fit < steps && m * (((steps + fit - 1) / fit) * 32 + 1) > kXsUnitsMax) ++fit;
+  int64_t ks = (kTargetBlocks + tiles - 1) / tiles;
+  if (ks < fit) ks = fit;
+  if (ks > kMaxSlices) ks = kMaxSlices;
+  if (ks > steps) ks = steps;
+  const int64_t per = (steps + ks - 1) / ks;
+  return {1, (int)((steps + per - 1) / per), (int)per};
+}
+
 template <int CODEC, int KSPLIT>
-hipError_t launch_one(const GemvProblem& p, int m, int y_bf16, hipStream_t stream) {
+hipError_t launch_one(const GemvProblem& p, int m, int y_bf16, const GemvShape& sh,
+                      hipStream_t stream) {
   const int rows = 16 * (4 / KSPLIT);
   const int64_t blocks = (p.n + rows - 1) / rows;
-  const int xu = xs_units_for(m, p.k);
-  gemv_kernel<CODEC, KSPLIT, false><<<dim3((uint32_t)blocks), dim3(256), (xu + 512) * 16, stream>>>(
-      p, nullptr, 0, m, y_bf16, xu);
+  Slicing sl{sh.kslices, sh.slice_steps, nullptr};
+  if (sh.kslices > 1) {
+    char* ws = nullptr;
+    const hipError_t e =
+        stream_workspace(kWorkspaceGemv, stream, (size_t)sh.kslices * m * p.n * 4, &ws);
+    if (e != hipSuccess) return e;
+    sl.part = reinterpret_cast<float*>(ws);
+  }
+  const int xu = xs_units_for(m, (int64_t)sh.slice_steps * 256);
+  gemv_kernel<CODEC, KSPLIT, false, 4>
+      <<<dim3((uint32_t)blocks, (uint32_t)sh.kslices), dim3(256), (xu + 512) * 16, stream>>>(
+          p, nullptr, 0, m, y_bf16, xu, sl);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || sh.kslices == 1) return e;
+  const int64_t total = (int64_t)m * p.n;
+  gemv_reduce<<<dim3((uint32_t)((total + 255) / 256)), dim3(256), 0, stream>>>(
+      sl.part, sh.kslices, total, p.y, y_bf16);
   return hipGetLastError();
 }
 
 template <int CODEC>
 hipError_t launch_codec(const GemvProblem& p, int m, int y_bf16, hipStream_t stream) {
-  switch (gemv_pick_ksplit(p.n, p.k, m)) {
-    case 1: return launch_one<CODEC, 1>(p, m, y_bf16, stream);
-    case 2: return launch_one<CODEC, 2>(p, m, y_bf16, stream);
-    default: return launch_one<CODEC, 4>(p, m, y_bf16, stream);
+  const GemvShape sh = gemv_shape(p.n, p.k, m);
+  switch (sh.ksplit) {
+    case 1: return launch_one<CODEC, 1>(p, m, y_bf16, sh, stream);
+    case 2: return launch_one<CODEC, 2>(p, m, y_bf16, sh, stream);
+    default: return launch_one<CODEC, 4>(p, m, y_bf16, sh, stream);
   }
 }
 
 }  // namespace
-
-int gemv_rows_per_block(int ksplit) { return 16 * (4 / ksplit); }
-
-int gemv_pick_ksplit(int64_t n, int64_t k, int m) {
-  (void)k;
-  (void)m;
-  // enough blocks of 64 rows to give every CU several: no k split
-  if ((n + 63) / 64 >= 1024) return 1;
-  if ((n + 31) / 32 >= 1024) return 2;
-  return 4;
-}
 
 hipError_t launch_gemv(int codec, const GemvProblem& p, int m, int y_bf16, hipStream_t stream) {
   if (codec == 0) return launch_codec<0>(p, m, y_bf16, stream);
@@ -403,22 +507,31 @@ hipError_t launch_gemv(int codec, const GemvProblem& p, int m, int y_bf16, hipSt
   return launch_codec<2>(p, m, y_bf16, stream);
 }
 
-int gemv_batched_rows(int, int64_t) { return gemv_rows_per_block(1); }
+int gemv_batched_rows(int, int64_t) { return 64; }
+
+template <int CODEC>
+hipError_t launch_batched_codec(const GemvProblem* probs_dev, int count, int64_t total_tiles,
+                                int xu, int m, int y_bf16, hipStream_t stream) {
+  const dim3 block(256), grid((uint32_t)total_tiles);
+  const size_t lds = (size_t)(xu + 512) * 16;  // activations + 4 x 2 KiB shuffle areas
+  const GemvProblem none{};
+  const Slicing whole{1, 0, nullptr};
+  if (m == 1)
+    gemv_kernel<CODEC, 1, true, 1>
+        <<<grid, block, lds, stream>>>(none, probs_dev, count, m, y_bf16, xu, whole);
+  else
+    gemv_kernel<CODEC, 1, true, 4>
+        <<<grid, block, lds, stream>>>(none, probs_dev, count, m, y_bf16, xu, whole);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemv_batched(int codec, const GemvProblem* probs_dev, int count,
                                int64_t total_tiles, int64_t k_max, int m, int y_bf16,
                                hipStream_t stream) {
-  const dim3 block(256), grid((uint32_t)total_tiles);
   const int xu = xs_units_for(m, k_max);
-  const size_t lds = (size_t)(xu + 512) * 16;  // activations + 4 x 2 KiB shuffle areas
-  GemvProblem none{};
-  if (codec == 0)
-    gemv_kernel<0, 1, true><<<grid, block, lds, stream>>>(none, probs_dev, count, m, y_bf16, xu);
-  else if (codec == 1)
-    gemv_kernel<1, 1, true><<<grid, block, lds, stream>>>(none, probs_dev, count, m, y_bf16, xu);
-  else
-    gemv_kernel<2, 1, true><<<grid, block, lds, stream>>>(none, probs_dev, count, m, y_bf16, xu);
-  return hipGetLastError();
+  if (codec == 0) return launch_batched_codec<0>(probs_dev, count, total_tiles, xu, m, y_bf16, stream);
+  if (codec == 1) return launch_batched_codec<1>(probs_dev, count, total_tiles, xu, m, y_bf16, stream);
+  return launch_batched_codec<2>(probs_dev, count, total_tiles, xu, m, y_bf16, stream);
 }
 
 }  // namespace w4

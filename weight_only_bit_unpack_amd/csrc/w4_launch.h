@@ -27,10 +27,6 @@ hipError_t launch_dequant(int codec, int64_t n, int64_t k, const uint8_t* packed
                           const uint16_t* scales, const uint16_t* codebook, void* out,
                           hipStream_t stream);
 
-// rows of one GEMV block for a given k-split (the batched plan uses it too)
-int gemv_rows_per_block(int ksplit);
-int gemv_pick_ksplit(int64_t n, int64_t k, int m);
-
 hipError_t launch_gemv(int codec, const GemvProblem& p, int m, int y_bf16, hipStream_t stream);
 
 // Rows per block of the batched GEMV for this m and largest k (the plan numbers
@@ -41,6 +37,11 @@ int gemv_batched_rows(int m, int64_t k_max);
 hipError_t launch_gemv_batched(int codec, const GemvProblem* probs_dev, int count,
                                int64_t total_tiles, int64_t k_max, int m, int y_bf16,
                                hipStream_t stream);
+
+// Library-owned device buffer of at least `bytes` for (current device, stream,
+// user); its contents are undefined.  Growing waits for the stream.
+enum { kWorkspaceGemm = 0, kWorkspaceGemv = 1 };
+hipError_t stream_workspace(int user, hipStream_t stream, size_t bytes, char** out);
 
 hipError_t launch_gemm(int codec, const GemvProblem& p, int m, int y_bf16, hipStream_t stream);
 

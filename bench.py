@@ -13,9 +13,9 @@ Also measured in the same run and reported under "rows": the same pass as
 168 separate w4_gemv calls, quantize_pack and unpack_dequant over the stack,
 and the prefill GEMM (M = 256, K = N = 8192, in TFLOP/s) with quantize_pack of
 its 8192^2 weight.  The CPU baseline times the oracle (numpy, one thread) on
-the first block of the stack.
+the first eight decoder blocks of the stack.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+    python bench.py [--gpus 1] [--steps 1000] [--warmup 200]
 """
 
 import argparse
@@ -36,8 +36,8 @@ METRIC = "W4 dequant-GEMV GB/s (% HBM peak) at m=1; W4A16 GEMM TFLOP/s at m=256"
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["headline", "gemm", "copy"], default=None,
                     help="run one target only (for profiler runs): the batched decode pass, "

@@ -24,13 +24,17 @@
 // partial in the MFMA register layout and a second kernel adds the partials in
 // split order, so results do not depend on timing.
 //
-// Software pipeline per k-step u: issue the loads of step u+3 (packed weights
-// and their side data) and u+1 (activations), rebuild step u+1 into the other
-// LDS buffer, run the 16 MFMAs of step u, then one LDS-only barrier.  Loads
-// past the block's k range use offsets past the buffer resource and return
-// zero, so the loop runs whole rounds of four steps without branches.
+// Software pipeline: weights are loaded four k-steps ahead and activations
+// one step ahead; the rebuilt weights are double-buffered in LDS, and each
+// step's block barrier sits between its two 16-k halves of MFMAs, so that the
+// LDS reads of the next step's operands run under the current step's MFMAs
+// (details at the loop).  Loads past the block's k range use offsets past the
+// buffer resource and return zero, so the loop runs whole rounds of four steps
+// without branches.
 #include "w4_device.h"
 #include "w4_launch.h"
+
+#include <type_traits>
 
 
 namespace w4 {
@@ -68,12 +72,12 @@ struct WRaw<0> {  // DYADIC: bf16 scale of the row's 64-group
     p1 = v[1];
     sb = __builtin_amdgcn_raw_buffer_load_b16(s0, so, 0, 0);
   }
-  __device__ __forceinline__ void rebuild(u32x4* dst, u32x4*) const {
+  template <int D>
+  __device__ __forceinline__ void rebuild(u32x4& hi, u32x4&) const {
     const DyadicScale d = dyadic_scale(sb);
     const uint32_t m0 = 0x000F000Fu, m1 = 0x00F000F0u, mg = kMagic;
     const float nz = __builtin_bit_cast(float, opaque(0x80000000u));
-    dst[0] = sigma_to_natural(dyadic_rebuild_any(p0, d, m0, m1, mg, nz));
-    dst[1] = sigma_to_natural(dyadic_rebuild_any(p1, d, m0, m1, mg, nz));
+    hi = sigma_to_natural(dyadic_rebuild_any(D == 0 ? p0 : p1, d, m0, m1, mg, nz));
   }
 };
 
@@ -92,10 +96,10 @@ struct WRaw<1> {  // LUT16: 16 bf16 levels + bf16 scale of the row's 64-group
     l1 = __builtin_amdgcn_raw_buffer_load_b128(s1, co + 16, 0, 0);
     sb = __builtin_amdgcn_raw_buffer_load_b16(s0, so, 0, 0);
   }
-  __device__ __forceinline__ void rebuild(u32x4* dst, u32x4*) const {
+  template <int D>
+  __device__ __forceinline__ void rebuild(u32x4& hi, u32x4&) const {
     const Lut16Table t = lut16_table(sb, l0, l1);
-    dst[0] = sigma_to_natural(lut16_rebuild(p0, t));
-    dst[1] = sigma_to_natural(lut16_rebuild(p1, t));
+    hi = sigma_to_natural(lut16_rebuild(D == 0 ? p0 : p1, t));
   }
 };
 
@@ -111,15 +115,13 @@ struct WRaw<2> {  // SIGNMAG8: 8 fp16 magnitudes of the row's 32-group
     p1 = v[1];
     c = __builtin_amdgcn_raw_buffer_load_b128(s1, co, 0, 0);
   }
-  __device__ __forceinline__ void rebuild(u32x4* hi, u32x4* lo) const {
+  template <int D>
+  __device__ __forceinline__ void rebuild(u32x4& hi, u32x4& lo) const {
     const SignMagTable t = signmag_table(c);
     u32x4 h, l;
-    signmag_rebuild(p0, t, h, l);
-    hi[0] = sigma_to_natural(h);
-    lo[0] = sigma_to_natural(l);
-    signmag_rebuild(p1, t, h, l);
-    hi[1] = sigma_to_natural(h);
-    lo[1] = sigma_to_natural(l);
+    signmag_rebuild(D == 0 ? p0 : p1, t, h, l);
+    hi = sigma_to_natural(h);
+    lo = sigma_to_natural(l);
   }
 };
 
@@ -212,15 +214,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         xv[i][kk] = __builtin_amdgcn_raw_buffer_load_b128(
             xr, base + (uint32_t)i * x_i + (uint32_t)kk * 1024u, 0, 0);
   };
-  auto rebuild = [&](const WRaw<CODEC>& r, int buf) {
-    u32x4 hi[2], lo[2];
-    r.rebuild(hi, lo);
-#pragma unroll
-    for (int d = 0; d < 2; ++d) {
-      wtile(buf, 0)[wr * STR + 2 * wq + d] = hi[d];
-      if constexpr (NPL == 2) wtile(buf, 1)[wr * STR + 2 * wq + d] = lo[d];
-    }
+  // rebuild packed dword D (k = 16 wq + 8 D .. + 7 of the step) into LDS
+  auto rebuild = [&](const WRaw<CODEC>& r, int buf, auto dtag) {
+    constexpr int D = decltype(dtag)::value;
+    u32x4 hi, lo;
+    r.template rebuild<D>(hi, lo);
+    wtile(buf, 0)[wr * STR + 2 * wq + D] = hi;
+    if constexpr (NPL == 2) wtile(buf, 1)[wr * STR + 2 * wq + D] = lo;
   };
+  using D0 = std::integral_constant<int, 0>;
+  using D1 = std::integral_constant<int, 1>;
 
   f32x16 acc[2][4];
 #pragma unroll
@@ -230,41 +233,66 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  auto mma_step = [&](const u32x4 (&xv)[2][2], int buf) {
+  // B operands of one 16-k block kk of a step (4 weight-row tiles of 32)
+  auto read_b = [&](u32x4 (&bq)[NPL][4], int buf, int kk) {
+    const int kb = 2 * kh + kk;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int kb = 2 * kh + kk;
+    for (int pl = 0; pl < NPL; ++pl)
 #pragma unroll
-      for (int pl = 0; pl < NPL; ++pl) {
-        u32x4 bq[4];
+      for (int j = 0; j < 4; ++j) bq[pl][j] = wtile(buf, pl)[(32 * j + r32) * STR + 2 * kb + h];
+  };
+  auto mma_half = [&](const u32x4 (&xv)[2][2], const u32x4 (&bq)[NPL][4], int kk) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bq[j] = wtile(buf, pl)[(32 * j + r32) * STR + 2 * kb + h];
+    for (int pl = 0; pl < NPL; ++pl)
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(xv[i][kk], bq[j], acc[i][j]);
-      }
-    }
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(xv[i][kk], bq[pl][j], acc[i][j]);
   };
 
-  // prologue: weights of steps 0..2, activations of step 0, step 0 rebuilt
+  // Each k-step u runs in two phases split by the block barrier:
+  //   A(u): reads of B(u, second 16-k block); MFMAs of the first block; the
+  //         second half of step u+1's rebuild (so all of u+1 is in LDS at the
+  //         barrier); the loads of step u+4 (weights) and u+1 (activations).
+  //   B(u): reads of B(u+1, first block), right after the barrier; MFMAs of
+  //         u's second block; the first half of step u+2's rebuild into the
+  //         buffer step u has just released.
+  // The LDS reads of the next step thus run under the MFMAs of the current
+  // one instead of between barriers, and each phase's rebuild work (about
+  // half a step's VALU) fits under its eight MFMAs per wave.
+  u32x4 b0[NPL][4], b1[NPL][4];
   load_w(wqr[0], 0);
   load_w(wqr[1], 1);
   load_w(wqr[2], 2);
+  load_w(wqr[3], 3);
   load_x(xq[0], 0);
-  rebuild(wqr[0], 0);
+  rebuild(wqr[0], 0, D0{});
+  rebuild(wqr[0], 0, D1{});
+  rebuild(wqr[1], 1, D0{});
   lds_barrier();
+  read_b(b0, 0, 0);
 
   for (int u = 0; u < nsteps; u += 4) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      load_w(wqr[(v + 3) & 3], u + v + 3);
-      load_x(xq[(v + 1) & 1], u + v + 1);
-      rebuild(wqr[(v + 1) & 3], (v + 1) & 1);
-      mma_step(xq[v & 1], v & 1);
+      const int cur = v & 1, nxt = (v + 1) & 1;
+      // phase A
+      read_b(b1, cur, 1);
+      load_x(xq[nxt], u + v + 1);
+      mma_half(xq[cur], b0, 0);
+      rebuild(wqr[(v + 1) & 3], nxt, D1{});
+      load_w(wqr[v & 3], u + v + 4);
+      __builtin_amdgcn_sched_barrier(0);
       lds_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      // phase B
+      read_b(b0, nxt, 0);
+      mma_half(xq[cur], b1, 1);
+      rebuild(wqr[(v + 2) & 3], cur, D0{});
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
+  lds_barrier();  // the last phase's LDS traffic is done before LDS is reused
 
   // the two k halves of a row group meet in LDS (the weight tiles are dead)
   f32x4* const red = reinterpret_cast<f32x4*>(lds) + mw * 32 * 64 + lane;

@@ -104,27 +104,23 @@ def time_gemm(w4, synthetic, torch, dev, stream, args):
     return ms_g, 2 * 256 * 8192 * 8192 / (ms_g * 1e-3) / 1e12
 
 
-def quantile_levels(w, group, n_levels, magnitude):
-    """Per-group levels for timing runs: the k-means starting point (sorted
-    values at 4k + 2, as normalised values for LUT16 or magnitudes for
-    SIGNMAG8), built with torch on the device.  Throughput does not depend on
-    the levels' values; parity of fitted levels is checked in the tests."""
+def magnitude_levels(w):
+    """SIGNMAG8 magnitudes for timing runs: the Lloyd starting point (sorted
+    |w| of each group of 32 at ranks 4q + 2, as fp16), built with torch on the
+    device.  Throughput does not depend on the levels' values; parity of
+    fitted levels is checked in the tests."""
     import torch
     n, k = w.shape
-    g = w.float().reshape(n, k // group, group)
-    if magnitude:
-        v = torch.sort(g.abs(), dim=-1).values
-        return v[..., 2::4][..., :n_levels].to(torch.float16).contiguous()
-    s = g.abs().amax(dim=-1, keepdim=True)
-    u = torch.where(s > 0, g / torch.where(s > 0, s, torch.ones_like(s)), torch.zeros_like(g))
-    v = torch.sort(u, dim=-1).values
-    return (s.squeeze(-1).to(torch.bfloat16).contiguous(),
-            v[..., 2::4][..., :n_levels].to(torch.bfloat16).contiguous())
+    v = torch.sort(w.float().reshape(n, k // 32, 32).abs(), dim=-1).values
+    return v[..., 2::4].to(torch.float16).contiguous()
+
+
+FIT_STEPS = 5  # timed k-means fits per shape (each takes milliseconds)
 
 
 def other_configs(w4, synthetic, torch, dev, stream, args):
-    """Rows for the 2048^2 single GEMV, the 3.9B-sized LUT16 GEMVs and the 2B
-    SIGNMAG8 dequant + batched GEMV."""
+    """Rows for the 2048^2 single GEMV, the 3.9B-sized LUT16 fits and GEMVs and
+    the 2B SIGNMAG8 dequant + batched GEMV."""
     rows = {}
     # single 2048^2 DYADIC weight, N(0, 0.02^2), m = 1: one call's latency
     W = synthetic.normal_bf16_device((2048, 2048), 0.02, synthetic.seed(0, 0, 0), dev)
@@ -137,12 +133,17 @@ def other_configs(w4, synthetic, torch, dev, stream, args):
     rows["gemv_m1_2048x2048_single_call"] = {"ms": ms, "GB/s": b / (ms * 1e-3) / 1e9}
     del W, P, S
 
-    # LUT16 on the 3.9B-sized shapes, m = 1, 4, 16
-    log("LUT16 3.9B-sized GEMVs")
+    # LUT16 on the 3.9B-sized shapes: k-means fit on the GPU, then GEMV at m = 1, 4, 16
+    log("LUT16 3.9B-sized fit + GEMVs")
     for i, (n, k) in enumerate([(4096, 4096), (11008, 4096), (4096, 11008)]):
         W = synthetic.normal_outliers_bf16_device((n, k), 0.015, 0.001, 0.15,
                                                   synthetic.seed(3, i, 0), dev)
-        sc, L = quantile_levels(W, 64, 16, magnitude=False)
+        sc = torch.empty((n, k // 64), dtype=torch.bfloat16, device=dev)
+        L = torch.empty((n, k // 64, 16), dtype=torch.bfloat16, device=dev)
+        ms = timed(lambda: w4.w4_lut16_fit(W, 25, scales=sc, codebook=L, stream=stream),
+                   stream, FIT_STEPS, 1)
+        rows[f"lut16_fit_{n}x{k}"] = {"ms": ms, "Mgroups/s": n * k / 64 / (ms * 1e-3) / 1e6,
+                                      "Gweights/s": n * k / (ms * 1e-3) / 1e9}
         P, _ = w4.w4_quantize_pack(W, w4.W4_LUT16, scales=sc, codebook=L)
         del W
         for m in (1, 4, 16):
@@ -159,7 +160,7 @@ def other_configs(w4, synthetic, torch, dev, stream, args):
     probs, total = [], 0
     for i in range(224):
         W = synthetic.student_t_bf16_device((2048, 2048), 5, 0.02, synthetic.seed(4, i, 0), dev)
-        cb = quantile_levels(W, 32, 8, magnitude=True)
+        cb = magnitude_levels(W)
         P, _ = w4.w4_quantize_pack(W, w4.W4_SIGNMAG8, codebook=cb)
         del W
         x = synthetic.normal_bf16_device((1, 2048), 1.0, synthetic.seed(4, i, 1), dev)

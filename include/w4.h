@@ -20,9 +20,9 @@
  * Conventions shared by every call
  * --------------------------------
  *  - Pointers are DEVICE pointers owned by the caller; the library keeps none
- *    of them after returning.  It allocates no memory, except w4_gemm, which
- *    keeps one device workspace per (device, stream) for the process's life
- *    (see there).
+ *    of them after returning.  It allocates no memory, except w4_gemm and
+ *    w4_gemv with m >= 2, which keep a device workspace per (device, stream)
+ *    for the process's life (see there).
  *  - `stream` is a hipStream_t (NULL = the null stream).  A call only enqueues
  *    work on it; it never synchronises the stream or the device.
  *  - All validation happens on the host before anything is enqueued.  On any
@@ -71,6 +71,8 @@ typedef enum { W4_DYADIC = 0, W4_LUT16 = 1, W4_SIGNMAG8 = 2 } w4_codec;
 /* Largest k of a matrix product call: keeps every per-block byte offset of the
  * kernels within 32 bits. */
 #define W4_MAX_MATMUL_K 4194304
+/* Largest Lloyd round count w4_lut16_fit accepts. */
+#define W4_MAX_FIT_ITERS 1024
 typedef enum { W4_F32 = 0, W4_BF16 = 1, W4_F16 = 2 } w4_dtype;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -107,6 +109,32 @@ w4_status w4_quantize_pack(int32_t codec, int64_t n, int64_t k, const uint16_t* 
 w4_status w4_unpack_dequant(int32_t codec, int64_t n, int64_t k, const uint8_t* packed,
                             const uint16_t* scales, const uint16_t* codebook, void* out,
                             void* stream);
+
+/*
+ * w4_lut16_fit -- fit the LUT16 side tables of a bf16 weight [n][k]: per group
+ * of 64, a scale and 16 levels by 1D k-means.  [KM] sec. 1.2 (per-block 16-
+ * centre k-means, 16-bit scale); [G32] sec. 1.3 (quantile start, 25 rounds).
+ * For each group, in fp64:
+ *   s = max |w| (written to scales as bf16; exact), u = w / s;
+ *   start: the elements of rank 4q + 2 (q = 0..15) in a stable ascending sort
+ *          of u (equal values keep element order);
+ *   `iters` rounds: assign each u to the centre with the smallest |u - c|,
+ *          the lowest centre on a tie; each centre with members becomes the
+ *          sum of its members, added in increasing element order, divided by
+ *          their count; a centre without members keeps its value;
+ *   codebook[r][g][q] = c_q rounded to bf16 (nearest, ties to even).
+ * An all-zero group gets scale +0 and 16 levels +0.  The result is bit-exact:
+ * every step is an exact operation or one IEEE fp64 operation in a fixed
+ * order.  The outputs are the scales / codebook inputs of w4_quantize_pack
+ * and the matrix calls for W4_LUT16.
+ * w: bf16 [n][k], 16-byte aligned; finite values.  scales: bf16 [n][k/64],
+ * 2-byte aligned.  codebook: bf16 [n][k/64][16], 16-byte aligned.
+ * iters: 0 .. W4_MAX_FIT_ITERS (0: the quantile start itself).
+ * Errors: W4_EINVAL (negative size, iters out of range, null pointer),
+ * W4_ESHAPE (k % 64 != 0, or more than 2^40 groups), W4_EALIGN.
+ */
+w4_status w4_lut16_fit(int64_t n, int64_t k, const uint16_t* w, uint16_t* scales,
+                       uint16_t* codebook, int32_t iters, void* stream);
 
 /*
  * w4_gemv -- fused dequant + matrix-vector product for small batches,

@@ -86,10 +86,13 @@ def dequant(packed, s_bits, lut_bits):
 
 # ----------------------------------------------------------------- fit (test data)
 def quantile_init(u, n_levels):
-    """``c_k = sorted(u)[k * (G / n) + (G / n) // 2]`` for each row of u [B, G]."""
+    """``c_k = sorted(u)[k * (G / n) + (G / n) // 2]`` for each row of u [B, G].
+
+    The sort is stable: equal values (also -0.0 and +0.0) keep their element
+    order, so the start is fully determined by the group."""
     gsz = u.shape[-1]
     stride = gsz // n_levels
-    srt = np.sort(u, axis=-1)
+    srt = np.sort(u, axis=-1, kind="stable")
     return srt[..., stride * np.arange(n_levels) + stride // 2].copy()
 
 

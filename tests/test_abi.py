@@ -26,7 +26,7 @@ def w4():
 
 def test_header_declares_the_calls():
     names = _declared()
-    for n in ["w4_quantize_pack", "w4_unpack_dequant", "w4_gemv", "w4_gemm",
+    for n in ["w4_quantize_pack", "w4_unpack_dequant", "w4_gemv", "w4_gemm", "w4_lut16_fit",
               "w4_gemv_batched_plan", "w4_gemv_batched", "w4_status_str", "w4_group_size"]:
         assert n in names
 
@@ -87,6 +87,22 @@ def test_quantize_dequant_validation(w4):
     assert d(1, 4, 64, P(16), P(16), None, P(16), None) == 1
     assert d(0, 4, 64, P(16), P(16), None, None, None) == 1
     assert d(0, 4, 64, P(16), P(16), None, P(8), None) == 3
+
+
+def test_lut16_fit_validation(w4):
+    f = w4._lib.w4_lut16_fit
+    P = ctypes.c_void_p
+    ok = dict(n=4, k=64, w=P(16), s=P(16), L=P(16), it=25)
+    call = lambda **kw: f(*[{**ok, **kw}[a] for a in ("n", "k", "w", "s", "L", "it")], None)
+    assert call(n=-1) == 1
+    assert call(k=96) == 2
+    assert call(it=-1) == 1
+    assert call(it=1025) == 1
+    assert call(w=None) == 1 and call(s=None) == 1 and call(L=None) == 1
+    assert call(w=P(8)) == 3 and call(L=P(24)) == 3 and call(s=P(17)) == 3
+    assert call(n=0, w=None, s=None, L=None) == 0
+    assert call(k=0, w=None, s=None, L=None) == 0
+    assert call(n=1 << 40, k=128) == 2
 
 
 def test_batched_plan_validation(w4):

@@ -112,14 +112,18 @@ def test_fullsize_decode_stack_batched_gemv(w4):
 # ------------------------------------------------------------ 3.9B-sized LUT16
 @pytest.mark.parametrize("n,k", [(4096, 4096), (11008, 4096), (4096, 11008)])
 def test_fullsize_lut16(w4, n, k):
-    """N(0, 0.015^2) with 0.1% outliers at +-10 sigma; oracle k-means fit
-    (quantile start, 25 Lloyd rounds); quantize, dequant and GEMV at
-    m = 1, 4, 16 on sampled rows."""
+    """N(0, 0.015^2) with 0.1% outliers at +-10 sigma; k-means fit (quantile
+    start, 25 Lloyd rounds) on the GPU, equal to the oracle's on every group;
+    quantize, dequant and GEMV at m = 1, 4, 16 on sampled rows."""
     report("fullsize_lut16", n=n, k=k)
     w = synthetic.normal_outliers_bf16_device((n, k), 0.015, 0.001, 0.15,
                                               synthetic.seed(3, n + k, 0))
     s, L = native.lut16_fit(host_bits(w))
-    s_dev, L_dev = dev_bf16(s), dev_bf16(L)
+    # the library's own fit is the oracle's, bit for bit, on the whole matrix
+    s_dev, L_dev = w4.w4_lut16_fit(w)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(s_dev), s)
+    assert np.array_equal(host_bits(L_dev), L)
     p, _ = w4.w4_quantize_pack(w, w4.W4_LUT16, scales=s_dev, codebook=L_dev)
     d = w4.w4_unpack_dequant(p, w4.W4_LUT16, scales=s_dev, codebook=L_dev)
     torch.cuda.synchronize()

@@ -223,6 +223,24 @@ def test_lut16_quantize_dequant_bitexact(w4, n, k):
     assert np.array_equal(host_bits(out), lut16.dequant_from_indices(idx, s, L))
 
 
+@pytest.mark.parametrize("iters", [0, 1, 25])
+def test_lut16_fit_bitexact(w4, iters):
+    """GPU k-means LUT fit == the C oracle's fit, bit for bit: tie-heavy groups
+    (signed-zero runs, few distinct values, all-zero, subnormal and near-max
+    magnitudes) and Gaussian-with-outliers groups, 16 groups per block with a
+    ragged last block."""
+    from tests.test_oracle_lut16 import tie_groups
+    report("lut16_fit", iters=iters)
+    ties = tie_groups().reshape(1, 8 * 64)
+    rnd = synthetic.normal_outliers_bf16((37, 320), 0.015, 0.001, 0.15, 77)
+    for w in (ties, rnd, synthetic.normal_bf16((300, 1024), 0.02, 78), rnd[:1, :64]):
+        s_o, L_o = native.lut16_fit(w, iters)
+        s, L = w4.w4_lut16_fit(dev_bf16(w), iters)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(s), s_o), w.shape
+        assert np.array_equal(host_bits(L), L_o), w.shape
+
+
 @pytest.mark.parametrize("m", [1, 4, 16])
 def test_lut16_gemv_and_gemm(w4, m):
     n, k = 300, 1024

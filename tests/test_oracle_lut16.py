@@ -154,6 +154,46 @@ def test_lut16_c_matches_python():
     assert np.array_equal(lut16.indices(w, s, L), native.lut16_indices(w, s, L))
 
 
+def tie_groups():
+    """bf16 groups whose fit depends on tie rules: runs of -0.0 / +0.0 in both
+    orders (the quantile start lands on zeros, some centres stay empty), few
+    distinct values, repeated values, an all-zero group, tiny and huge
+    magnitudes.  Shared with the GPU parity test of the fit."""
+    g = np.random.default_rng(29)
+    rows = []
+    z = np.zeros(64, np.uint16)
+    a = z.copy(); a[0:40:2] = 0x8000; a[40:] = bits.rne_bf16(np.arange(1, 25) / 24.0)
+    rows.append(a)
+    b = z.copy(); b[1:40:2] = 0x8000; b[40:] = bits.rne_bf16(-np.arange(1, 25) / 24.0)
+    rows.append(b)
+    c = bits.rne_bf16(g.choice([-0.5, 0.25, 1.0], 64))       # three distinct values
+    rows.append(c)
+    d = bits.rne_bf16(np.repeat(g.normal(0, 0.02, 8), 8))   # eight values, 8 times each
+    rows.append(d)
+    rows.append(z.copy())                                    # all zero
+    e = (g.integers(0x0001, 0x0080, 64) | (g.integers(0, 2, 64) << 15)).astype(np.uint16)
+    rows.append(e)                                           # subnormal bf16 only
+    f = (g.integers(0x7E00, 0x7F7F, 64) | (g.integers(0, 2, 64) << 15)).astype(np.uint16)
+    rows.append(f)                                           # magnitudes near the bf16 max
+    h = z.copy(); h[5] = 0x3F80; h[9] = 0x8000               # one nonzero value
+    rows.append(h)
+    return np.stack(rows).reshape(2, 4 * 64)
+
+
+def test_lut16_c_matches_python_on_ties():
+    w = tie_groups()
+    for iters in (0, 1, 25):
+        s, L = lut16.fit(w, iters)
+        s2, L2 = native.lut16_fit(w, iters)
+        assert np.array_equal(s, s2) and np.array_equal(L, L2), iters
+    # the quantile start on zero runs keeps the zeros' signs in element order
+    s0, L0 = lut16.fit(w, 0)
+    u = bits.bf16_to_f64(w[0, :64])
+    order = sorted(range(64), key=lambda i: (u[i], i))   # stable by element index
+    want = np.array([w[0, order[4 * q + 2]] for q in range(16)], np.uint16)
+    assert np.array_equal(L0[0, 0], bits.rne_bf16(bits.bf16_to_f64(want)))
+
+
 # ------------------------------------------------------------------ SIGNMAG8
 def _sm_data(rows=8, k=512, seed=31):
     return synthetic.student_t_bf16((rows, k), 5, 0.02, seed)

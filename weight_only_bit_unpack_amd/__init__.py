@@ -6,7 +6,7 @@ forwards raw device pointers and the current HIP stream to the C ABI
 (``include/w4.h``), whose functions carry the same names.  All computation
 happens in the HIP kernels; there is no fallback of any kind, and importing
 this package fails if ``libw4.so`` has not been built
-(``python -m weight_only_bit_unpack_amd.build``).
+(``python weight_only_bit_unpack_amd/build.py``).
 """
 
 import ctypes
@@ -23,7 +23,7 @@ GROUP = {W4_DYADIC: 64, W4_LUT16: 64, W4_SIGNMAG8: 32}
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m weight_only_bit_unpack_amd.build`")
+        f"{LIB_PATH} is missing: build it with `python weight_only_bit_unpack_amd/build.py`")
 
 _lib = ctypes.CDLL(LIB_PATH)
 _P, _I32, _I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
@@ -46,6 +46,7 @@ _SIGS = {
     "w4_group_size": ([_I32], _I32),
     "w4_quantize_pack": ([_I32, _I64, _I64, _P, _P, _P, _P, _P], _I32),
     "w4_unpack_dequant": ([_I32, _I64, _I64, _P, _P, _P, _P, _P], _I32),
+    "w4_lut16_fit": ([_I64, _I64, _P, _P, _P, _I32, _P], _I32),
     "w4_gemv": ([_I32, _I64, _I64, _P, _P, _P, _P, _I32, _P, _I32, _P], _I32),
     "w4_gemm": ([_I32, _I64, _I64, _P, _P, _P, _P, _I32, _P, _I32, _P], _I32),
     "w4_gemv_batched_plan": ([_I32, _I32, _I32, ctypes.POINTER(W4Problem), _I32,
@@ -149,6 +150,24 @@ def w4_unpack_dequant(packed, codec=W4_DYADIC, *, scales=None, codebook=None, ou
     _check(_lib.w4_unpack_dequant(codec, n, k, _ptr(packed), _ptr(scales), _ptr(codebook),
                                   _ptr(out), _stream(stream)))
     return out
+
+
+def w4_lut16_fit(w, iters=25, *, scales=None, codebook=None, stream=None):
+    """Fit the LUT16 codec's per-group scale and 16 levels to a bf16 weight
+    [n, k] on the GPU (1D k-means per group of 64).  Returns (scales bf16
+    [n, k/64], codebook bf16 [n, k/64, 16]), the inputs w4_quantize_pack
+    takes for W4_LUT16."""
+    _need(w, "w", _U16)
+    n, k = w.shape
+    if scales is None:
+        scales = torch.empty((n, k // 64), dtype=torch.bfloat16, device=w.device)
+    if codebook is None:
+        codebook = torch.empty((n, k // 64, 16), dtype=torch.bfloat16, device=w.device)
+    _need(scales, "scales", _U16, (n, k // 64))
+    _need(codebook, "codebook", _U16, (n, k // 64, 16))
+    _check(_lib.w4_lut16_fit(n, k, _ptr(w), _ptr(scales), _ptr(codebook), iters,
+                             _stream(stream)))
+    return scales, codebook
 
 
 def _matmul(fn, packed, x, codec, scales, codebook, y, y_dtype, stream):

@@ -1,6 +1,6 @@
 """Build libw4.so (gfx950) in-tree with hipcc.
 
-    python -m weight_only_bit_unpack_amd.build
+    python weight_only_bit_unpack_amd/build.py
 
 Every source under csrc/ is compiled for gfx950 only; the objects go to
 csrc/_build/ and the shared library to this package directory, where the
@@ -21,7 +21,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["w4_api.cpp", "w4_quantize.hip", "w4_dequant.hip", "w4_gemv.hip", "w4_gemm.hip",
-           "w4_workspace.cpp"]
+           "w4_workspace.cpp", "w4_fit.hip"]
 
 CFLAGS = [
     f"--offload-arch={ARCH}",

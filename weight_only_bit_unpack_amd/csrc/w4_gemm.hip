@@ -41,6 +41,7 @@ namespace w4 {
 namespace {
 
 constexpr int BM = 256, BN = 128, BK = 64;
+constexpr int kMaxSplits = 8;
 constexpr int STR = BK / 8 + 1;  // 16-byte units per LDS weight row (+1 pad: conflict-free reads)
 constexpr uint32_t kOOB = 0x80000000u;
 
@@ -395,11 +396,15 @@ __global__ __launch_bounds__(256) void splitk_reduce(const f32x4* __restrict__ p
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;  // < tiles * 4 * 32 * 64
   const int64_t per_split = (int64_t)tiles * 4 * 32 * 64;
   if (t >= per_split) return;
-  f32x4 v = partial[t];
-  for (int s = 1; s < S; ++s) {
-    const f32x4 w = partial[(int64_t)s * per_split + t];
-    v += w;
-  }
+  // every split's load in flight at once, then the sum in split order
+  f32x4 p[kMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s)
+    p[s] = s < S ? partial[(int64_t)s * per_split + t] : (f32x4){0.f, 0.f, 0.f, 0.f};
+  f32x4 v = p[0];
+#pragma unroll
+  for (int s = 1; s < kMaxSplits; ++s)
+    if (s < S) v += p[s];
   const int lane = (int)(t & 63), r4g = (int)((t >> 6) & 31), mw = (int)((t >> 11) & 3);
   const uint32_t tile = (uint32_t)(t >> 13);
   const int r32 = lane & 31, h = lane >> 5;
@@ -427,7 +432,7 @@ int gemm_splits(int64_t n, int64_t k, int m, int cus) {
   const int64_t tiles = ((n + BN - 1) / BN) * ((m + BM - 1) / BM);
   const int64_t steps = k / BK;
   int64_t s = tiles > 0 ? (cus + tiles - 1) / tiles : 1;
-  if (s > 8) s = 8;
+  if (s > kMaxSplits) s = kMaxSplits;
   if (s > steps / 8) s = steps / 8;
   return s < 1 ? 1 : (int)s;
 }

@@ -9,7 +9,8 @@ matrix.  One step = one pass over the stack (one batched launch), inputs
 resident in HBM.  `value` = algorithmic bytes of the pass (packed nibbles +
 bf16 scales + x + fp32 y) / step time, in GB/s.
 
-Also measured in the same run and reported under "rows": the same pass as
+Also measured in the same run and reported under "rows" (with a plain 1 GiB
+device copy as context for what HBM delivers on the box): the same pass as
 168 separate w4_gemv calls, quantize_pack and unpack_dequant over the stack,
 and the prefill GEMM (M = 256, K = N = 8192, in TFLOP/s) with quantize_pack of
 its 8192^2 weight.  The CPU baseline times the oracle (numpy, one thread) on
@@ -39,9 +40,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["headline", "gemm", "copy"], default=None,
+    ap.add_argument("--only", choices=["headline", "gemm", "copy", "fit"], default=None,
                     help="run one target only (for profiler runs): the batched decode pass, "
-                         "the M=256 GEMM, or a 1 GiB device copy that calibrates HBM counters")
+                         "the M=256 GEMM, a 1 GiB device copy that calibrates HBM counters, "
+                         "or the LUT16 k-means fit of the three 3.9B-sized matrices")
     ap.add_argument("--only-headline", action="store_true", help="same as --only headline")
     a = ap.parse_args()
     if a.only_headline:
@@ -207,6 +209,15 @@ def main():
         print(json.dumps({"target": "copy", "bytes_read": 1 << 30, "bytes_written": 1 << 30,
                           "ms": ms_c, "GB/s": 2 * (1 << 30) / (ms_c * 1e-3) / 1e9}), flush=True)
         return
+    if args.only == "fit":
+        for i, (n, k) in enumerate([(4096, 4096), (11008, 4096), (4096, 11008)]):
+            W = synthetic.normal_outliers_bf16_device((n, k), 0.015, 0.001, 0.15,
+                                                      synthetic.seed(3, i, 0), dev)
+            ms_f = timed(lambda: w4.w4_lut16_fit(W, 25, stream=stream), stream, args.steps,
+                         args.warmup)
+            print(json.dumps({"target": "fit", "shape": [n, k], "ms": ms_f,
+                              "Mgroups/s": n * k / 64 / (ms_f * 1e-3) / 1e6}), flush=True)
+        return
     if args.only == "gemm":
         ms_g, tf = time_gemm(w4, synthetic, torch, dev, stream, args)
         print(json.dumps({"target": "gemm", "ms": ms_g, "TFLOP/s": tf}), flush=True)
@@ -294,6 +305,13 @@ def main():
 
     if args.only is None:
         rows.update(other_configs(w4, synthetic, torch, dev, stream, args))
+        # context: what a plain device copy reaches on this GPU (read + write)
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        ms_c = timed(lambda: dst.copy_(src), stream, 20, 5)
+        rows["context_device_copy_1gib"] = {"ms": ms_c,
+                                            "GB/s_read_plus_write": 2 * (1 << 30) / (ms_c * 1e-3) / 1e9}
+        del src, dst
 
     # ---------------------------------------------------------- CPU baseline
     cpu = None

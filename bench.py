@@ -106,6 +106,21 @@ def time_gemm(w4, synthetic, torch, dev, stream, args):
     return ms_g, 2 * 256 * 8192 * 8192 / (ms_g * 1e-3) / 1e12
 
 
+def shared_table_levels(w):
+    """LUT16S side data for timing runs: group absmax scales and one table of
+    16 quantiles of the normalised weights (first 512 rows), built with torch
+    on the device.  Throughput does not depend on the values."""
+    import torch
+    n, k = w.shape
+    g = w.float().reshape(n, k // 64, 64)
+    s = g.abs().amax(dim=-1, keepdim=True)
+    u = torch.where(s > 0, g / torch.where(s > 0, s, torch.ones_like(s)), torch.zeros_like(g))
+    v = torch.sort(u[:512].reshape(-1)).values
+    q = (torch.arange(16, device=w.device) * (v.numel() // 16) + v.numel() // 32)
+    return (s.squeeze(-1).to(torch.bfloat16).contiguous(),
+            v[q].to(torch.bfloat16).contiguous())
+
+
 def magnitude_levels(w):
     """SIGNMAG8 magnitudes for timing runs: the Lloyd starting point (sorted
     |w| of each group of 32 at ranks 4q + 2, as fp16), built with torch on the
@@ -156,6 +171,25 @@ def other_configs(w4, synthetic, torch, dev, stream, args):
             b = n * k // 2 + n * (k // 64) * 34 + 2 * m * k + 4 * m * n
             rows[f"lut16_gemv_m{m}_{n}x{k}"] = {"ms": ms, "GB/s": b / (ms * 1e-3) / 1e9}
         del P, sc, L
+
+    # LUT16S (one table per matrix, 4.25 bits per weight): the three 3.9B-sized
+    # matrices in one batched m = 1 launch
+    log("LUT16S 3.9B-sized batched GEMV")
+    probs, total = [], 0
+    for i, (n, k) in enumerate([(4096, 4096), (11008, 4096), (4096, 11008)]):
+        W = synthetic.normal_outliers_bf16_device((n, k), 0.015, 0.001, 0.15,
+                                                  synthetic.seed(6, i, 0), dev)
+        sc, T = shared_table_levels(W)
+        P, _ = w4.w4_quantize_pack(W, w4.W4_LUT16S, scales=sc, codebook=T)
+        del W
+        x = synthetic.normal_bf16_device((1, k), 1.0, synthetic.seed(6, i, 1), dev)
+        probs.append({"packed": P, "scales": sc, "codebook": T, "x": x,
+                      "y": torch.empty((1, n), device=dev)})
+        total += n * k // 2 + n * (k // 64) * 2 + 32 + 2 * k + 4 * n
+    batch = w4.w4_gemv_batched_plan(probs, w4.W4_LUT16S)
+    ms = timed(lambda: batch(stream), stream, args.steps, args.warmup)
+    rows["lut16s_gemv_m1_3.9b_shapes_batched"] = {"ms": ms, "GB/s": total / (ms * 1e-3) / 1e9}
+    del probs, batch
 
     # SIGNMAG8: 224 x 2048^2, Student-t nu = 5; dense dequant + one batched m = 1 GEMV
     log("SIGNMAG8 2B stack")

@@ -38,12 +38,13 @@
  *
  * Quantized weight = three planar row-major arrays
  *   packed   uint8 [n][k/2]  nibble(r, c) = (packed[r][c/2] >> (4*(c%2))) & 15
- *   scales   bf16  [n][k/64] DYADIC, LUT16;           NULL for SIGNMAG8
+ *   scales   bf16  [n][k/64] DYADIC, LUT16, LUT16S;   NULL for SIGNMAG8
  *   codebook LUT16:    bf16 [n][k/64][16] normalised levels L_j;
+ *            LUT16S:   bf16 [16] normalised levels L_j shared by every group;
  *            SIGNMAG8: fp16 [n][k/32][8]  magnitudes M_j;    NULL for DYADIC
  * Reconstruction (w_hat, "dequantized weight"):
  *   DYADIC:   w_hat = RNE_bf16((s/8) * (nib - 8))    a zero result is +0.0
- *   LUT16:    w_hat = RNE_bf16(s * L[nib])
+ *   LUT16, LUT16S: w_hat = RNE_bf16(s * L[nib])
  *   SIGNMAG8: w_hat = (nib & 8 ? -1 : +1) * M[nib & 7]    (fp16, exact)
  * (RNE = round to nearest, ties to even.)
  */
@@ -66,7 +67,11 @@ typedef enum {
   W4_EHIP = 5          /* the kernel launch failed (hipGetLastError)                    */
 } w4_status;
 
-typedef enum { W4_DYADIC = 0, W4_LUT16 = 1, W4_SIGNMAG8 = 2 } w4_codec;
+/* W4_LUT16S: the LUT16 rebuild with one 16-level table for the whole weight
+ * and a bf16 scale per group of 64 -- 4.25 bits per weight plus 32 bytes, the
+ * size [KM] sec. 2.1 states for its 3.9B model (about 2.1 GB).  The table is
+ * an input; the oracle fits it by k-means over the whole weight. */
+typedef enum { W4_DYADIC = 0, W4_LUT16 = 1, W4_SIGNMAG8 = 2, W4_LUT16S = 3 } w4_codec;
 
 /* Largest k of a matrix product call: keeps every per-block byte offset of the
  * kernels within 32 bits. */
@@ -89,6 +94,7 @@ int32_t w4_group_size(int32_t codec);
  *             codes; an all-zero group gets s = +0 and idx 8.  codebook: NULL.
  *   LUT16:    reads scales (bf16 [n][k/64]) and codebook (bf16 [n][k/64][16]);
  *             idx = the lowest j minimising |fl32(w - s*L_j)| (fp32 decision).
+ *   LUT16S:   as LUT16 with the one table codebook (bf16 [16]) for every group.
  *   SIGNMAG8: reads codebook (fp16 [n][k/32][8]); scales: NULL;
  *             nibble = (w < 0) << 3 | the lowest j minimising |fl32(|w| - M_j)|.
  * w: bf16 [n][k], 16-byte aligned.  packed: uint8 [n][k/2], 16-byte aligned.

@@ -138,3 +138,55 @@ def fit(w_bits, iters=LLOYD_ITERS):
     c = np.where((s == 0.0)[:, None], 0.0, c)
     s_bits = f32_to_bf16_bits_exact(s.astype(np.float32)).reshape(n, g)
     return s_bits, rne_bf16(c).reshape(n, g, N_LEVELS)
+
+
+# ----------------------------------------------------------------- LUT16S
+# One 16-level table for the whole weight plus a bf16 scale (the group's
+# absmax) per group of 64: the reading of the k-means page under which its
+# 3.9B model takes about 2.1 GB (section 2.1; 4.25 bits per weight).  The
+# rebuild and the nearest-level rule are LUT16's with that table in every
+# group.
+
+def group_scales(w_bits):
+    """Group absmax as bf16 bits [N, K/64] (exact: the absmax is a bf16 value)."""
+    w_bits = np.asarray(w_bits)
+    n, k = w_bits.shape
+    w = bf16_to_f64(w_bits).reshape(n, k // GROUP, GROUP)
+    s = np.max(np.abs(w), axis=-1)
+    return f32_to_bf16_bits_exact(s.astype(np.float32))
+
+
+def shared_tables(s_bits, table_bits):
+    """The one table [16] repeated for every group: [N, K/64, 16]."""
+    return np.broadcast_to(np.asarray(table_bits, dtype=np.uint16), s_bits.shape + (N_LEVELS,))
+
+
+def fit_shared(w_bits, iters=LLOYD_ITERS):
+    """Whole-weight k-means table.  w [N, K] -> (scale bits [N, K/64], table bits [16]).
+
+    u = w / s per group (fp64; an all-zero group gives zeros); the start is
+    ``sorted(u)[q * (T/16) + T/32]`` over all T = N*K values of u in row-major
+    element order (stable sort); then `iters` Lloyd rounds exactly as in the
+    per-group fit, over all of u at once: nearest centre with the lowest index
+    on ties, each centre moved to the fp64 sum of its members in increasing
+    element order divided by their count, an empty centre kept.  Levels are
+    ``RNE_bf16(c)``.  Test-data generator: parity unpinned beyond the
+    procedure pins (it equals the per-group fit on a one-group weight)."""
+    w_bits = np.asarray(w_bits)
+    n, k = w_bits.shape
+    s_bits = group_scales(w_bits)
+    w = bf16_to_f64(w_bits).reshape(n, k // GROUP, GROUP)
+    s = bf16_to_f64(s_bits)[..., None]
+    u = (w / np.where(s == 0.0, 1.0, s)).reshape(-1)
+    t = u.size
+    stride = t // N_LEVELS
+    c = np.sort(u, kind="stable")[stride * np.arange(N_LEVELS) + stride // 2].copy()
+    for _ in range(iters):
+        a = np.empty(t, dtype=np.int64)
+        for i0 in range(0, t, 1 << 20):                  # assignment in chunks
+            d = np.abs(u[i0:i0 + (1 << 20), None] - c[None, :])
+            a[i0:i0 + (1 << 20)] = np.argmin(d, axis=-1)
+        sums = np.bincount(a, weights=u, minlength=N_LEVELS)  # one pass in element order
+        cnt = np.bincount(a, minlength=N_LEVELS)
+        c = np.where(cnt > 0, sums / np.maximum(cnt, 1), c)
+    return s_bits, rne_bf16(c)

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(w4):
 
 
 def test_group_sizes_and_status_strings(w4):
-    assert [w4.w4_group_size(c) for c in (0, 1, 2, 7)] == [64, 64, 32, -1]
+    assert [w4.w4_group_size(c) for c in (0, 1, 2, 3, 7)] == [64, 64, 32, 64, -1]
     for s in range(6):
         assert w4.w4_status_str(s).startswith("W4_")
 
@@ -52,7 +52,7 @@ def _gemv(w4, codec=0, n=16, k=64, packed=16, scales=16, cb=16, x=16, m=1, y=16,
 
 def test_validation_errors(w4):
     E = {"inval": 1, "shape": 2, "align": 3, "unsup": 4}
-    assert _gemv(w4, codec=3) == E["inval"]
+    assert _gemv(w4, codec=4) == E["inval"]
     assert _gemv(w4, n=-1) == E["inval"]
     assert _gemv(w4, k=96) == E["shape"]
     assert _gemv(w4, m=17) == E["shape"]
@@ -62,6 +62,9 @@ def test_validation_errors(w4):
     assert _gemv(w4, scales=None) == E["inval"]
     assert _gemv(w4, scales=17) == E["align"]
     assert _gemv(w4, codec=1, cb=None) == E["inval"]
+    assert _gemv(w4, codec=3, cb=None) == E["inval"]
+    assert _gemv(w4, codec=3, scales=None) == E["inval"]
+    assert _gemv(w4, codec=3, cb=24) == E["align"]
     assert _gemv(w4, codec=2, scales=None, cb=32 + 8) == E["align"]
     assert _gemv(w4, x=None) == E["inval"]
     assert _gemv(w4, x=24) == E["align"]

@@ -142,6 +142,45 @@ def test_fullsize_lut16(w4, n, k):
         _check_outputs(y, rows, host_bits(x), w_hat)
 
 
+# ------------------------------------------------------------ 3.9B-sized LUT16S
+def test_fullsize_lut16s_batched():
+    """The three 3.9B-sized matrices in the one-table reading (4.25 bits per
+    weight): group scales = absmax (oracle, whole matrix), the table from the
+    oracle's whole-weight k-means over the first 512 rows of each matrix;
+    quantize + dequant bit-exact and one batched m = 1 GEMV over all three on
+    sampled rows."""
+    import weight_only_bit_unpack_amd as w4
+    report("fullsize_lut16s")
+    probs, checks = [], []
+    for i, (n, k) in enumerate(synthetic.llama39b_shapes()):
+        w = synthetic.normal_outliers_bf16_device((n, k), 0.015, 0.001, 0.15,
+                                                  synthetic.seed(6, i, 0))
+        wb = host_bits(w)
+        s = lut16.group_scales(wb)
+        _, T = lut16.fit_shared(wb[:512], iters=10)
+        args = dict(scales=dev_bf16(s), codebook=dev_bf16(T))
+        p, _ = w4.w4_quantize_pack(w, w4.W4_LUT16S, **args)
+        d = w4.w4_unpack_dequant(p, w4.W4_LUT16S, **args)
+        torch.cuda.synchronize()
+        rows = _rows(n, 8100 + i)
+        sel = torch.as_tensor(rows, device="cuda")
+        tables = np.ascontiguousarray(lut16.shared_tables(s[rows], T))
+        idx = native.lut16_indices(wb[rows], s[rows], tables)
+        assert np.array_equal(host_u8(p.index_select(0, sel)), packing.pack(idx))
+        deq = lut16.dequant_from_indices(idx, s[rows], tables)
+        assert np.array_equal(host_bits(d.index_select(0, sel)), deq)
+        del w, d, wb
+        x = synthetic.normal_bf16_device((1, k), 1.0, synthetic.seed(6, i, 1))
+        y = torch.full((1, n), float("nan"), device="cuda")
+        probs.append(dict(packed=p, x=x, y=y, **args))
+        checks.append((rows, bits.bf16_to_f64(deq)))
+    batch = w4.w4_gemv_batched_plan(probs, w4.W4_LUT16S)
+    batch()
+    torch.cuda.synchronize()
+    for pr, (rows, w_hat) in zip(probs, checks):
+        _check_outputs(pr["y"], rows, host_bits(pr["x"]), w_hat)
+
+
 # ------------------------------------------------------------ 2B SIGNMAG8
 def test_fullsize_signmag8_stack(w4):
     """2048^2 matrices, Student-t nu = 5 at sigma 0.02, group 32 sign +

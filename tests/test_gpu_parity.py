@@ -258,6 +258,46 @@ def test_lut16_gemv_and_gemm(w4, m):
     _gemv_check(y2, x, w_hat, False)
 
 
+# ------------------------------------------------------------------ LUT16S
+def _lut16s_case(n, k, seed):
+    """Weight with a zero group, its group scales and the oracle's whole-weight
+    table, the table repeated per group, and the oracle's indices."""
+    w = synthetic.normal_outliers_bf16((n, k), 0.015, 0.001, 0.15, seed)
+    w[0, :64] = 0
+    s, T = lut16.fit_shared(w, iters=10)
+    tables = np.ascontiguousarray(lut16.shared_tables(s, T))
+    return w, s, T, tables, native.lut16_indices(w, s, tables)
+
+
+@pytest.mark.parametrize("n,k", [(300, 1024), (37, 320)])
+def test_lut16s_quantize_dequant_bitexact(w4, n, k):
+    report("lut16s_quant", n=n, k=k)
+    w, s, T, tables, idx = _lut16s_case(n, k, 950 + n)
+    args = dict(scales=dev_bf16(s), codebook=dev_bf16(T))
+    p, _ = w4.w4_quantize_pack(dev_bf16(w), w4.W4_LUT16S, **args)
+    d = w4.w4_unpack_dequant(p, w4.W4_LUT16S, **args)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_u8(p), packing.pack(idx))
+    assert np.array_equal(host_bits(d), lut16.dequant_from_indices(idx, s, tables))
+
+
+@pytest.mark.parametrize("m", [1, 4, 16, 130])
+def test_lut16s_matmul(w4, m):
+    """GEMV (m <= 16: single call, fp32 and bf16 y) or GEMM (m = 130)."""
+    n, k = 300, 1024
+    report("lut16s_matmul", n=n, k=k, m=m)
+    w, s, T, tables, idx = _lut16s_case(n, k, 960 + m)
+    w_hat = bits.bf16_to_f64(lut16.dequant_from_indices(idx, s, tables))
+    x = synthetic.normal_bf16((m, k), 1.0, 961 + m)
+    args = dict(scales=dev_bf16(s), codebook=dev_bf16(T))
+    fn = w4.w4_gemv if m <= 16 else w4.w4_gemm
+    y = fn(dev_u8(packing.pack(idx)), dev_bf16(x), w4.W4_LUT16S, **args)
+    yb = fn(dev_u8(packing.pack(idx)), dev_bf16(x), w4.W4_LUT16S, y_dtype=torch.bfloat16, **args)
+    torch.cuda.synchronize()
+    _gemv_check(y, x, w_hat, False)
+    _gemv_check(yb, x, w_hat, True)
+
+
 # ------------------------------------------------------------------ SIGNMAG8
 def _sm_case(n, k, seed):
     w = synthetic.student_t_bf16((n, k), 5, 0.02, seed)
@@ -310,6 +350,10 @@ def _batched_case(codec, n, k, seed):
         idx = native.lut16_indices(w, s, L)
         w_hat = bits.bf16_to_f64(lut16.dequant_from_indices(idx, s, L))
         return packing.pack(idx), dict(scales=dev_bf16(s), codebook=dev_bf16(L)), w_hat
+    if codec == 3:
+        w, s, T, tables, idx = _lut16s_case(n, k, seed)
+        w_hat = bits.bf16_to_f64(lut16.dequant_from_indices(idx, s, tables))
+        return packing.pack(idx), dict(scales=dev_bf16(s), codebook=dev_bf16(T)), w_hat
     w, cb = _sm_case(n, k, seed)
     nib = native.signmag8_indices(w, cb)
     return packing.pack(nib), dict(codebook=dev_f16(cb)), signmag8.dequant_values(cb, nib)
@@ -321,6 +365,8 @@ def _batched_case(codec, n, k, seed):
     (0, 4, [(1000, 2048), (64, 1024), (333, 832)]),
     (1, 1, [(300, 1024), (129, 2048)]),
     (2, 3, [(300, 1024), (65, 2048)]),
+    (3, 1, [(300, 1024), (129, 2048), (64, 64)]),
+    (3, 16, [(300, 1024), (70, 832)]),
 ])
 def test_gemv_batched_codecs(w4, codec, m, shapes):
     report("gemv_batched_codecs", codec=codec, m=m, count=len(shapes))

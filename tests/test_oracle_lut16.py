@@ -194,6 +194,47 @@ def test_lut16_c_matches_python_on_ties():
     assert np.array_equal(L0[0, 0], bits.rne_bf16(bits.bf16_to_f64(want)))
 
 
+# ------------------------------------------------------------------ LUT16S
+def test_lut16s_fit_equals_group_fit_on_one_group():
+    # with a single group the whole-weight fit and the per-group fit coincide
+    for seed in (1, 2, 3):
+        w = synthetic.normal_outliers_bf16((1, 64), 0.015, 0.05, 0.15, seed)
+        s, L = lut16.fit(w)
+        s2, T = lut16.fit_shared(w)
+        assert np.array_equal(s, s2) and np.array_equal(L[0, 0], T)
+
+
+def test_lut16s_fit_recovers_16_values_and_roundtrips():
+    # every group holds the same 16 normalised values (4 copies each, absmax 1)
+    # times a power-of-two scale: the start already sits on them, Lloyd keeps
+    # them, and quantize -> dequant reproduces the weight exactly
+    g = np.random.default_rng(11)
+    vals = np.sort(g.choice(np.arange(-127, 128), 16, replace=False)) / 128.0
+    vals[-1] = 1.0
+    rows = []
+    for r in range(6):
+        groups = [g.permutation(np.repeat(vals, 4)) * 2.0 ** int(g.integers(-20, 5))
+                  for _ in range(3)]
+        rows.append(np.concatenate(groups))
+    w = bits.rne_bf16(np.stack(rows))
+    s, T = lut16.fit_shared(w)
+    assert np.array_equal(bits.bf16_to_f64(T), vals)
+    tables = lut16.shared_tables(s, T)
+    p = lut16.quantize_pack(w, s, tables)
+    assert np.array_equal(lut16.dequant(p, s, tables), w)
+    assert np.array_equal(s, lut16.group_scales(w))
+
+
+def test_lut16s_zero_groups_and_scale():
+    w = _lut_data(4, 256, 41)
+    w[1, 64:128] = 0
+    s, T = lut16.fit_shared(w)
+    assert s[1, 1] == 0
+    tables = lut16.shared_tables(s, T)
+    d = lut16.dequant(lut16.quantize_pack(w, s, tables), s, tables)
+    assert np.all(bits.bf16_to_f64(d[1, 64:128]) == 0)
+
+
 # ------------------------------------------------------------------ SIGNMAG8
 def _sm_data(rows=8, k=512, seed=31):
     return synthetic.student_t_bf16((rows, k), 5, 0.02, seed)

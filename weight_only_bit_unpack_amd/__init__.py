@@ -17,9 +17,9 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libw4.so")
 
-W4_DYADIC, W4_LUT16, W4_SIGNMAG8 = 0, 1, 2
+W4_DYADIC, W4_LUT16, W4_SIGNMAG8, W4_LUT16S = 0, 1, 2, 3
 W4_F32, W4_BF16, W4_F16 = 0, 1, 2
-GROUP = {W4_DYADIC: 64, W4_LUT16: 64, W4_SIGNMAG8: 32}
+GROUP = {W4_DYADIC: 64, W4_LUT16: 64, W4_SIGNMAG8: 32, W4_LUT16S: 64}
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -109,10 +109,12 @@ def _need(t, name, dtypes, shape=None):
 
 def _side_tables(codec, n, k, scales, codebook):
     g = GROUP[codec]
-    if codec in (W4_DYADIC, W4_LUT16):
+    if codec in (W4_DYADIC, W4_LUT16, W4_LUT16S):
         _need(scales, "scales", _U16, (n, k // 64))
     if codec == W4_LUT16:
         _need(codebook, "codebook", _U16, (n, k // 64, 16))
+    if codec == W4_LUT16S:
+        _need(codebook, "codebook", _U16, (16,))
     if codec == W4_SIGNMAG8:
         _need(codebook, "codebook", _U16, (n, k // g, 8))
 

@@ -14,7 +14,9 @@ namespace {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-bool valid_codec(int32_t c) { return c == W4_DYADIC || c == W4_LUT16 || c == W4_SIGNMAG8; }
+bool valid_codec(int32_t c) {
+  return c == W4_DYADIC || c == W4_LUT16 || c == W4_SIGNMAG8 || c == W4_LUT16S;
+}
 
 // Checks the quantized-weight triple of a codec for an [n][k] weight.
 w4_status check_weight(int32_t codec, int64_t n, int64_t k, const void* packed, const void* scales,
@@ -25,11 +27,11 @@ w4_status check_weight(int32_t codec, int64_t n, int64_t k, const void* packed, 
   if (n == 0 || k == 0) return W4_OK;
   if (!packed) return W4_EINVAL;
   if (!aligned(packed, 16)) return W4_EALIGN;
-  if (codec == W4_DYADIC || codec == W4_LUT16) {
+  if (codec == W4_DYADIC || codec == W4_LUT16 || codec == W4_LUT16S) {
     if (!scales) return W4_EINVAL;
     if (!aligned(scales, 2)) return W4_EALIGN;
   }
-  if (codec == W4_LUT16 || codec == W4_SIGNMAG8) {
+  if (codec == W4_LUT16 || codec == W4_SIGNMAG8 || codec == W4_LUT16S) {
     if (!codebook) return W4_EINVAL;
     if (!aligned(codebook, 16)) return W4_EALIGN;
   }
@@ -96,6 +98,7 @@ int32_t w4_group_size(int32_t codec) {
   switch (codec) {
     case W4_DYADIC: return 64;
     case W4_LUT16: return 64;
+    case W4_LUT16S: return 64;
     case W4_SIGNMAG8: return 32;
     default: return -1;
   }

@@ -44,16 +44,17 @@ __global__ __launch_bounds__(256) void dequant_dyadic_kernel(const u32x4* __rest
   }
 }
 
+// shared: one table for every group (LUT16S)
 __global__ __launch_bounds__(256) void dequant_lut16_kernel(const u32x4* __restrict__ packed,
                                                             const uint16_t* __restrict__ scales,
                                                             const u32x4* __restrict__ lut,
                                                             u32x4* __restrict__ out,
-                                                            int64_t nchunks) {
+                                                            int64_t nchunks, int shared) {
   const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (c >= nchunks) return;
-  const int64_t g = c >> 1;
+  const int64_t g = c >> 1, gt = shared ? 0 : g;
   const u32x4 p = __builtin_nontemporal_load(&packed[c]);
-  const Lut16Table t = lut16_table(scales[g], lut[2 * g], lut[2 * g + 1]);
+  const Lut16Table t = lut16_table(scales[g], lut[2 * gt], lut[2 * gt + 1]);
   const uint32_t pw[4] = {p.x, p.y, p.z, p.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -103,9 +104,9 @@ hipError_t launch_dequant(int codec, int64_t n, int64_t k, const uint8_t* packed
   auto* o = reinterpret_cast<u32x4*>(out);
   if (codec == 0)
     dequant_dyadic_kernel<<<dim3((uint32_t)blocks), dim3(256), 0, stream>>>(pk, scales, o, nchunks);
-  else if (codec == 1)
+  else if (codec == 1 || codec == 3)
     dequant_lut16_kernel<<<dim3((uint32_t)blocks), dim3(256), 0, stream>>>(
-        pk, scales, reinterpret_cast<const u32x4*>(codebook), o, nchunks);
+        pk, scales, reinterpret_cast<const u32x4*>(codebook), o, nchunks, codec == 3);
   else
     dequant_signmag8_kernel<<<dim3((uint32_t)blocks), dim3(256), 0, stream>>>(
         pk, reinterpret_cast<const u32x4*>(codebook), o, nchunks);

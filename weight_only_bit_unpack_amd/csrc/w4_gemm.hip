@@ -55,6 +55,11 @@ __device__ __forceinline__ uint32_t opaque(uint32_t v) {
   return v;
 }
 
+// The one 16-level table of a LUT16S weight, loaded once per thread.
+struct SharedTable {
+  u32x4 l0, l1;
+};
+
 // Packed bytes and side data one thread rebuilds per k-step: weight row
 // tid / 4, k = 16 (tid % 4) .. + 15 of the step (8 packed bytes).  The rebuilt
 // values go to LDS in natural k order (the activations stay as loaded).
@@ -74,7 +79,7 @@ struct WRaw<0> {  // DYADIC: bf16 scale of the row's 64-group
     sb = __builtin_amdgcn_raw_buffer_load_b16(s0, so, 0, 0);
   }
   template <int D>
-  __device__ __forceinline__ void rebuild(u32x4& hi, u32x4&) const {
+  __device__ __forceinline__ void rebuild(u32x4& hi, u32x4&, const SharedTable&) const {
     const DyadicScale d = dyadic_scale(sb);
     const uint32_t m0 = 0x000F000Fu, m1 = 0x00F000F0u, mg = kMagic;
     const float nz = __builtin_bit_cast(float, opaque(0x80000000u));
@@ -98,7 +103,7 @@ struct WRaw<1> {  // LUT16: 16 bf16 levels + bf16 scale of the row's 64-group
     sb = __builtin_amdgcn_raw_buffer_load_b16(s0, so, 0, 0);
   }
   template <int D>
-  __device__ __forceinline__ void rebuild(u32x4& hi, u32x4&) const {
+  __device__ __forceinline__ void rebuild(u32x4& hi, u32x4&, const SharedTable&) const {
     const Lut16Table t = lut16_table(sb, l0, l1);
     hi = sigma_to_natural(lut16_rebuild(D == 0 ? p0 : p1, t));
   }
@@ -117,12 +122,31 @@ struct WRaw<2> {  // SIGNMAG8: 8 fp16 magnitudes of the row's 32-group
     c = __builtin_amdgcn_raw_buffer_load_b128(s1, co, 0, 0);
   }
   template <int D>
-  __device__ __forceinline__ void rebuild(u32x4& hi, u32x4& lo) const {
+  __device__ __forceinline__ void rebuild(u32x4& hi, u32x4& lo, const SharedTable&) const {
     const SignMagTable t = signmag_table(c);
     u32x4 h, l;
     signmag_rebuild(D == 0 ? p0 : p1, t, h, l);
     hi = sigma_to_natural(h);
     lo = sigma_to_natural(l);
+  }
+};
+
+template <>
+struct WRaw<3> {  // LUT16S: bf16 scale of the row's 64-group; levels shared
+  uint32_t p0, p1;
+  uint16_t sb;
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t pk, __amdgpu_buffer_rsrc_t s0,
+                                       __amdgpu_buffer_rsrc_t, uint32_t po, uint32_t so,
+                                       uint32_t) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(pk, po, 0, 0);
+    p0 = v[0];
+    p1 = v[1];
+    sb = __builtin_amdgcn_raw_buffer_load_b16(s0, so, 0, 0);
+  }
+  template <int D>
+  __device__ __forceinline__ void rebuild(u32x4& hi, u32x4&, const SharedTable& st) const {
+    const Lut16Table t = lut16_table(sb, st.l0, st.l1);
+    hi = sigma_to_natural(lut16_rebuild(D == 0 ? p0 : p1, t));
   }
 };
 
@@ -171,7 +195,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const uint32_t row_bytes = (uint32_t)(K >> 1);
   const __amdgpu_buffer_rsrc_t pk = rsrc(P.packed + n0 * (K >> 1), (uint32_t)rows_n * row_bytes);
   __amdgpu_buffer_rsrc_t s0 = pk, s1 = pk;
-  if constexpr (CODEC == 0) {
+  if constexpr (CODEC == 0 || CODEC == 3) {
     s0 = rsrc(P.scales + n0 * (K >> 6), (uint32_t)(rows_n * (K >> 6) * 2));
   } else if constexpr (CODEC == 1) {
     s0 = rsrc(P.scales + n0 * (K >> 6), (uint32_t)(rows_n * (K >> 6) * 2));
@@ -215,11 +239,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         xv[i][kk] = __builtin_amdgcn_raw_buffer_load_b128(
             xr, base + (uint32_t)i * x_i + (uint32_t)kk * 1024u, 0, 0);
   };
+  SharedTable st{};
+  if constexpr (CODEC == 3) {
+    st.l0 = reinterpret_cast<const u32x4*>(P.codebook)[0];
+    st.l1 = reinterpret_cast<const u32x4*>(P.codebook)[1];
+  }
   // rebuild packed dword D (k = 16 wq + 8 D .. + 7 of the step) into LDS
   auto rebuild = [&](const WRaw<CODEC>& r, int buf, auto dtag) {
     constexpr int D = decltype(dtag)::value;
     u32x4 hi, lo;
-    r.template rebuild<D>(hi, lo);
+    r.template rebuild<D>(hi, lo, st);
     wtile(buf, 0)[wr * STR + 2 * wq + D] = hi;
     if constexpr (NPL == 2) wtile(buf, 1)[wr * STR + 2 * wq + D] = lo;
   };
@@ -479,6 +508,8 @@ hipError_t launch_gemm(int codec, const GemvProblem& p, int m, int y_bf16, hipSt
     e = launch_codec<0>(p, m, y_bf16, xpk, partial, blocks, stream);
   else if (codec == 1)
     e = launch_codec<1>(p, m, y_bf16, xpk, partial, blocks, stream);
+  else if (codec == 3)
+    e = launch_codec<3>(p, m, y_bf16, xpk, partial, blocks, stream);
   else
     e = launch_codec<2>(p, m, y_bf16, xpk, partial, blocks, stream);
   if (e != hipSuccess || S == 1) return e;

@@ -84,6 +84,11 @@ struct Shuffle {
   }
 };
 
+// The one 16-level table of a LUT16S weight, loaded once per wave.
+struct SharedTable {
+  u32x4 l0, l1;
+};
+
 // Raw per-step loads of one lane: 32 packed bytes plus the side data of the
 // group(s) they belong to.  `sp` / `ss` are the step's uniform byte offsets
 // into the packed and side arrays, or kOOB for a padding step.
@@ -102,7 +107,7 @@ struct Raw<0> {  // DYADIC: one bf16 scale per 64-group
     sb = __builtin_amdgcn_raw_buffer_load_b16(S.side, L.s + ss, 0, 0);
   }
   template <typename F>
-  __device__ __forceinline__ void apply(const Shuffle& sh, F&& mma) const {
+  __device__ __forceinline__ void apply(const Shuffle& sh, const SharedTable&, F&& mma) const {
     u32x4 p0, p1;
     sh(a0, a1, p0, p1);
     const uint32_t pw[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
@@ -134,7 +139,7 @@ struct Raw<1> {  // LUT16: 16 bf16 levels (side) + bf16 scale (side2) per 64-gro
     sb = __builtin_amdgcn_raw_buffer_load_b16(S.side2, L.s2 + (ss == kOOB ? kOOB : ss >> 4), 0, 0);
   }
   template <typename F>
-  __device__ __forceinline__ void apply(const Shuffle& sh, F&& mma) const {
+  __device__ __forceinline__ void apply(const Shuffle& sh, const SharedTable&, F&& mma) const {
     u32x4 p0, p1;
     sh(a0, a1, p0, p1);
     const uint32_t pw[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
@@ -157,7 +162,7 @@ struct Raw<2> {  // SIGNMAG8: two 32-groups, 8 fp16 magnitudes each
     c1 = __builtin_amdgcn_raw_buffer_load_b128(S.side, coff + 16, 0, 0);
   }
   template <typename F>
-  __device__ __forceinline__ void apply(const Shuffle& sh, F&& mma) const {
+  __device__ __forceinline__ void apply(const Shuffle& sh, const SharedTable&, F&& mma) const {
     u32x4 p0, p1;
     sh(a0, a1, p0, p1);
     const uint32_t pw[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
@@ -169,6 +174,28 @@ struct Raw<2> {  // SIGNMAG8: two 32-groups, 8 fp16 magnitudes each
       mma(j, h);
       mma(j, l);
     }
+  }
+};
+
+template <>
+struct Raw<3> {  // LUT16S: one bf16 scale per 64-group (side); levels shared
+  static constexpr uint32_t kSideStep = 8;  // 4 groups x 2 bytes per 256-k step
+  u32x4 a0, a1;
+  uint16_t sb;
+  __device__ __forceinline__ void fetch(const Slice& S, const LaneBase& L, uint32_t sp,
+                                        uint32_t ss) {
+    a0 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, L.pa + sp, 0, 0);
+    a1 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, L.pb + sp, 0, 0);
+    sb = __builtin_amdgcn_raw_buffer_load_b16(S.side, L.s + ss, 0, 0);
+  }
+  template <typename F>
+  __device__ __forceinline__ void apply(const Shuffle& sh, const SharedTable& st, F&& mma) const {
+    u32x4 p0, p1;
+    sh(a0, a1, p0, p1);
+    const uint32_t pw[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+    const Lut16Table t = lut16_table(sb, st.l0, st.l1);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mma(j, lut16_rebuild(pw[j], t));
   }
 };
 
@@ -259,7 +286,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvProblem single, const Gem
   const uint32_t row_bytes = (uint32_t)(K >> 1);
   const uint32_t g64 = (uint32_t)(K >> 6);  // 64-groups per row
   S.packed = rsrc(P.packed + row0 * (K >> 1), (uint32_t)rows_here * row_bytes);
-  if constexpr (CODEC == 0) {
+  if constexpr (CODEC == 0 || CODEC == 3) {
     S.side = rsrc(P.scales + row0 * (K >> 6), (uint32_t)rows_here * g64 * 2);
   } else if constexpr (CODEC == 1) {
     S.side = rsrc(P.codebook + row0 * (K >> 6) * 16, (uint32_t)rows_here * g64 * 32);
@@ -270,6 +297,11 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvProblem single, const Gem
   S.x = rsrc(P.x, (uint32_t)(m * K * 2));
 
   const int64_t kc = gemv_chunk(m, xs_units, kend - kbeg);
+  SharedTable st{};
+  if constexpr (CODEC == 3) {
+    st.l0 = reinterpret_cast<const u32x4*>(P.codebook)[0];
+    st.l1 = reinterpret_cast<const u32x4*>(P.codebook)[1];
+  }
   const int row_units = (int)(kc / 8) + 1;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 
@@ -286,7 +318,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvProblem single, const Gem
       const uint32_t g0 = rloc * g64 + (uint32_t)((k0 >> 6) + q);  // lane's first 64-group
       L.pa = rowA * row_bytes + (uint32_t)(k0 >> 1) + chA;
       L.pb = (rowA + 8) * row_bytes + (uint32_t)(k0 >> 1) + chB;
-      L.s = CODEC == 0 ? g0 * 2 : g0 * 32;
+      L.s = (CODEC == 0 || CODEC == 3) ? g0 * 2 : g0 * 32;
       L.s2 = g0 * 2;
     }
     auto fetch = [&](Raw<CODEC>& r, int i) {
@@ -341,7 +373,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvProblem single, const Gem
 
     auto compute = [&](const Raw<CODEC>& r, int i) {
       const u32x4* xa = &xs[mr * row_units + 32 * step_of(i) + 8 * q];
-      r.apply(sh, [&](int j, const u32x4& b) { acc = mfma16x16x32(xa[j], b, acc); });
+      r.apply(sh, st, [&](int j, const u32x4& b) { acc = mfma16x16x32(xa[j], b, acc); });
     };
     // three buffers in rotation: a buffer is refilled right after it is used,
     // so two steps stay in flight while one is computed and no live buffer is
@@ -504,6 +536,7 @@ hipError_t launch_codec(const GemvProblem& p, int m, int y_bf16, hipStream_t str
 hipError_t launch_gemv(int codec, const GemvProblem& p, int m, int y_bf16, hipStream_t stream) {
   if (codec == 0) return launch_codec<0>(p, m, y_bf16, stream);
   if (codec == 1) return launch_codec<1>(p, m, y_bf16, stream);
+  if (codec == 3) return launch_codec<3>(p, m, y_bf16, stream);
   return launch_codec<2>(p, m, y_bf16, stream);
 }
 
@@ -531,6 +564,7 @@ hipError_t launch_gemv_batched(int codec, const GemvProblem* probs_dev, int coun
   const int xu = xs_units_for(m, k_max);
   if (codec == 0) return launch_batched_codec<0>(probs_dev, count, total_tiles, xu, m, y_bf16, stream);
   if (codec == 1) return launch_batched_codec<1>(probs_dev, count, total_tiles, xu, m, y_bf16, stream);
+  if (codec == 3) return launch_batched_codec<3>(probs_dev, count, total_tiles, xu, m, y_bf16, stream);
   return launch_batched_codec<2>(probs_dev, count, total_tiles, xu, m, y_bf16, stream);
 }
 

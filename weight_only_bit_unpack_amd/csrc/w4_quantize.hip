@@ -100,19 +100,19 @@ __global__ __launch_bounds__(256) void quantize_dyadic_kernel(const u32x4* __res
   }
 }
 
-// LUT16: levels v_j = s * L_j (exact in fp32); index = lowest j minimising
-// |fl32(w - v_j)|.
+// LUT16 / LUT16S: levels v_j = s * L_j (exact in fp32); index = lowest j
+// minimising |fl32(w - v_j)|.  shared: one table for every group (LUT16S).
 __global__ __launch_bounds__(256) void quantize_lut16_kernel(const u32x4* __restrict__ w,
                                                              uint32_t* __restrict__ packed,
                                                              const uint16_t* __restrict__ scales,
                                                              const u32x4* __restrict__ lut,
-                                                             int64_t nchunks) {
+                                                             int64_t nchunks, int shared) {
   const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (c >= nchunks) return;
-  const int64_t g = c >> 3;
+  const int64_t g = c >> 3, gt = shared ? 0 : g;
   const u32x4 v = __builtin_nontemporal_load(&w[c]);
   const float s = bf16_bits_to_f32(scales[g]);
-  const u32x4 l0 = lut[2 * g], l1 = lut[2 * g + 1];
+  const u32x4 l0 = lut[2 * gt], l1 = lut[2 * gt + 1];
   const uint32_t lw[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
   float lv[16];
 #pragma unroll
@@ -188,9 +188,9 @@ hipError_t launch_quantize(int codec, int64_t n, int64_t k, const uint16_t* w, u
   auto* pk = reinterpret_cast<uint32_t*>(packed);
   if (codec == 0)
     quantize_dyadic_kernel<<<dim3((uint32_t)blocks), dim3(256), 0, stream>>>(wv, pk, scales, nchunks);
-  else if (codec == 1)
+  else if (codec == 1 || codec == 3)
     quantize_lut16_kernel<<<dim3((uint32_t)blocks), dim3(256), 0, stream>>>(
-        wv, pk, scales, reinterpret_cast<const u32x4*>(codebook), nchunks);
+        wv, pk, scales, reinterpret_cast<const u32x4*>(codebook), nchunks, codec == 3);
   else
     quantize_signmag8_kernel<<<dim3((uint32_t)blocks), dim3(256), 0, stream>>>(
         wv, pk, reinterpret_cast<const u32x4*>(codebook), nchunks);

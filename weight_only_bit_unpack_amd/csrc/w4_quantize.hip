@@ -3,7 +3,8 @@
 // DyadicGumbel page, sections 2.1-2.3 and 2.5: per group of 64 weights a bf16
 // scale (the group absmax here) and for each weight the hard argmin over the
 // 16 codes (scale/8)*(j-8); two 4-bit indices per byte, low nibble first.
-// k-means page, section 1.2: nearest of the group's 16 LUT levels.
+// k-means page, section 1.2: nearest of the group's 16 LUT levels (a table
+// per group, LUT16, or one table for the whole weight, LUT16S).
 // int4-g32 page, sections 1.3 and 2: sign bit + nearest of 8 magnitudes.
 //
 // One thread handles 8 consecutive weights (one 16-byte load, one 4-byte

@@ -191,6 +191,34 @@ def other_configs(w4, synthetic, torch, dev, stream, args):
     rows["lut16s_gemv_m1_3.9b_shapes_batched"] = {"ms": ms, "GB/s": total / (ms * 1e-3) / 1e9}
     del probs, batch
 
+    # DYADIC5 (3/4/5-bit groups in one 5-bit index space): the 1B decode stack
+    # with widths 3, 4, 5 drawn per group, one batched m = 1 launch, and the
+    # quantizer on the 8192^2 prefill weight
+    log("DYADIC5 1B stack batched GEMV")
+    gen = torch.Generator(device=dev).manual_seed(synthetic.seed(7, 0, 0))
+    probs, total = [], 0
+    for i, (n, k) in enumerate(synthetic.llama1b_stack_shapes()):
+        W = synthetic.student_t_bf16_device((n, k), 4, 0.02, synthetic.seed(2, i, 0), dev)
+        wd = torch.randint(3, 6, (n, k // 64), dtype=torch.uint8, device=dev, generator=gen)
+        P, M, S = w4.w4_quantize_dyadic5(W, wd)
+        del W, wd
+        x = synthetic.normal_bf16_device((1, k), 1.0, synthetic.seed(2, i, 1), dev)
+        probs.append({"packed": P, "codebook": M, "scales": S, "x": x,
+                      "y": torch.empty((1, n), device=dev)})
+        total += n * k // 2 + n * k // 8 + 2 * n * (k // 64) + 2 * k + 4 * n
+    batch = w4.w4_gemv_batched_plan(probs, w4.W4_DYADIC5)
+    ms = timed(lambda: batch(stream), stream, args.steps, args.warmup)
+    rows["dyadic5_gemv_m1_llama1b_stack_batched"] = {"ms": ms, "GB/s": total / (ms * 1e-3) / 1e9}
+    del probs, batch
+    W = synthetic.normal_bf16_device((8192, 8192), 0.02, synthetic.seed(5, 0, 0), dev)
+    wd = torch.randint(3, 6, (8192, 128), dtype=torch.uint8, device=dev, generator=gen)
+    P, M, S = w4.w4_quantize_dyadic5(W, wd)
+    ms = timed(lambda: w4.w4_quantize_dyadic5(W, wd, packed=P, msb=M, scales=S, stream=stream),
+               stream, 20, 3)
+    b = 2 * 8192 * 8192 + 8192 * 128 + 8192 * 4096 + 8192 * 1024 + 2 * 8192 * 128
+    rows["quantize_dyadic5_8192x8192"] = {"ms": ms, "GB/s": b / (ms * 1e-3) / 1e9}
+    del W, wd, P, M, S
+
     # SIGNMAG8: 224 x 2048^2, Student-t nu = 5; dense dequant + one batched m = 1 GEMV
     log("SIGNMAG8 2B stack")
     probs, total = [], 0

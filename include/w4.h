@@ -41,10 +41,19 @@
  *   scales   bf16  [n][k/64] DYADIC, LUT16, LUT16S;   NULL for SIGNMAG8
  *   codebook LUT16:    bf16 [n][k/64][16] normalised levels L_j;
  *            LUT16S:   bf16 [16] normalised levels L_j shared by every group;
+ *            DYADIC5:  uint8 [n][k/8] high-bit plane (passed as codebook):
+ *                      per run of 32 weights k = 32c .. 32c+31 a little-endian
+ *                      32-bit word M; the 5-bit index of weight 32c + i is
+ *                      nibble | (M >> bit(i) & 1) << 4 with, for d = i / 8 and
+ *                      e = i % 8, bit(i) = P[e] + A[2d + (e % 4 >= 2)],
+ *                      P = {4, 8, 4, 8, 20, 24, 20, 24},
+ *                      A = {-4, -3, -2, -1, 4, 5, 6, 7};
+ *                      the nibble plane holds the low 4 bits;
  *            SIGNMAG8: fp16 [n][k/32][8]  magnitudes M_j;    NULL for DYADIC
  * Reconstruction (w_hat, "dequantized weight"):
  *   DYADIC:   w_hat = RNE_bf16((s/8) * (nib - 8))    a zero result is +0.0
  *   LUT16, LUT16S: w_hat = RNE_bf16(s * L[nib])
+ *   DYADIC5:  w_hat = RNE_bf16((s/16) * (j5 - 16))  an exact zero is +0.0
  *   SIGNMAG8: w_hat = (nib & 8 ? -1 : +1) * M[nib & 7]    (fp16, exact)
  * (RNE = round to nearest, ties to even.)
  */
@@ -71,7 +80,17 @@ typedef enum {
  * and a bf16 scale per group of 64 -- 4.25 bits per weight plus 32 bytes, the
  * size [KM] sec. 2.1 states for its 3.9B model (about 2.1 GB).  The table is
  * an input; the oracle fits it by k-means over the whole weight. */
-typedef enum { W4_DYADIC = 0, W4_LUT16 = 1, W4_SIGNMAG8 = 2, W4_LUT16S = 3 } w4_codec;
+/* W4_DYADIC5: [DG] sec. 2.1's dyadic codes at b = 3, 4 and 5 bits in one
+ * 5-bit index space (the b-bit code j is the 5-bit code j * 2^(5-b)), so a
+ * group's width only restricts which codes it may take; see
+ * w4_quantize_dyadic5.  Reconstruction RNE_bf16((s/16) * (j5 - 16)). */
+typedef enum {
+  W4_DYADIC = 0,
+  W4_LUT16 = 1,
+  W4_SIGNMAG8 = 2,
+  W4_LUT16S = 3,
+  W4_DYADIC5 = 4
+} w4_codec;
 
 /* Largest k of a matrix product call: keeps every per-block byte offset of the
  * kernels within 32 bits. */
@@ -95,6 +114,8 @@ int32_t w4_group_size(int32_t codec);
  *   LUT16:    reads scales (bf16 [n][k/64]) and codebook (bf16 [n][k/64][16]);
  *             idx = the lowest j minimising |fl32(w - s*L_j)| (fp32 decision).
  *   LUT16S:   as LUT16 with the one table codebook (bf16 [16]) for every group.
+ *   DYADIC5:  not provided here (W4_EUNSUPPORTED): w4_quantize_dyadic5 writes
+ *             both of its index planes.
  *   SIGNMAG8: reads codebook (fp16 [n][k/32][8]); scales: NULL;
  *             nibble = (w < 0) << 3 | the lowest j minimising |fl32(|w| - M_j)|.
  * w: bf16 [n][k], 16-byte aligned.  packed: uint8 [n][k/2], 16-byte aligned.
@@ -115,6 +136,27 @@ w4_status w4_quantize_pack(int32_t codec, int64_t n, int64_t k, const uint16_t* 
 w4_status w4_unpack_dequant(int32_t codec, int64_t n, int64_t k, const uint8_t* packed,
                             const uint16_t* scales, const uint16_t* codebook, void* out,
                             void* stream);
+
+/*
+ * w4_quantize_dyadic5 -- quantize a bf16 weight [n][k] to W4_DYADIC5 with a
+ * width b in {3, 4, 5} bits per group of 64.  [DG] sec. 2.1 (codes
+ * (s/half)(j - half), half = 2^(b-1); the 3/4/5-bit codebooks share one index
+ * space), sec. 2.2 (scale = the group's absmax here, as for W4_DYADIC).
+ * For each group: s = max |w| (bf16, exact), written to scales; each weight
+ * takes the lowest j minimising |w - (s/half)(j - half)| over the group's
+ * 2^b exact codes and is stored as j5 = j * 2^(5-b); an all-zero group gets
+ * s = +0 and j5 = 16.  The widths choose the precision per group (the pages
+ * give no rule for choosing them); widths == NULL means 5 bits everywhere,
+ * and a width other than 3 or 4 means 5.
+ * w: bf16 [n][k], 16-byte aligned.  widths: uint8 [n][k/64] or NULL.
+ * packed: uint8 [n][k/2] (low 4 bits of j5), 16-byte aligned.  msb: uint8
+ * [n][k/8] high-bit plane (layout at the top of this header), 16-byte
+ * aligned.  scales: bf16 [n][k/64], 2-byte aligned.
+ * Errors: W4_EINVAL (negative size, null pointer), W4_ESHAPE (k % 64 != 0),
+ * W4_EALIGN.
+ */
+w4_status w4_quantize_dyadic5(int64_t n, int64_t k, const uint16_t* w, const uint8_t* widths,
+                              uint8_t* packed, uint8_t* msb, uint16_t* scales, void* stream);
 
 /*
  * w4_lut16_fit -- fit the LUT16 side tables of a bf16 weight [n][k]: per group

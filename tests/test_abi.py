@@ -27,6 +27,7 @@ def w4():
 def test_header_declares_the_calls():
     names = _declared()
     for n in ["w4_quantize_pack", "w4_unpack_dequant", "w4_gemv", "w4_gemm", "w4_lut16_fit",
+              "w4_quantize_dyadic5",
               "w4_gemv_batched_plan", "w4_gemv_batched", "w4_status_str", "w4_group_size"]:
         assert n in names
 
@@ -39,7 +40,7 @@ def test_library_exports_every_declared_symbol(w4):
 
 
 def test_group_sizes_and_status_strings(w4):
-    assert [w4.w4_group_size(c) for c in (0, 1, 2, 3, 7)] == [64, 64, 32, 64, -1]
+    assert [w4.w4_group_size(c) for c in (0, 1, 2, 3, 4, 7)] == [64, 64, 32, 64, 64, -1]
     for s in range(6):
         assert w4.w4_status_str(s).startswith("W4_")
 
@@ -52,7 +53,7 @@ def _gemv(w4, codec=0, n=16, k=64, packed=16, scales=16, cb=16, x=16, m=1, y=16,
 
 def test_validation_errors(w4):
     E = {"inval": 1, "shape": 2, "align": 3, "unsup": 4}
-    assert _gemv(w4, codec=4) == E["inval"]
+    assert _gemv(w4, codec=5) == E["inval"]
     assert _gemv(w4, n=-1) == E["inval"]
     assert _gemv(w4, k=96) == E["shape"]
     assert _gemv(w4, m=17) == E["shape"]
@@ -65,6 +66,9 @@ def test_validation_errors(w4):
     assert _gemv(w4, codec=3, cb=None) == E["inval"]
     assert _gemv(w4, codec=3, scales=None) == E["inval"]
     assert _gemv(w4, codec=3, cb=24) == E["align"]
+    assert _gemv(w4, codec=4, cb=None) == E["inval"]
+    assert _gemv(w4, codec=4, scales=None) == E["inval"]
+    assert _gemv(w4, codec=4, cb=24) == E["align"]
     assert _gemv(w4, codec=2, scales=None, cb=32 + 8) == E["align"]
     assert _gemv(w4, x=None) == E["inval"]
     assert _gemv(w4, x=24) == E["align"]
@@ -106,6 +110,20 @@ def test_lut16_fit_validation(w4):
     assert call(n=0, w=None, s=None, L=None) == 0
     assert call(k=0, w=None, s=None, L=None) == 0
     assert call(n=1 << 40, k=128) == 2
+
+
+def test_quantize_dyadic5_validation(w4):
+    f = w4._lib.w4_quantize_dyadic5
+    P = ctypes.c_void_p
+    ok = dict(n=4, k=64, w=P(16), wd=None, p=P(16), m=P(16), s=P(16))
+    call = lambda **kw: f(*[{**ok, **kw}[a] for a in ("n", "k", "w", "wd", "p", "m", "s")], None)
+    assert call(n=-1) == 1 and call(k=-64) == 1
+    assert call(k=96) == 2
+    assert call(w=None) == 1 and call(p=None) == 1 and call(m=None) == 1 and call(s=None) == 1
+    assert call(w=P(8)) == 3 and call(p=P(8)) == 3 and call(m=P(4)) == 3 and call(s=P(3)) == 3
+    assert call(n=0, w=None, p=None, m=None, s=None) == 0
+    # the generic quantize call does not write DYADIC5's second plane
+    assert w4._lib.w4_quantize_pack(4, 4, 64, P(16), P(16), P(16), P(16), None) == 4
 
 
 def test_batched_plan_validation(w4):

@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import synthetic
-from oracle import bits, dyadic, lut16, matmul, native, packing, signmag8
+from oracle import bits, dyadic, dyadic5, lut16, matmul, native, packing, signmag8
 from tests.gpu_util import dev_bf16, dev_f16, dev_u8, host_bits, host_f32, host_u8, report
 
 pytestmark = pytest.mark.gpu
@@ -298,6 +298,66 @@ def test_lut16s_matmul(w4, m):
     _gemv_check(yb, x, w_hat, True)
 
 
+# ------------------------------------------------------------------ DYADIC5
+def _d5_case(n, k, seed, huge=False):
+    """Edge-case weight, random group widths (3, 4, 5 and two values that
+    mean 5), the oracle's 5-bit indices, scales and both planes."""
+    w = _edge_weight(n, k, seed, huge=huge)
+    widths = np.random.default_rng(seed).choice([3, 4, 5, 0, 9], size=(n, k // 64)).astype(np.uint8)
+    idx, s = dyadic5.quantize(w, widths)
+    nib, msb = dyadic5.planes(idx)
+    return w, widths, idx, s, nib, msb
+
+
+@pytest.mark.parametrize("n,k", [(300, 1024), (37, 320), (6, 128)])
+def test_dyadic5_quantize_dequant_bitexact(w4, n, k):
+    """Per-group widths and widths = None (5 bits everywhere): scales, nibble
+    plane and high-bit plane bit for bit; dequant of the oracle's planes."""
+    report("dyadic5_quant", n=n, k=k)
+    w, widths, idx, s, nib, msb = _d5_case(n, k, 1500 + n)
+    for wd, want_idx in ((widths, idx), (None, dyadic5.indices(w, s))):
+        p, m, sd = w4.w4_quantize_dyadic5(dev_bf16(w), None if wd is None else dev_u8(wd))
+        torch.cuda.synchronize()
+        want_nib, want_msb = dyadic5.planes(want_idx)
+        assert np.array_equal(host_bits(sd), s)
+        assert np.array_equal(host_u8(p), want_nib)
+        assert np.array_equal(host_u8(m), want_msb)
+    d = w4.w4_unpack_dequant(dev_u8(nib), w4.W4_DYADIC5, scales=dev_bf16(s), codebook=dev_u8(msb))
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(d), dyadic5.dequant_from_indices(idx, s))
+
+
+def test_dyadic5_dequant_exhaustive_scales(w4):
+    """Every finite bf16 scale of either sign (zero included) x every 5-bit index."""
+    allb = bits.all_finite_bf16()
+    n = len(allb)
+    idx = np.tile(np.arange(32, dtype=np.uint8), (n, 2))
+    report("dyadic5_dequant_exhaustive", n=n)
+    nib, msb = dyadic5.planes(idx)
+    out = w4.w4_unpack_dequant(dev_u8(nib), w4.W4_DYADIC5, scales=dev_bf16(allb[:, None]),
+                               codebook=dev_u8(msb))
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(out), dyadic5.dequant_from_indices(idx, allb[:, None]))
+
+
+@pytest.mark.parametrize("m", [1, 4, 16, 130])
+def test_dyadic5_matmul(w4, m):
+    """GEMV (m <= 16: single call, k split for m > 1) or GEMM (m = 130), fp32
+    and bf16 outputs, against the fp64 oracle on the same 5-bit weights."""
+    n, k = 300, 1024
+    report("dyadic5_matmul", n=n, k=k, m=m)
+    w, widths, idx, s, nib, msb = _d5_case(n, k, 1600 + m)
+    w_hat = bits.bf16_to_f64(dyadic5.dequant_from_indices(idx, s))
+    x = synthetic.normal_bf16((m, k), 1.0, 1601 + m)
+    args = dict(scales=dev_bf16(s), codebook=dev_u8(msb))
+    fn = w4.w4_gemv if m <= 16 else w4.w4_gemm
+    y = fn(dev_u8(nib), dev_bf16(x), w4.W4_DYADIC5, **args)
+    yb = fn(dev_u8(nib), dev_bf16(x), w4.W4_DYADIC5, y_dtype=torch.bfloat16, **args)
+    torch.cuda.synchronize()
+    _gemv_check(y, x, w_hat, False)
+    _gemv_check(yb, x, w_hat, True)
+
+
 # ------------------------------------------------------------------ SIGNMAG8
 def _sm_case(n, k, seed):
     w = synthetic.student_t_bf16((n, k), 5, 0.02, seed)
@@ -350,6 +410,10 @@ def _batched_case(codec, n, k, seed):
         idx = native.lut16_indices(w, s, L)
         w_hat = bits.bf16_to_f64(lut16.dequant_from_indices(idx, s, L))
         return packing.pack(idx), dict(scales=dev_bf16(s), codebook=dev_bf16(L)), w_hat
+    if codec == 4:
+        w, widths, idx, s, nib, msb = _d5_case(n, k, seed)
+        w_hat = bits.bf16_to_f64(dyadic5.dequant_from_indices(idx, s))
+        return nib, dict(scales=dev_bf16(s), codebook=dev_u8(msb)), w_hat
     if codec == 3:
         w, s, T, tables, idx = _lut16s_case(n, k, seed)
         w_hat = bits.bf16_to_f64(lut16.dequant_from_indices(idx, s, tables))
@@ -367,6 +431,8 @@ def _batched_case(codec, n, k, seed):
     (2, 3, [(300, 1024), (65, 2048)]),
     (3, 1, [(300, 1024), (129, 2048), (64, 64)]),
     (3, 16, [(300, 1024), (70, 832)]),
+    (4, 1, [(2048, 2048), (300, 1024), (70, 832)]),
+    (4, 8, [(300, 1024), (129, 2048)]),
 ])
 def test_gemv_batched_codecs(w4, codec, m, shapes):
     report("gemv_batched_codecs", codec=codec, m=m, count=len(shapes))

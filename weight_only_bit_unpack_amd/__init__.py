@@ -17,9 +17,9 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libw4.so")
 
-W4_DYADIC, W4_LUT16, W4_SIGNMAG8, W4_LUT16S = 0, 1, 2, 3
+W4_DYADIC, W4_LUT16, W4_SIGNMAG8, W4_LUT16S, W4_DYADIC5 = 0, 1, 2, 3, 4
 W4_F32, W4_BF16, W4_F16 = 0, 1, 2
-GROUP = {W4_DYADIC: 64, W4_LUT16: 64, W4_SIGNMAG8: 32, W4_LUT16S: 64}
+GROUP = {W4_DYADIC: 64, W4_LUT16: 64, W4_SIGNMAG8: 32, W4_LUT16S: 64, W4_DYADIC5: 64}
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -47,6 +47,7 @@ _SIGS = {
     "w4_quantize_pack": ([_I32, _I64, _I64, _P, _P, _P, _P, _P], _I32),
     "w4_unpack_dequant": ([_I32, _I64, _I64, _P, _P, _P, _P, _P], _I32),
     "w4_lut16_fit": ([_I64, _I64, _P, _P, _P, _I32, _P], _I32),
+    "w4_quantize_dyadic5": ([_I64, _I64, _P, _P, _P, _P, _P, _P], _I32),
     "w4_gemv": ([_I32, _I64, _I64, _P, _P, _P, _P, _I32, _P, _I32, _P], _I32),
     "w4_gemm": ([_I32, _I64, _I64, _P, _P, _P, _P, _I32, _P, _I32, _P], _I32),
     "w4_gemv_batched_plan": ([_I32, _I32, _I32, ctypes.POINTER(W4Problem), _I32,
@@ -109,8 +110,10 @@ def _need(t, name, dtypes, shape=None):
 
 def _side_tables(codec, n, k, scales, codebook):
     g = GROUP[codec]
-    if codec in (W4_DYADIC, W4_LUT16, W4_LUT16S):
+    if codec in (W4_DYADIC, W4_LUT16, W4_LUT16S, W4_DYADIC5):
         _need(scales, "scales", _U16, (n, k // 64))
+    if codec == W4_DYADIC5:
+        _need(codebook, "codebook (high-bit plane)", (torch.uint8,), (n, k // 8))
     if codec == W4_LUT16:
         _need(codebook, "codebook", _U16, (n, k // 64, 16))
     if codec == W4_LUT16S:
@@ -152,6 +155,29 @@ def w4_unpack_dequant(packed, codec=W4_DYADIC, *, scales=None, codebook=None, ou
     _check(_lib.w4_unpack_dequant(codec, n, k, _ptr(packed), _ptr(scales), _ptr(codebook),
                                   _ptr(out), _stream(stream)))
     return out
+
+
+def w4_quantize_dyadic5(w, widths=None, *, packed=None, msb=None, scales=None, stream=None):
+    """Quantize a bf16 weight [n, k] to W4_DYADIC5 with a width of 3, 4 or 5
+    bits per group of 64 (``widths`` uint8 [n, k/64]; None: 5 everywhere).
+    Returns (packed [n, k/2], msb [n, k/8], scales [n, k/64]); the matrix calls
+    take the high-bit plane ``msb`` as their ``codebook``."""
+    _need(w, "w", _U16)
+    n, k = w.shape
+    if widths is not None:
+        _need(widths, "widths", (torch.uint8,), (n, k // 64))
+    if packed is None:
+        packed = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
+    if msb is None:
+        msb = torch.empty((n, k // 8), dtype=torch.uint8, device=w.device)
+    if scales is None:
+        scales = torch.empty((n, k // 64), dtype=torch.bfloat16, device=w.device)
+    _need(packed, "packed", (torch.uint8,), (n, k // 2))
+    _need(msb, "msb", (torch.uint8,), (n, k // 8))
+    _need(scales, "scales", _U16, (n, k // 64))
+    _check(_lib.w4_quantize_dyadic5(n, k, _ptr(w), _ptr(widths), _ptr(packed), _ptr(msb),
+                                    _ptr(scales), _stream(stream)))
+    return packed, msb, scales
 
 
 def w4_lut16_fit(w, iters=25, *, scales=None, codebook=None, stream=None):

@@ -15,7 +15,8 @@ namespace {
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 bool valid_codec(int32_t c) {
-  return c == W4_DYADIC || c == W4_LUT16 || c == W4_SIGNMAG8 || c == W4_LUT16S;
+  return c == W4_DYADIC || c == W4_LUT16 || c == W4_SIGNMAG8 || c == W4_LUT16S ||
+         c == W4_DYADIC5;
 }
 
 // Checks the quantized-weight triple of a codec for an [n][k] weight.
@@ -27,11 +28,11 @@ w4_status check_weight(int32_t codec, int64_t n, int64_t k, const void* packed, 
   if (n == 0 || k == 0) return W4_OK;
   if (!packed) return W4_EINVAL;
   if (!aligned(packed, 16)) return W4_EALIGN;
-  if (codec == W4_DYADIC || codec == W4_LUT16 || codec == W4_LUT16S) {
+  if (codec == W4_DYADIC || codec == W4_LUT16 || codec == W4_LUT16S || codec == W4_DYADIC5) {
     if (!scales) return W4_EINVAL;
     if (!aligned(scales, 2)) return W4_EALIGN;
   }
-  if (codec == W4_LUT16 || codec == W4_SIGNMAG8 || codec == W4_LUT16S) {
+  if (codec == W4_LUT16 || codec == W4_SIGNMAG8 || codec == W4_LUT16S || codec == W4_DYADIC5) {
     if (!codebook) return W4_EINVAL;
     if (!aligned(codebook, 16)) return W4_EALIGN;
   }
@@ -99,6 +100,7 @@ int32_t w4_group_size(int32_t codec) {
     case W4_DYADIC: return 64;
     case W4_LUT16: return 64;
     case W4_LUT16S: return 64;
+    case W4_DYADIC5: return 64;
     case W4_SIGNMAG8: return 32;
     default: return -1;
   }
@@ -109,6 +111,7 @@ w4_status w4_quantize_pack(int32_t codec, int64_t n, int64_t k, const uint16_t* 
                            void* stream) {
   w4_status st = check_weight(codec, n, k, packed, scales, codebook);
   if (st != W4_OK) return st;
+  if (codec == W4_DYADIC5) return W4_EUNSUPPORTED;
   if (n == 0 || k == 0) return W4_OK;
   if (!w) return W4_EINVAL;
   if (!aligned(w, 16)) return W4_EALIGN;
@@ -126,6 +129,18 @@ w4_status w4_unpack_dequant(int32_t codec, int64_t n, int64_t k, const uint8_t* 
   if (!aligned(out, 16)) return W4_EALIGN;
   return launched(w4::launch_dequant(codec, n, k, packed, scales, codebook, out,
                                      static_cast<hipStream_t>(stream)));
+}
+
+w4_status w4_quantize_dyadic5(int64_t n, int64_t k, const uint16_t* w, const uint8_t* widths,
+                              uint8_t* packed, uint8_t* msb, uint16_t* scales, void* stream) {
+  if (n < 0 || k < 0) return W4_EINVAL;
+  if (k % 64 != 0) return W4_ESHAPE;
+  if (n == 0 || k == 0) return W4_OK;
+  if (!w || !packed || !msb || !scales) return W4_EINVAL;
+  if (!aligned(w, 16) || !aligned(packed, 16) || !aligned(msb, 16) || !aligned(scales, 2))
+    return W4_EALIGN;
+  return launched(w4::launch_quantize_dyadic5(n, k, w, widths, packed, msb, scales,
+                                              static_cast<hipStream_t>(stream)));
 }
 
 w4_status w4_lut16_fit(int64_t n, int64_t k, const uint16_t* w, uint16_t* scales,

@@ -93,6 +93,37 @@ __global__ __launch_bounds__(256) void dequant_signmag8_kernel(const u32x4* __re
   }
 }
 
+// +0.0f the optimiser cannot see through (keeps the fma form of the rebuild)
+__device__ __forceinline__ float opaque_pz() {
+  uint32_t v = 0u;
+  asm volatile("" : "+v"(v));
+  return __builtin_bit_cast(float, v);
+}
+
+// DYADIC5: one thread per run of 32 weights: 16 packed bytes, the run's
+// high-bit word and the group scale -> four 16-byte stores.
+__global__ __launch_bounds__(256) void dequant_dyadic5_kernel(const u32x4* __restrict__ packed,
+                                                              const uint32_t* __restrict__ msb,
+                                                              const uint16_t* __restrict__ scales,
+                                                              u32x4* __restrict__ out,
+                                                              int64_t nruns) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= nruns) return;
+  const u32x4 p = __builtin_nontemporal_load(&packed[c]);
+  const uint32_t M = msb[c];
+  const Dyadic5Scale d = dyadic5_scale(scales[c >> 1]);
+  const float pz = opaque_pz();
+  uint32_t e0, e1;
+  dyadic5_msb<0>(M, e0, e1);
+  __builtin_nontemporal_store(sigma_to_natural(dyadic5_rebuild(p.x, e0, e1, d, pz)), &out[4 * c]);
+  dyadic5_msb<1>(M, e0, e1);
+  __builtin_nontemporal_store(sigma_to_natural(dyadic5_rebuild(p.y, e0, e1, d, pz)), &out[4 * c + 1]);
+  dyadic5_msb<2>(M, e0, e1);
+  __builtin_nontemporal_store(sigma_to_natural(dyadic5_rebuild(p.z, e0, e1, d, pz)), &out[4 * c + 2]);
+  dyadic5_msb<3>(M, e0, e1);
+  __builtin_nontemporal_store(sigma_to_natural(dyadic5_rebuild(p.w, e0, e1, d, pz)), &out[4 * c + 3]);
+}
+
 }  // namespace
 
 hipError_t launch_dequant(int codec, int64_t n, int64_t k, const uint8_t* packed,
@@ -107,6 +138,9 @@ hipError_t launch_dequant(int codec, int64_t n, int64_t k, const uint8_t* packed
   else if (codec == 1 || codec == 3)
     dequant_lut16_kernel<<<dim3((uint32_t)blocks), dim3(256), 0, stream>>>(
         pk, scales, reinterpret_cast<const u32x4*>(codebook), o, nchunks, codec == 3);
+  else if (codec == 4)
+    dequant_dyadic5_kernel<<<dim3((uint32_t)blocks), dim3(256), 0, stream>>>(
+        pk, reinterpret_cast<const uint32_t*>(codebook), scales, o, nchunks);  // chunk = run of 32
   else
     dequant_signmag8_kernel<<<dim3((uint32_t)blocks), dim3(256), 0, stream>>>(
         pk, reinterpret_cast<const u32x4*>(codebook), o, nchunks);

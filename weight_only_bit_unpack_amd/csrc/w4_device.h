@@ -164,6 +164,62 @@ __device__ __forceinline__ uint32_t merge_sel(uint32_t x_shifted_by_1) {
   return and_or(x_shifted_by_1, 0x04040404u, 0x03020100u);
 }
 
+// ---------------------------------------------------------------- DYADIC5
+// w_hat = RNE_bf16((s/16) * (j - 16)), j = nibble | high bit << 4.
+// The high bit becomes one more mantissa bit of the fp16 magic number:
+//   nibble in bits 0-3, high bit in bit 4:  h = 1024 + j,       (h - 1040) * s/16
+//   nibble in bits 4-7, high bit in bit 8:  h = 1024 + 16 j,    (h - 1280) * s/256
+// h - 1040 and h - 1280 are exact small integers (times 16) in fp16, the
+// products are exact in fp32 for every bf16 scale, and the conversion is the
+// one RNE.  The addend pz is +0.0f hidden from the optimiser: an exact zero
+// product then comes out +0 even for a zero scale.
+struct Dyadic5Scale {
+  float s16, s256;
+};
+
+__device__ __forceinline__ Dyadic5Scale dyadic5_scale(uint32_t sbits) {
+  Dyadic5Scale d;
+  d.s16 = bf16_bits_to_f32(sbits) * 0.0625f;
+  d.s256 = d.s16 * 0.0625f;
+  return d;
+}
+
+// High bits of packed dword D (0..3) of a run of 32 weights, from the run's
+// word M: the first two value pairs take M shifted by A[2D], the last two by
+// A[2D + 1], A = {-4, -3, -2, -1, 4, 5, 6, 7} (negative: left shift); the
+// pairs' high bits then sit at bits (4, 20) and (8, 24).
+template <int D>
+__device__ __forceinline__ void dyadic5_msb(uint32_t M, uint32_t& e0, uint32_t& e1) {
+  if constexpr (D == 0) {
+    e0 = M << 4;
+    e1 = M << 3;
+  } else if constexpr (D == 1) {
+    e0 = M << 2;
+    e1 = M << 1;
+  } else if constexpr (D == 2) {
+    e0 = M >> 4;
+    e1 = M >> 5;
+  } else {
+    e0 = M >> 6;
+    e1 = M >> 7;
+  }
+}
+
+// One packed dword + its high bits -> 8 bf16 values in SIGMA order.
+__device__ __forceinline__ u32x4 dyadic5_rebuild(uint32_t p, uint32_t e0, uint32_t e1,
+                                                 const Dyadic5Scale& d, float pz) {
+  const uint32_t q = p >> 8;
+  const uint32_t mg = kMagic;
+  const uint32_t o1 = 0x64106410u;  // fp16 1040 twice
+  const uint32_t o2 = 0x65006500u;  // fp16 1280 twice
+  u32x4 r;
+  r.x = sub_mul_pair(and_or(p, 0x000F000Fu, and_or(e0, 0x00100010u, mg)), o1, d.s16, pz);
+  r.y = sub_mul_pair(and_or(p, 0x00F000F0u, and_or(e0, 0x01000100u, mg)), o2, d.s256, pz);
+  r.z = sub_mul_pair(and_or(q, 0x000F000Fu, and_or(e1, 0x00100010u, mg)), o1, d.s16, pz);
+  r.w = sub_mul_pair(and_or(q, 0x00F000F0u, and_or(e1, 0x01000100u, mg)), o2, d.s256, pz);
+  return r;
+}
+
 // ---------------------------------------------------------------- LUT16
 // Per-group table T[j] = RNE_bf16(s * L_j), split into a low-byte plane and a
 // high-byte plane of 4 dwords each.

@@ -55,9 +55,12 @@ __device__ __forceinline__ uint32_t opaque(uint32_t v) {
   return v;
 }
 
-// The one 16-level table of a LUT16S weight, loaded once per thread.
-struct SharedTable {
+// Per-thread constants of the rebuild: the one 16-level table of a LUT16S
+// weight; for DYADIC5, the shift that brings the thread's half of a run's
+// high-bit word to the position its first packed dword expects.
+struct RebuildConsts {
   u32x4 l0, l1;
+  uint32_t msb_shift;
 };
 
 // Packed bytes and side data one thread rebuilds per k-step: weight row
@@ -79,7 +82,7 @@ struct WRaw<0> {  // DYADIC: bf16 scale of the row's 64-group
     sb = __builtin_amdgcn_raw_buffer_load_b16(s0, so, 0, 0);
   }
   template <int D>
-  __device__ __forceinline__ void rebuild(u32x4& hi, u32x4&, const SharedTable&) const {
+  __device__ __forceinline__ void rebuild(u32x4& hi, u32x4&, const RebuildConsts&) const {
     const DyadicScale d = dyadic_scale(sb);
     const uint32_t m0 = 0x000F000Fu, m1 = 0x00F000F0u, mg = kMagic;
     const float nz = __builtin_bit_cast(float, opaque(0x80000000u));
@@ -103,7 +106,7 @@ struct WRaw<1> {  // LUT16: 16 bf16 levels + bf16 scale of the row's 64-group
     sb = __builtin_amdgcn_raw_buffer_load_b16(s0, so, 0, 0);
   }
   template <int D>
-  __device__ __forceinline__ void rebuild(u32x4& hi, u32x4&, const SharedTable&) const {
+  __device__ __forceinline__ void rebuild(u32x4& hi, u32x4&, const RebuildConsts&) const {
     const Lut16Table t = lut16_table(sb, l0, l1);
     hi = sigma_to_natural(lut16_rebuild(D == 0 ? p0 : p1, t));
   }
@@ -122,7 +125,7 @@ struct WRaw<2> {  // SIGNMAG8: 8 fp16 magnitudes of the row's 32-group
     c = __builtin_amdgcn_raw_buffer_load_b128(s1, co, 0, 0);
   }
   template <int D>
-  __device__ __forceinline__ void rebuild(u32x4& hi, u32x4& lo, const SharedTable&) const {
+  __device__ __forceinline__ void rebuild(u32x4& hi, u32x4& lo, const RebuildConsts&) const {
     const SignMagTable t = signmag_table(c);
     u32x4 h, l;
     signmag_rebuild(D == 0 ? p0 : p1, t, h, l);
@@ -144,9 +147,33 @@ struct WRaw<3> {  // LUT16S: bf16 scale of the row's 64-group; levels shared
     sb = __builtin_amdgcn_raw_buffer_load_b16(s0, so, 0, 0);
   }
   template <int D>
-  __device__ __forceinline__ void rebuild(u32x4& hi, u32x4&, const SharedTable& st) const {
+  __device__ __forceinline__ void rebuild(u32x4& hi, u32x4&, const RebuildConsts& st) const {
     const Lut16Table t = lut16_table(sb, st.l0, st.l1);
     hi = sigma_to_natural(lut16_rebuild(D == 0 ? p0 : p1, t));
+  }
+};
+
+template <>
+struct WRaw<4> {  // DYADIC5: bf16 scale of the row's 64-group + high-bit word of its run of 32
+  uint32_t p0, p1, h;
+  uint16_t sb;
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t pk, __amdgpu_buffer_rsrc_t s0,
+                                       __amdgpu_buffer_rsrc_t s1, uint32_t po, uint32_t so,
+                                       uint32_t co) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(pk, po, 0, 0);
+    p0 = v[0];
+    p1 = v[1];
+    sb = __builtin_amdgcn_raw_buffer_load_b16(s0, so, 0, 0);
+    h = __builtin_amdgcn_raw_buffer_load_b32(s1, co, 0, 0);
+  }
+  // dword D of the thread's 16 weights is dword 2 (wq % 2) + D of the run;
+  // msb_shift (0 or 8) folds the 2 (wq % 2) into the shifts of dwords 0, 1
+  template <int D>
+  __device__ __forceinline__ void rebuild(u32x4& hi, u32x4&, const RebuildConsts& c) const {
+    uint32_t e0, e1;
+    dyadic5_msb<D>(h >> c.msb_shift, e0, e1);
+    const float pz = __builtin_bit_cast(float, opaque(0u));
+    hi = sigma_to_natural(dyadic5_rebuild(D == 0 ? p0 : p1, e0, e1, dyadic5_scale(sb), pz));
   }
 };
 
@@ -197,6 +224,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __amdgpu_buffer_rsrc_t s0 = pk, s1 = pk;
   if constexpr (CODEC == 0 || CODEC == 3) {
     s0 = rsrc(P.scales + n0 * (K >> 6), (uint32_t)(rows_n * (K >> 6) * 2));
+  } else if constexpr (CODEC == 4) {
+    s0 = rsrc(P.scales + n0 * (K >> 6), (uint32_t)(rows_n * (K >> 6) * 2));
+    s1 = rsrc(reinterpret_cast<const uint8_t*>(P.codebook) + n0 * (K >> 3),
+              (uint32_t)(rows_n * (K >> 3)));
   } else if constexpr (CODEC == 1) {
     s0 = rsrc(P.scales + n0 * (K >> 6), (uint32_t)(rows_n * (K >> 6) * 2));
     s1 = rsrc(P.codebook + n0 * (K >> 6) * 16, (uint32_t)(rows_n * (K >> 6) * 32));
@@ -206,6 +237,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const uint32_t p_lane = (uint32_t)wr * row_bytes + 8u * (uint32_t)wq;
   const uint32_t g64_lane = (uint32_t)wr * (uint32_t)(K >> 6);
   const uint32_t g32_lane = (uint32_t)wr * (uint32_t)(K >> 5) + (uint32_t)(wq >> 1);
+  // DYADIC5: byte offset of the high-bit word of the thread's run of 32
+  const uint32_t h_lane = (uint32_t)wr * (uint32_t)(K >> 3) + 4u * (uint32_t)(wq >> 1);
 
   // activation role: the block's 8 row tiles of 32 in the packed layout
   // (pack_activations); wave (mw, kh) takes row tiles 2 mw + i and, within a
@@ -225,7 +258,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const bool in = u < nsteps;
     const uint32_t ks = (uint32_t)(ks0 + u);
     // byte offsets: packed, 64-group scale, codebook (LUT16 levels / SIGNMAG8 magnitudes)
-    const uint32_t co = CODEC == 1 ? 32u * (g64_lane + ks) : 16u * (g32_lane + 2u * ks);
+    const uint32_t co = CODEC == 1   ? 32u * (g64_lane + ks)
+                        : CODEC == 4 ? h_lane + 8u * ks
+                                     : 16u * (g32_lane + 2u * ks);
     r.load(pk, s0, s1, opaque(in ? p_lane + ks * 32u : kOOB),
            opaque(in ? 2u * (g64_lane + ks) : kOOB), opaque(in ? co : kOOB));
   };
@@ -239,7 +274,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         xv[i][kk] = __builtin_amdgcn_raw_buffer_load_b128(
             xr, base + (uint32_t)i * x_i + (uint32_t)kk * 1024u, 0, 0);
   };
-  SharedTable st{};
+  RebuildConsts st{};
+  st.msb_shift = 8u * (uint32_t)(wq & 1);
   if constexpr (CODEC == 3) {
     st.l0 = reinterpret_cast<const u32x4*>(P.codebook)[0];
     st.l1 = reinterpret_cast<const u32x4*>(P.codebook)[1];
@@ -510,6 +546,8 @@ hipError_t launch_gemm(int codec, const GemvProblem& p, int m, int y_bf16, hipSt
     e = launch_codec<1>(p, m, y_bf16, xpk, partial, blocks, stream);
   else if (codec == 3)
     e = launch_codec<3>(p, m, y_bf16, xpk, partial, blocks, stream);
+  else if (codec == 4)
+    e = launch_codec<4>(p, m, y_bf16, xpk, partial, blocks, stream);
   else
     e = launch_codec<2>(p, m, y_bf16, xpk, partial, blocks, stream);
   if (e != hipSuccess || S == 1) return e;

@@ -199,6 +199,46 @@ struct Raw<3> {  // LUT16S: one bf16 scale per 64-group (side); levels shared
   }
 };
 
+template <>
+struct Raw<4> {  // DYADIC5: bf16 scale per 64-group (side) + high-bit words (side2)
+  static constexpr uint32_t kSideStep = 8;  // 4 groups x 2 bytes per 256-k step
+  u32x4 a0, a1;
+  uint32_t h0, h1;  // high-bit words of the lane's two runs of 32 weights
+  uint16_t sb;
+  __device__ __forceinline__ void fetch(const Slice& S, const LaneBase& L, uint32_t sp,
+                                        uint32_t ss) {
+    a0 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, L.pa + sp, 0, 0);
+    a1 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, L.pb + sp, 0, 0);
+    sb = __builtin_amdgcn_raw_buffer_load_b16(S.side, L.s + ss, 0, 0);
+    // 8 high-bit bytes per lane per step: offset step = 4 x the scale step
+    const auto h = __builtin_amdgcn_raw_buffer_load_b64(S.side2, L.s2 + (ss == kOOB ? kOOB : 4 * ss),
+                                                        0, 0);
+    h0 = h[0];
+    h1 = h[1];
+  }
+  template <typename F>
+  __device__ __forceinline__ void apply(const Shuffle& sh, const SharedTable&, F&& mma) const {
+    u32x4 p0, p1;
+    sh(a0, a1, p0, p1);
+    const uint32_t pw[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+    const Dyadic5Scale d = dyadic5_scale(sb);
+    const float pz = __builtin_bit_cast(float, opaque(0u));
+    uint32_t e0, e1;
+#define W4_DYADIC5_STEP(J)                                         \
+  dyadic5_msb<(J) & 3>((J) < 4 ? h0 : h1, e0, e1);                 \
+  mma(J, dyadic5_rebuild(pw[J], e0, e1, d, pz));
+    W4_DYADIC5_STEP(0)
+    W4_DYADIC5_STEP(1)
+    W4_DYADIC5_STEP(2)
+    W4_DYADIC5_STEP(3)
+    W4_DYADIC5_STEP(4)
+    W4_DYADIC5_STEP(5)
+    W4_DYADIC5_STEP(6)
+    W4_DYADIC5_STEP(7)
+#undef W4_DYADIC5_STEP
+  }
+};
+
 // k-chunk length staged in LDS for a given m and LDS capacity (16-byte units):
 // rows of kc/8 units plus one pad unit each.
 __host__ __device__ __forceinline__ int64_t gemv_chunk(int m, int xs_units, int64_t K) {
@@ -288,6 +328,10 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvProblem single, const Gem
   S.packed = rsrc(P.packed + row0 * (K >> 1), (uint32_t)rows_here * row_bytes);
   if constexpr (CODEC == 0 || CODEC == 3) {
     S.side = rsrc(P.scales + row0 * (K >> 6), (uint32_t)rows_here * g64 * 2);
+  } else if constexpr (CODEC == 4) {
+    S.side = rsrc(P.scales + row0 * (K >> 6), (uint32_t)rows_here * g64 * 2);
+    S.side2 = rsrc(reinterpret_cast<const uint8_t*>(P.codebook) + row0 * (K >> 3),
+                   (uint32_t)rows_here * (uint32_t)(K >> 3));
   } else if constexpr (CODEC == 1) {
     S.side = rsrc(P.codebook + row0 * (K >> 6) * 16, (uint32_t)rows_here * g64 * 32);
     S.side2 = rsrc(P.scales + row0 * (K >> 6), (uint32_t)rows_here * g64 * 2);
@@ -318,8 +362,9 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvProblem single, const Gem
       const uint32_t g0 = rloc * g64 + (uint32_t)((k0 >> 6) + q);  // lane's first 64-group
       L.pa = rowA * row_bytes + (uint32_t)(k0 >> 1) + chA;
       L.pb = (rowA + 8) * row_bytes + (uint32_t)(k0 >> 1) + chB;
-      L.s = (CODEC == 0 || CODEC == 3) ? g0 * 2 : g0 * 32;
-      L.s2 = g0 * 2;
+      L.s = (CODEC == 0 || CODEC == 3 || CODEC == 4) ? g0 * 2 : g0 * 32;
+      L.s2 = CODEC == 4 ? rloc * (uint32_t)(K >> 3) + (uint32_t)(k0 >> 3) + 8u * (uint32_t)q
+                        : g0 * 2;
     }
     auto fetch = [&](Raw<CODEC>& r, int i) {
       const bool in = i < nw;
@@ -537,6 +582,7 @@ hipError_t launch_gemv(int codec, const GemvProblem& p, int m, int y_bf16, hipSt
   if (codec == 0) return launch_codec<0>(p, m, y_bf16, stream);
   if (codec == 1) return launch_codec<1>(p, m, y_bf16, stream);
   if (codec == 3) return launch_codec<3>(p, m, y_bf16, stream);
+  if (codec == 4) return launch_codec<4>(p, m, y_bf16, stream);
   return launch_codec<2>(p, m, y_bf16, stream);
 }
 
@@ -565,6 +611,7 @@ hipError_t launch_gemv_batched(int codec, const GemvProblem* probs_dev, int coun
   if (codec == 0) return launch_batched_codec<0>(probs_dev, count, total_tiles, xu, m, y_bf16, stream);
   if (codec == 1) return launch_batched_codec<1>(probs_dev, count, total_tiles, xu, m, y_bf16, stream);
   if (codec == 3) return launch_batched_codec<3>(probs_dev, count, total_tiles, xu, m, y_bf16, stream);
+  if (codec == 4) return launch_batched_codec<4>(probs_dev, count, total_tiles, xu, m, y_bf16, stream);
   return launch_batched_codec<2>(probs_dev, count, total_tiles, xu, m, y_bf16, stream);
 }
 

@@ -23,6 +23,10 @@ struct GemvProblem {
 hipError_t launch_quantize(int codec, int64_t n, int64_t k, const uint16_t* w, uint8_t* packed,
                            uint16_t* scales, const uint16_t* codebook, hipStream_t stream);
 
+hipError_t launch_quantize_dyadic5(int64_t n, int64_t k, const uint16_t* w, const uint8_t* widths,
+                                   uint8_t* packed, uint8_t* msb, uint16_t* scales,
+                                   hipStream_t stream);
+
 hipError_t launch_dequant(int codec, int64_t n, int64_t k, const uint8_t* packed,
                           const uint16_t* scales, const uint16_t* codebook, void* out,
                           hipStream_t stream);

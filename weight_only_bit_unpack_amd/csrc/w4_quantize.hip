@@ -179,7 +179,80 @@ __global__ __launch_bounds__(256) void quantize_signmag8_kernel(const u32x4* __r
   packed[c] = word;
 }
 
+// Bit of a run's 32-bit high-bit word that holds weight i (0..31) of the run
+// (the layout w4_device.h's dyadic5_msb reads).
+__device__ __forceinline__ constexpr int dyadic5_msb_bit(int i) {
+  constexpr int P[8] = {4, 8, 4, 8, 20, 24, 20, 24};
+  constexpr int A[8] = {-4, -3, -2, -1, 4, 5, 6, 7};
+  return P[i % 8] + A[2 * (i / 8) + ((i % 8) % 4 >= 2 ? 1 : 0)];
+}
+
+// DYADIC5: one thread per run of 32 weights (two threads per 64-group).
+// Group width b in {3, 4, 5}, half = 2^(b-1): the b-bit index is the number
+// of midpoints m_t = (2t + 1 - 2 half) * s / (2 half), t = 0 .. 2 half - 2,
+// below w (strictly: a weight on a midpoint takes the lower code), found by a
+// binary search; every m_t is exact in fp32 (an odd integer below 64 times a
+// power-of-two fraction of a bf16 scale).  Stored as j5 = index << (5 - b).
+__global__ __launch_bounds__(256) void quantize_dyadic5_kernel(const u32x4* __restrict__ w,
+                                                               const uint8_t* __restrict__ widths,
+                                                               u32x4* __restrict__ packed,
+                                                               uint32_t* __restrict__ msb,
+                                                               uint16_t* __restrict__ scales,
+                                                               int64_t nruns) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const bool live = c < nruns;
+  float f[32];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (live) v = __builtin_nontemporal_load(&w[4 * c + i]);
+    unpack8(v, &f[8 * i]);
+  }
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) a = __builtin_fmaxf(a, __builtin_fabsf(f[i]));
+  a = __builtin_fmaxf(a, __shfl_xor(a, 1));  // the other half of the 64-group
+  const int64_t g = c >> 1;
+  int b = 5;
+  if (live && widths) {
+    const int wb = widths[g];
+    b = (wb == 3 || wb == 4) ? wb : 5;
+  }
+  const int half = 1 << (b - 1), top = 2 * half - 1;  // top = number of midpoints
+  const float step2 = a * (0.5f / (float)half);        // s / (2 half), exact
+  uint32_t words[4] = {0u, 0u, 0u, 0u}, M = 0u;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    int cnt = 0;
+#pragma unroll
+    for (int bit = 16; bit >= 1; bit >>= 1) {
+      const int t = cnt + bit - 1;  // candidate midpoint index
+      if (cnt + bit <= top && f[i] > (float)(2 * t + 1 - 2 * half) * step2) cnt += bit;
+    }
+    if (a == 0.0f) cnt = half;  // all-zero group: the zero code
+    const uint32_t j5 = (uint32_t)cnt << (5 - b);
+    words[i / 8] |= (j5 & 15u) << (4 * (i % 8));
+    M |= (j5 >> 4) << dyadic5_msb_bit(i);
+  }
+  if (live) {
+    packed[c] = (u32x4){words[0], words[1], words[2], words[3]};
+    msb[c] = M;
+    if ((c & 1) == 0) scales[g] = (uint16_t)(__builtin_bit_cast(uint32_t, a) >> 16);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_quantize_dyadic5(int64_t n, int64_t k, const uint16_t* w, const uint8_t* widths,
+                                   uint8_t* packed, uint8_t* msb, uint16_t* scales,
+                                   hipStream_t stream) {
+  const int64_t nruns = n * k / 32;
+  const int64_t blocks = (nruns + 255) / 256;
+  quantize_dyadic5_kernel<<<dim3((uint32_t)blocks), dim3(256), 0, stream>>>(
+      reinterpret_cast<const u32x4*>(w), widths, reinterpret_cast<u32x4*>(packed),
+      reinterpret_cast<uint32_t*>(msb), scales, nruns);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize(int codec, int64_t n, int64_t k, const uint16_t* w, uint8_t* packed,
                            uint16_t* scales, const uint16_t* codebook, hipStream_t stream) {

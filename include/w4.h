@@ -179,7 +179,7 @@ w4_status w4_quantize_dyadic5(int64_t n, int64_t k, const uint16_t* w, const uin
  * 2-byte aligned.  codebook: bf16 [n][k/64][16], 16-byte aligned.
  * iters: 0 .. W4_MAX_FIT_ITERS (0: the quantile start itself).
  * Errors: W4_EINVAL (negative size, iters out of range, null pointer),
- * W4_ESHAPE (k % 64 != 0, or more than 2^40 groups), W4_EALIGN.
+ * W4_ESHAPE (k % 64 != 0, or more than 16 * (2^31 - 1) groups), W4_EALIGN.
  */
 w4_status w4_lut16_fit(int64_t n, int64_t k, const uint16_t* w, uint16_t* scales,
                        uint16_t* codebook, int32_t iters, void* stream);

@@ -109,7 +109,7 @@ def test_lut16_fit_validation(w4):
     assert call(w=P(8)) == 3 and call(L=P(24)) == 3 and call(s=P(17)) == 3
     assert call(n=0, w=None, s=None, L=None) == 0
     assert call(k=0, w=None, s=None, L=None) == 0
-    assert call(n=1 << 40, k=128) == 2
+    assert call(n=1 << 35, k=128) == 2          # 2^36 groups: more than 16 * (2^31 - 1)
 
 
 def test_quantize_dyadic5_validation(w4):

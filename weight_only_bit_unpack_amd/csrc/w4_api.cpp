@@ -150,7 +150,8 @@ w4_status w4_lut16_fit(int64_t n, int64_t k, const uint16_t* w, uint16_t* scales
   if (n == 0 || k == 0) return W4_OK;
   if (!w || !scales || !codebook) return W4_EINVAL;
   if (!aligned(w, 16) || !aligned(codebook, 16) || !aligned(scales, 2)) return W4_EALIGN;
-  if (n > (INT64_C(1) << 40) / (k / 64)) return W4_ESHAPE;  // grid of groups / 16 blocks
+  // one block per 16 groups: at most 2^31 - 1 blocks
+  if (n > ((INT64_C(1) << 31) - 1) * 16 / (k / 64)) return W4_ESHAPE;
   return launched(w4::launch_lut16_fit(n, k, w, scales, codebook, iters,
                                        static_cast<hipStream_t>(stream)));
 }

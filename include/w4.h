@@ -240,7 +240,8 @@ w4_status w4_gemm(int32_t codec, int64_t n, int64_t k, const uint8_t* packed,
  * Errors: W4_EINVAL / W4_ESHAPE / W4_EALIGN / W4_EUNSUPPORTED as for w4_gemv
  * (the plan reports the first failing problem's status and writes nothing to
  * *info); W4_ESHAPE when the problems need more than 2^31 - 1 tiles;
- * w4_gemv_batched returns W4_EINVAL when m differs from info->m.
+ * w4_gemv_batched returns W4_EINVAL when m differs from info->m or
+ * info->tile_rows is not one the plan can choose.
  */
 typedef struct {
   const uint8_t* packed;
@@ -254,11 +255,14 @@ typedef struct {
 } w4_gemv_problem;
 
 typedef struct {
-  int64_t total_tiles; /* 64-row work tiles over all problems */
+  int64_t total_tiles; /* work tiles over all problems */
   int64_t k_min;       /* smallest k */
   int64_t k_max;       /* largest k (sizes the kernel's LDS) */
   int32_t count;       /* number of problems */
   int32_t m;           /* the plan's m; w4_gemv_batched must be called with it */
+  int32_t tile_rows;   /* rows per work tile: 64, or 32 / 16 (m == 1 only)
+                          when 64-row tiles would give fewer than 1024 */
+  int32_t reserved;    /* 0 */
 } w4_gemv_batch_info;
 
 w4_status w4_gemv_batched_plan(int32_t codec, int32_t m, int32_t y_dtype,

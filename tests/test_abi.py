@@ -126,6 +126,11 @@ def test_quantize_dyadic5_validation(w4):
     assert w4._lib.w4_quantize_pack(4, 4, 64, P(16), P(16), P(16), P(16), None) == 4
 
 
+def test_struct_sizes_match_the_header(w4):
+    assert ctypes.sizeof(w4.W4Problem) == 64
+    assert ctypes.sizeof(w4.W4BatchInfo) == 40
+
+
 def test_batched_plan_validation(w4):
     arr = (w4.W4Problem * 3)()
     for i in range(2):
@@ -139,17 +144,20 @@ def test_batched_plan_validation(w4):
     assert info.total_tiles == 2 + 3 and arr[1].tile_begin == 0 and arr[0].tile_begin == 3
     assert (info.k_min, info.k_max, info.count, info.m) == (128, 192, 2, 16)
     assert (arr[2].n, arr[2].k, arr[2].tile_begin) == (7, 7, 7)
-    # m = 1: blocks of 64 * t rows (t row tiles per wave); the same order
-    assert plan(1) == 0 and info.m == 1
-    rows = next(r for r in (64, 128, 192, 256)
-                if info.total_tiles == -(-100 // r) + -(-164 // r) and arr[0].tile_begin == -(-164 // r))
-    assert arr[1].tile_begin == 0 and rows >= 64
+    assert info.tile_rows == 64
+    # m = 1 with few tiles: 16-row tiles (7 + 11), the same order
+    assert plan(1) == 0 and info.m == 1 and info.tile_rows == 16
+    assert info.total_tiles == 7 + 11 and arr[1].tile_begin == 0 and arr[0].tile_begin == 11
     assert w4._lib.w4_gemv_batched(0, 2, 0, ctypes.c_void_p(16), ctypes.byref(info), None) == 1
     arr[1].k = 100
     assert plan(1) == 2
     assert plan(17) == 2
     assert w4._lib.w4_gemv_batched(0, 1, 0, ctypes.c_void_p(8), ctypes.byref(info), None) == 3
-    bad = w4.W4BatchInfo(5, -1, 128, 2, 1)
+    bad = w4.W4BatchInfo(5, -1, 128, 2, 1, 64, 0)
     assert w4._lib.w4_gemv_batched(0, 1, 0, ctypes.c_void_p(16), ctypes.byref(bad), None) == 1
+    odd_rows = w4.W4BatchInfo(5, 128, 192, 2, 1, 48, 0)
+    assert w4._lib.w4_gemv_batched(0, 1, 0, ctypes.c_void_p(16), ctypes.byref(odd_rows), None) == 1
+    m16_rows = w4.W4BatchInfo(5, 128, 192, 2, 16, 16, 0)     # 16-row tiles only for m = 1
+    assert w4._lib.w4_gemv_batched(0, 16, 0, ctypes.c_void_p(16), ctypes.byref(m16_rows), None) == 1
     empty = w4.W4BatchInfo(0, 0, 0, 0, 1)
     assert w4._lib.w4_gemv_batched(0, 1, 0, None, ctypes.byref(empty), None) == 0

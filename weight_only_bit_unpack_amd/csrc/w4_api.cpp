@@ -80,6 +80,7 @@ constexpr int32_t kGemmMaxM = 65535 * 128;
 }  // namespace
 
 static_assert(sizeof(w4_gemv_problem) == sizeof(w4::GemvProblem), "problem layout");
+static_assert(sizeof(w4_gemv_batch_info) == 40, "batch info layout");
 
 extern "C" {
 
@@ -193,8 +194,17 @@ w4_status w4_gemv_batched_plan(int32_t codec, int32_t m, int32_t y_dtype,
     if (problems[i].k > kmax) kmax = problems[i].k;
     if (problems[i].k < kmin) kmin = problems[i].k;
   }
-  const int64_t rows = w4::gemv_batched_rows(m, kmax);
-  for (int32_t i = 0; i < count; ++i) total += (problems[i].n + rows - 1) / rows;
+  // the tallest tiles that still give the launch enough blocks
+  auto tiles_of = [&](int64_t rows) {
+    int64_t t = 0;
+    for (int32_t i = 0; i < count; ++i) t += (problems[i].n + rows - 1) / rows;
+    return t;
+  };
+  int64_t rows = 64;
+  if (m == 1) {
+    while (rows > 16 && tiles_of(rows) < w4::kGemvBatchedMinTiles) rows /= 2;
+  }
+  total = tiles_of(rows);
   if (total > 0x7FFFFFFF) return W4_ESHAPE;
   // Work is handed out in tile order; giving the longest rows (largest k) the
   // first tiles leaves short tiles for the end of the launch.
@@ -212,6 +222,8 @@ w4_status w4_gemv_batched_plan(int32_t codec, int32_t m, int32_t y_dtype,
   info->k_max = kmax;
   info->count = count;
   info->m = m;
+  info->tile_rows = (int32_t)rows;
+  info->reserved = 0;
   return W4_OK;
 }
 
@@ -226,12 +238,14 @@ w4_status w4_gemv_batched(int32_t codec, int32_t m, int32_t y_dtype,
   if (m > kGemvMaxM) return W4_ESHAPE;
   if (y_dtype != W4_F32 && y_dtype != W4_BF16) return W4_EUNSUPPORTED;
   if (info->count == 0 || info->total_tiles == 0) return W4_OK;
+  if (info->tile_rows != 64 && !(m == 1 && (info->tile_rows == 32 || info->tile_rows == 16)))
+    return W4_EINVAL;
   if (!problems_device) return W4_EINVAL;
   if (!aligned(problems_device, 16)) return W4_EALIGN;
   if (info->total_tiles > 0x7FFFFFFF) return W4_ESHAPE;
   return launched(w4::launch_gemv_batched(
       codec, reinterpret_cast<const w4::GemvProblem*>(problems_device), info->count,
-      info->total_tiles, info->k_max, m, y_dtype == W4_BF16,
+      info->total_tiles, info->k_max, info->tile_rows, m, y_dtype == W4_BF16,
       static_cast<hipStream_t>(stream)));
 }
 

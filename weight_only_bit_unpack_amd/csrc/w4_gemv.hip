@@ -586,16 +586,22 @@ hipError_t launch_gemv(int codec, const GemvProblem& p, int m, int y_bf16, hipSt
   return launch_codec<2>(p, m, y_bf16, stream);
 }
 
-int gemv_batched_rows(int, int64_t) { return 64; }
-
 template <int CODEC>
 hipError_t launch_batched_codec(const GemvProblem* probs_dev, int count, int64_t total_tiles,
-                                int xu, int m, int y_bf16, hipStream_t stream) {
+                                int xu, int tile_rows, int m, int y_bf16, hipStream_t stream) {
   const dim3 block(256), grid((uint32_t)total_tiles);
   const size_t lds = (size_t)(xu + 512) * 16;  // activations + 4 x 2 KiB shuffle areas
   const GemvProblem none{};
   const Slicing whole{1, 0, nullptr};
-  if (m == 1)
+  // m == 1: tiles of 64 / 32 / 16 rows = 4 / 2 / 1 row tiles of 16 per block,
+  // the block's 4 waves splitting k 1 / 2 / 4 ways
+  if (m == 1 && tile_rows == 16)
+    gemv_kernel<CODEC, 4, true, 1>
+        <<<grid, block, lds, stream>>>(none, probs_dev, count, m, y_bf16, xu, whole);
+  else if (m == 1 && tile_rows == 32)
+    gemv_kernel<CODEC, 2, true, 1>
+        <<<grid, block, lds, stream>>>(none, probs_dev, count, m, y_bf16, xu, whole);
+  else if (m == 1)
     gemv_kernel<CODEC, 1, true, 1>
         <<<grid, block, lds, stream>>>(none, probs_dev, count, m, y_bf16, xu, whole);
   else
@@ -605,14 +611,23 @@ hipError_t launch_batched_codec(const GemvProblem* probs_dev, int count, int64_t
 }
 
 hipError_t launch_gemv_batched(int codec, const GemvProblem* probs_dev, int count,
-                               int64_t total_tiles, int64_t k_max, int m, int y_bf16,
-                               hipStream_t stream) {
+                               int64_t total_tiles, int64_t k_max, int tile_rows, int m,
+                               int y_bf16, hipStream_t stream) {
   const int xu = xs_units_for(m, k_max);
-  if (codec == 0) return launch_batched_codec<0>(probs_dev, count, total_tiles, xu, m, y_bf16, stream);
-  if (codec == 1) return launch_batched_codec<1>(probs_dev, count, total_tiles, xu, m, y_bf16, stream);
-  if (codec == 3) return launch_batched_codec<3>(probs_dev, count, total_tiles, xu, m, y_bf16, stream);
-  if (codec == 4) return launch_batched_codec<4>(probs_dev, count, total_tiles, xu, m, y_bf16, stream);
-  return launch_batched_codec<2>(probs_dev, count, total_tiles, xu, m, y_bf16, stream);
+  if (codec == 0)
+    return launch_batched_codec<0>(probs_dev, count, total_tiles, xu, tile_rows, m, y_bf16,
+                                     stream);
+  if (codec == 1)
+    return launch_batched_codec<1>(probs_dev, count, total_tiles, xu, tile_rows, m, y_bf16,
+                                     stream);
+  if (codec == 3)
+    return launch_batched_codec<3>(probs_dev, count, total_tiles, xu, tile_rows, m, y_bf16,
+                                     stream);
+  if (codec == 4)
+    return launch_batched_codec<4>(probs_dev, count, total_tiles, xu, tile_rows, m, y_bf16,
+                                     stream);
+  return launch_batched_codec<2>(probs_dev, count, total_tiles, xu, tile_rows, m, y_bf16,
+                                  stream);
 }
 
 }  // namespace w4

@@ -36,14 +36,14 @@ hipError_t launch_lut16_fit(int64_t n, int64_t k, const uint16_t* w, uint16_t* s
 
 hipError_t launch_gemv(int codec, const GemvProblem& p, int m, int y_bf16, hipStream_t stream);
 
-// Rows per block of the batched GEMV for this m and largest k (the plan numbers
-// the blocks with it).
-int gemv_batched_rows(int m, int64_t k_max);
-// probs_dev: count problems with tile_begin set by the plan (blocks of
-// gemv_batched_rows(m, k_max) rows)
+// The batched GEMV's plan takes 64-row tiles, or for m == 1 halves them (down
+// to 16) while the launch would have fewer than this many tiles.
+constexpr int64_t kGemvBatchedMinTiles = 1024;
+// probs_dev: count problems with tile_begin set by the plan for tiles of
+// tile_rows (64; 32 or 16 only with m == 1) rows
 hipError_t launch_gemv_batched(int codec, const GemvProblem* probs_dev, int count,
-                               int64_t total_tiles, int64_t k_max, int m, int y_bf16,
-                               hipStream_t stream);
+                               int64_t total_tiles, int64_t k_max, int tile_rows, int m,
+                               int y_bf16, hipStream_t stream);
 
 // Library-owned device buffer of at least `bytes` for (current device, stream,
 // user); its contents are undefined.  Growing waits for the stream.

@@ -250,7 +250,8 @@ def other_configs(w4, synthetic, torch, dev, stream, args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
+        print(json.dumps({"error": "the benchmark runs on one GPU only (the library has no "
+                                   "multi-GPU path); run with --gpus 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 

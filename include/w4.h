@@ -223,6 +223,17 @@ w4_status w4_gemm(int32_t codec, int64_t n, int64_t k, const uint8_t* packed,
                   int32_t m, void* y, int32_t y_dtype, void* stream);
 
 /*
+ * w4_linear -- the linear layer with the kernel chosen by batch size, as
+ * [KM] sec. 4.1 lays out: m <= 16 -> w4_gemv (the table-lookup kernel),
+ * larger m -> w4_gemm (the mixed 4-bit x bf16 MFMA kernel; the page's further
+ * switch to a plain bf16 GEMM above m = 256 is not taken, as w4_gemm serves
+ * every m).  Same arguments, results and errors as the call it selects.
+ */
+w4_status w4_linear(int32_t codec, int64_t n, int64_t k, const uint8_t* packed,
+                    const uint16_t* scales, const uint16_t* codebook, const uint16_t* x,
+                    int32_t m, void* y, int32_t y_dtype, void* stream);
+
+/*
  * Batched GEMV: one launch over many independent w4_gemv problems of one codec
  * and one m (e.g. every linear layer of a decode step whose inputs are ready).
  * [DG] sec. 2.5 runs one unpack launch per layer, 168 per forward; one launch

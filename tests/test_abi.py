@@ -26,7 +26,7 @@ def w4():
 
 def test_header_declares_the_calls():
     names = _declared()
-    for n in ["w4_quantize_pack", "w4_unpack_dequant", "w4_gemv", "w4_gemm", "w4_lut16_fit",
+    for n in ["w4_quantize_pack", "w4_unpack_dequant", "w4_gemv", "w4_gemm", "w4_linear", "w4_lut16_fit",
               "w4_quantize_dyadic5",
               "w4_gemv_batched_plan", "w4_gemv_batched", "w4_status_str", "w4_group_size"]:
         assert n in names
@@ -78,6 +78,10 @@ def test_validation_errors(w4):
     # k beyond W4_MAX_MATMUL_K (4,194,304) is rejected before any launch
     assert _gemv(w4, k=4194304 + 64) == E["shape"]
     assert _gemv(w4, k=4194304 + 64, fn="w4_gemm") == E["shape"]
+    # w4_linear validates as the call it selects
+    assert _gemv(w4, m=-1, fn="w4_linear") == E["inval"]
+    assert _gemv(w4, m=17, packed=8, fn="w4_linear") == E["align"]
+    assert _gemv(w4, k=96, fn="w4_linear") == E["shape"]
     # empty problems are accepted without touching anything
     assert _gemv(w4, n=0, packed=None, scales=None, x=None, y=None) == 0
     assert _gemv(w4, m=0, x=None, y=None) == 0

@@ -258,6 +258,20 @@ def test_lut16_gemv_and_gemm(w4, m):
     _gemv_check(y2, x, w_hat, False)
 
 
+@pytest.mark.parametrize("m", [1, 16, 17, 256])
+def test_linear_dispatch(w4, m):
+    """w4_linear equals the call it selects, bit for bit, on both sides of m = 16."""
+    n, k = 300, 1024
+    report("linear", m=m)
+    w = synthetic.normal_bf16((n, k), 0.02, 1700 + m)
+    x = dev_bf16(synthetic.normal_bf16((m, k), 1.0, 1701 + m))
+    p, s = w4.w4_quantize_pack(dev_bf16(w), w4.W4_DYADIC)
+    y = w4.w4_linear(p, x, w4.W4_DYADIC, scales=s)
+    direct = (w4.w4_gemv if m <= 16 else w4.w4_gemm)(p, x, w4.W4_DYADIC, scales=s)
+    torch.cuda.synchronize()
+    assert torch.equal(y, direct)
+
+
 # ------------------------------------------------------------------ LUT16S
 def _lut16s_case(n, k, seed):
     """Weight with a zero group, its group scales and the oracle's whole-weight

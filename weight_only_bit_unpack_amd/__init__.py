@@ -50,6 +50,7 @@ _SIGS = {
     "w4_quantize_dyadic5": ([_I64, _I64, _P, _P, _P, _P, _P, _P], _I32),
     "w4_gemv": ([_I32, _I64, _I64, _P, _P, _P, _P, _I32, _P, _I32, _P], _I32),
     "w4_gemm": ([_I32, _I64, _I64, _P, _P, _P, _P, _I32, _P, _I32, _P], _I32),
+    "w4_linear": ([_I32, _I64, _I64, _P, _P, _P, _P, _I32, _P, _I32, _P], _I32),
     "w4_gemv_batched_plan": ([_I32, _I32, _I32, ctypes.POINTER(W4Problem), _I32,
                               ctypes.POINTER(W4BatchInfo)], _I32),
     "w4_gemv_batched": ([_I32, _I32, _I32, _P, ctypes.POINTER(W4BatchInfo), _P], _I32),
@@ -227,6 +228,13 @@ def w4_gemm(packed, x, codec=W4_DYADIC, *, scales=None, codebook=None, y=None,
             y_dtype=torch.float32, stream=None):
     """Y[m, n] = X[m, k] @ w_hat[n, k]^T, bf16 MFMA (fused dequant), any m >= 1."""
     return _matmul(_lib.w4_gemm, packed, x, codec, scales, codebook, y, y_dtype, stream)
+
+
+def w4_linear(packed, x, codec=W4_DYADIC, *, scales=None, codebook=None, y=None,
+              y_dtype=torch.float32, stream=None):
+    """Y[m, n] = X[m, k] @ w_hat[n, k]^T with the kernel chosen by m (GEMV for
+    m <= 16, GEMM above)."""
+    return _matmul(_lib.w4_linear, packed, x, codec, scales, codebook, y, y_dtype, stream)
 
 
 class W4GemvBatch:

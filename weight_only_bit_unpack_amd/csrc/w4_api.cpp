@@ -177,6 +177,14 @@ w4_status w4_gemm(int32_t codec, int64_t n, int64_t k, const uint8_t* packed,
                                   y_dtype == W4_BF16, static_cast<hipStream_t>(stream)));
 }
 
+w4_status w4_linear(int32_t codec, int64_t n, int64_t k, const uint8_t* packed,
+                    const uint16_t* scales, const uint16_t* codebook, const uint16_t* x,
+                    int32_t m, void* y, int32_t y_dtype, void* stream) {
+  if (m >= 0 && m <= kGemvMaxM)
+    return w4_gemv(codec, n, k, packed, scales, codebook, x, m, y, y_dtype, stream);
+  return w4_gemm(codec, n, k, packed, scales, codebook, x, m, y, y_dtype, stream);
+}
+
 w4_status w4_gemv_batched_plan(int32_t codec, int32_t m, int32_t y_dtype,
                                w4_gemv_problem* problems, int32_t count,
                                w4_gemv_batch_info* info) {

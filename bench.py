@@ -121,17 +121,6 @@ def shared_table_levels(w):
             v[q].to(torch.bfloat16).contiguous())
 
 
-def magnitude_levels(w):
-    """SIGNMAG8 magnitudes for timing runs: the Lloyd starting point (sorted
-    |w| of each group of 32 at ranks 4q + 2, as fp16), built with torch on the
-    device.  Throughput does not depend on the levels' values; parity of
-    fitted levels is checked in the tests."""
-    import torch
-    n, k = w.shape
-    v = torch.sort(w.float().reshape(n, k // 32, 32).abs(), dim=-1).values
-    return v[..., 2::4].to(torch.float16).contiguous()
-
-
 FIT_STEPS = 5  # timed k-means fits per shape (each takes milliseconds)
 
 
@@ -224,8 +213,14 @@ def other_configs(w4, synthetic, torch, dev, stream, args):
     probs, total = [], 0
     for i in range(224):
         W = synthetic.student_t_bf16_device((2048, 2048), 5, 0.02, synthetic.seed(4, i, 0), dev)
-        cb = magnitude_levels(W)
-        P, _ = w4.w4_quantize_pack(W, w4.W4_SIGNMAG8, codebook=cb)
+        cb = w4.w4_signmag8_fit(W, 25, stream=stream)
+        if i == 0:
+            ms = timed(lambda: w4.w4_signmag8_fit(W, 25, codebook=cb, stream=stream), stream,
+                       FIT_STEPS, 1)
+            rows["signmag8_fit_2048x2048"] = {"ms": ms,
+                                              "Mgroups/s": 2048 * 64 / (ms * 1e-3) / 1e6,
+                                              "Gweights/s": 2048 * 2048 / (ms * 1e-3) / 1e9}
+        P, _ = w4.w4_quantize_pack(W, w4.W4_SIGNMAG8, codebook=cb, stream=stream)
         del W
         x = synthetic.normal_bf16_device((1, 2048), 1.0, synthetic.seed(4, i, 1), dev)
         probs.append({"packed": P, "codebook": cb, "x": x, "y": torch.empty((1, 2048), device=dev)})
@@ -278,8 +273,13 @@ def main():
                                                       synthetic.seed(3, i, 0), dev)
             ms_f = timed(lambda: w4.w4_lut16_fit(W, 25, stream=stream), stream, args.steps,
                          args.warmup)
-            print(json.dumps({"target": "fit", "shape": [n, k], "ms": ms_f,
+            print(json.dumps({"target": "lut16_fit", "shape": [n, k], "ms": ms_f,
                               "Mgroups/s": n * k / 64 / (ms_f * 1e-3) / 1e6}), flush=True)
+        W = synthetic.student_t_bf16_device((2048, 2048), 5, 0.02, synthetic.seed(4, 0, 0), dev)
+        ms_f = timed(lambda: w4.w4_signmag8_fit(W, 25, stream=stream), stream, args.steps,
+                     args.warmup)
+        print(json.dumps({"target": "signmag8_fit", "shape": [2048, 2048], "ms": ms_f,
+                          "Mgroups/s": 2048 * 64 / (ms_f * 1e-3) / 1e6}), flush=True)
         return
     if args.only == "gemm":
         ms_g, tf = time_gemm(w4, synthetic, torch, dev, stream, args)

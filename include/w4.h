@@ -95,7 +95,7 @@ typedef enum {
 /* Largest k of a matrix product call: keeps every per-block byte offset of the
  * kernels within 32 bits. */
 #define W4_MAX_MATMUL_K 4194304
-/* Largest Lloyd round count w4_lut16_fit accepts. */
+/* Largest Lloyd round count w4_lut16_fit and w4_signmag8_fit accept. */
 #define W4_MAX_FIT_ITERS 1024
 typedef enum { W4_F32 = 0, W4_BF16 = 1, W4_F16 = 2 } w4_dtype;
 
@@ -183,6 +183,28 @@ w4_status w4_quantize_dyadic5(int64_t n, int64_t k, const uint16_t* w, const uin
  */
 w4_status w4_lut16_fit(int64_t n, int64_t k, const uint16_t* w, uint16_t* scales,
                        uint16_t* codebook, int32_t iters, void* stream);
+
+/*
+ * w4_signmag8_fit -- fit the W4_SIGNMAG8 magnitudes of a bf16 weight [n][k]:
+ * per group of 32, 8 levels by 1D k-means on the magnitudes.  [G32] sec. 1.3
+ * (groups of 32, |w| clustered into 8 magnitudes by Lloyd rounds from a
+ * quantile start, 25 rounds, fp16 codebook).
+ * For each group, in fp64: a = |w|;
+ *   start: the elements of rank 4q + 2 (q = 0..7) in an ascending sort of a;
+ *   `iters` rounds as in w4_lut16_fit (nearest centre, lowest on a tie; the
+ *          members' sum in increasing element order over their count; a
+ *          centre without members keeps its value);
+ *   codebook[r][g][q] = c_q rounded to fp16 (nearest, ties to even; at or
+ *          above 65520 the result is +inf).
+ * Bit-exact like w4_lut16_fit.  The output is the codebook input of
+ * w4_quantize_pack and the matrix calls for W4_SIGNMAG8 (those need k % 64 == 0).
+ * w: bf16 [n][k], 16-byte aligned; finite values.  codebook: fp16 [n][k/32][8],
+ * 16-byte aligned.  iters: 0 .. W4_MAX_FIT_ITERS.
+ * Errors: W4_EINVAL (negative size, iters out of range, null pointer),
+ * W4_ESHAPE (k % 32 != 0, or more than 32 * (2^31 - 1) groups), W4_EALIGN.
+ */
+w4_status w4_signmag8_fit(int64_t n, int64_t k, const uint16_t* w, uint16_t* codebook,
+                          int32_t iters, void* stream);
 
 /*
  * w4_gemv -- fused dequant + matrix-vector product for small batches,

@@ -184,8 +184,9 @@ def test_fullsize_lut16s_batched():
 # ------------------------------------------------------------ 2B SIGNMAG8
 def test_fullsize_signmag8_stack(w4):
     """2048^2 matrices, Student-t nu = 5 at sigma 0.02, group 32 sign +
-    3-bit magnitude with the oracle's fitted fp16 codebooks: dense dequant
-    and one batched m = 1 GEMV launch over 16 matrices."""
+    3-bit magnitude: the fp16 codebooks fitted on the GPU, equal to the
+    oracle's fit on every group; dense dequant and one batched m = 1 GEMV
+    launch over 16 matrices."""
     n = k = 2048
     count = 16
     report("fullsize_signmag8", matrices=count)
@@ -193,7 +194,9 @@ def test_fullsize_signmag8_stack(w4):
     for i in range(count):
         w = synthetic.student_t_bf16_device((n, k), 5, 0.02, synthetic.seed(4, i, 0))
         cb = native.signmag8_fit(host_bits(w))
-        cb_dev = dev_f16(cb)
+        cb_dev = w4.w4_signmag8_fit(w)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(cb_dev), cb)
         p, _ = w4.w4_quantize_pack(w, w4.W4_SIGNMAG8, codebook=cb_dev)
         d = w4.w4_unpack_dequant(p, w4.W4_SIGNMAG8, codebook=cb_dev)
         torch.cuda.synchronize()

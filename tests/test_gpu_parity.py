@@ -241,6 +241,23 @@ def test_lut16_fit_bitexact(w4, iters):
         assert np.array_equal(host_bits(L), L_o), w.shape
 
 
+@pytest.mark.parametrize("iters", [0, 1, 25])
+def test_signmag8_fit_bitexact(w4, iters):
+    """GPU k-means magnitude fit == the C oracle's fit, bit for bit: tie and
+    fp16-rounding groups (equal magnitudes, signed zeros, subnormal, overflow),
+    Student-t groups, 32 groups per block with a ragged last block, k a
+    multiple of 32 but not of 64."""
+    from tests.test_oracle_lut16 import signmag8_tie_groups
+    report("signmag8_fit", iters=iters)
+    ties = signmag8_tie_groups()
+    rnd = synthetic.student_t_bf16((37, 352), 5, 0.02, 79)
+    for w in (ties, rnd, synthetic.normal_bf16((300, 1024), 0.02, 80), rnd[:1, :32]):
+        cb_o = native.signmag8_fit(w, iters)
+        cb = w4.w4_signmag8_fit(dev_bf16(w), iters)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(cb), cb_o), w.shape
+
+
 @pytest.mark.parametrize("m", [1, 4, 16])
 def test_lut16_gemv_and_gemm(w4, m):
     n, k = 300, 1024

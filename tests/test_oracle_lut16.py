@@ -282,3 +282,41 @@ def test_signmag8_fit_monotone_and_c_matches():
     a = np.abs(bits.bf16_to_f64(w)).reshape(-1, 32)
     _, h = lut16.lloyd(a, lut16.quantile_init(a, 8), 25, history=True)
     assert np.all(np.diff(h, axis=-1) <= 1e-15)
+
+
+def signmag8_tie_groups():
+    """bf16 groups of 32 whose SIGNMAG8 fit depends on ties and on the fp16
+    rounding: +-x pairs (equal magnitudes), signed zeros, few distinct
+    magnitudes, magnitudes whose centres round to fp16 subnormals, to zero,
+    to the fp16 maximum or overflow to infinity.  Shared with the GPU parity
+    test of the fit."""
+    g = np.random.default_rng(31)
+    rows = []
+    z = np.zeros(32, np.uint16)
+    a = bits.rne_bf16(np.repeat(g.normal(0, 0.02, 16), 2) * np.tile([1, -1], 16))
+    rows.append(a)                                           # +-x pairs
+    b = z.copy(); b[0:20:2] = 0x8000; b[20:] = bits.rne_bf16(-np.arange(1, 13) / 12.0)
+    rows.append(b)                                           # signed zeros + a ramp
+    rows.append(bits.rne_bf16(g.choice([-0.5, 0.25, 1.0, -1.0], 32)))
+    rows.append(z.copy())                                    # all zero
+    # magnitudes between 2^-27 and 2^-13: fp16 subnormals, zero and the first normals
+    rows.append(bits.rne_bf16(g.choice([-1, 1], 32) * 2.0 ** g.uniform(-27, -13, 32)))
+    # magnitudes around the fp16 maximum 65504 and the overflow threshold 65520
+    rows.append(bits.rne_bf16(g.choice([-1, 1], 32) * g.uniform(64000, 67000, 32)))
+    rows.append((g.integers(0x7E00, 0x7F7F, 32) | (g.integers(0, 2, 32) << 15)).astype(np.uint16))
+    h = z.copy(); h[7] = 0xBF80
+    rows.append(h)                                           # one nonzero value
+    return np.stack(rows).reshape(2, 4 * 32)
+
+
+def test_signmag8_c_matches_python_on_ties():
+    w = signmag8_tie_groups()
+    for iters in (0, 1, 25):
+        cb = signmag8.fit(w, iters)
+        assert np.array_equal(cb, native.signmag8_fit(w, iters)), iters
+    cb = signmag8.fit(w, 25)
+    # the overflow and subnormal cases are reached
+    assert np.any(cb == 0x7C00) and np.any((cb > 0) & (cb < 0x0400))
+    # 0 rounds: the centres are the magnitudes of sorted rank 4q + 2
+    a = np.sort(np.abs(bits.bf16_to_f64(w[0, :32])))
+    assert np.array_equal(signmag8.fit(w, 0)[0, 0], bits.rne_fp16(a[2::4]))

@@ -47,6 +47,7 @@ _SIGS = {
     "w4_quantize_pack": ([_I32, _I64, _I64, _P, _P, _P, _P, _P], _I32),
     "w4_unpack_dequant": ([_I32, _I64, _I64, _P, _P, _P, _P, _P], _I32),
     "w4_lut16_fit": ([_I64, _I64, _P, _P, _P, _I32, _P], _I32),
+    "w4_signmag8_fit": ([_I64, _I64, _P, _P, _I32, _P], _I32),
     "w4_quantize_dyadic5": ([_I64, _I64, _P, _P, _P, _P, _P, _P], _I32),
     "w4_gemv": ([_I32, _I64, _I64, _P, _P, _P, _P, _I32, _P, _I32, _P], _I32),
     "w4_gemm": ([_I32, _I64, _I64, _P, _P, _P, _P, _I32, _P, _I32, _P], _I32),
@@ -197,6 +198,19 @@ def w4_lut16_fit(w, iters=25, *, scales=None, codebook=None, stream=None):
     _check(_lib.w4_lut16_fit(n, k, _ptr(w), _ptr(scales), _ptr(codebook), iters,
                              _stream(stream)))
     return scales, codebook
+
+
+def w4_signmag8_fit(w, iters=25, *, codebook=None, stream=None):
+    """Fit the SIGNMAG8 codec's 8 fp16 magnitudes per group of 32 to a bf16
+    weight [n, k] on the GPU (1D k-means on |w|).  Returns the codebook
+    (float16 [n, k/32, 8]) that w4_quantize_pack takes for W4_SIGNMAG8."""
+    _need(w, "w", _U16)
+    n, k = w.shape
+    if codebook is None:
+        codebook = torch.empty((n, k // 32, 8), dtype=torch.float16, device=w.device)
+    _need(codebook, "codebook", _U16, (n, k // 32, 8))
+    _check(_lib.w4_signmag8_fit(n, k, _ptr(w), _ptr(codebook), iters, _stream(stream)))
+    return codebook
 
 
 def _matmul(fn, packed, x, codec, scales, codebook, y, y_dtype, stream):

@@ -95,7 +95,7 @@ typedef enum {
 /* Largest k of a matrix product call: keeps every per-block byte offset of the
  * kernels within 32 bits. */
 #define W4_MAX_MATMUL_K 4194304
-/* Largest Lloyd round count w4_lut16_fit and w4_signmag8_fit accept. */
+/* Largest Lloyd round count the fit calls accept. */
 #define W4_MAX_FIT_ITERS 1024
 typedef enum { W4_F32 = 0, W4_BF16 = 1, W4_F16 = 2 } w4_dtype;
 
@@ -205,6 +205,39 @@ w4_status w4_lut16_fit(int64_t n, int64_t k, const uint16_t* w, uint16_t* scales
  */
 w4_status w4_signmag8_fit(int64_t n, int64_t k, const uint16_t* w, uint16_t* codebook,
                           int32_t iters, void* stream);
+
+/*
+ * w4_signmag8_fit_warm -- fit the W4_SIGNMAG8 magnitudes with the warm start:
+ * per group of 32, the best of 112 parametric transforms gives 8 starting
+ * levels, then Lloyd rounds as in w4_signmag8_fit.  [G32] sec. 1.2 (the two
+ * transform families and their inverses), 1.3 steps 1-3, 5.1 (the per-group
+ * procedure), 2 (the 8-bit per-group parameter code).
+ * For each group, in fp64, with a = |w| and gmax = max a:
+ *   candidates in increasing code (the lowest code wins a tie):
+ *     rational, code = b_idx << 3 | beta_idx: f(a) = a / (b + a^beta) with
+ *       b = 10^((5 b_idx - 42) / 14) * gmax (b_idx 0..14) and beta =
+ *       {0.50, 0.55, 0.65, 0.75, 0.85, 0.95, 1.00}[beta_idx];
+ *     tanh, code = 128 | b_idx << 3: f(a) = tanh(a / b), b =
+ *       {0.25, 0.4, 0.6, 0.85, 1.2, 1.8, 3.0}[b_idx] * gmax;
+ *   per candidate: fmax = f(gmax); q_i = rint((f(a_i) / fmax) * 7) in 0..7;
+ *     levels L_q = f^-1((q / 7) * fmax) (rational beta = 1: fd*b / (1 - fd);
+ *     beta < 1: the root of w = fd*b + fd*w^beta; tanh: b * atanh(fd));
+ *     error = sum over i in element order of (a_i - L_{q_i})^2;
+ *   the winner's 8 levels start `iters` Lloyd rounds on a; codebook = the
+ *   levels rounded to fp16; params (if not NULL) = the winner's code.
+ * An all-zero group gets 8 zero levels and code 0.  pow, tanh and atanh are
+ * the device math library's, within a few ulps of the exact functions: the
+ * result can differ from another implementation of the same steps in the
+ * last bits of a level, and so, on a near-tie of two candidates' errors, in
+ * the candidate chosen.
+ * w: bf16 [n][k], 16-byte aligned; finite values.  codebook: fp16
+ * [n][k/32][8], 16-byte aligned.  params: uint8 [n][k/32] or NULL.
+ * iters: 0 .. W4_MAX_FIT_ITERS.
+ * Errors: W4_EINVAL (negative size, iters out of range, null w or codebook),
+ * W4_ESHAPE (k % 32 != 0, or more than 2 * (2^31 - 1) groups), W4_EALIGN.
+ */
+w4_status w4_signmag8_fit_warm(int64_t n, int64_t k, const uint16_t* w, uint16_t* codebook,
+                               uint8_t* params, int32_t iters, void* stream);
 
 /*
  * w4_gemv -- fused dequant + matrix-vector product for small batches,

@@ -27,7 +27,7 @@ def w4():
 def test_header_declares_the_calls():
     names = _declared()
     for n in ["w4_quantize_pack", "w4_unpack_dequant", "w4_gemv", "w4_gemm", "w4_linear", "w4_lut16_fit",
-              "w4_signmag8_fit", "w4_quantize_dyadic5",
+              "w4_signmag8_fit", "w4_signmag8_fit_warm", "w4_quantize_dyadic5",
               "w4_gemv_batched_plan", "w4_gemv_batched", "w4_status_str", "w4_group_size"]:
         assert n in names
 
@@ -129,6 +129,21 @@ def test_signmag8_fit_validation(w4):
     assert call(n=0, w=None, cb=None) == 0
     assert call(k=0, w=None, cb=None) == 0
     assert call(n=1 << 36, k=64) == 2          # 2^37 groups: more than 32 * (2^31 - 1)
+
+
+def test_signmag8_fit_warm_validation(w4):
+    f = w4._lib.w4_signmag8_fit_warm
+    P = ctypes.c_void_p
+    ok = dict(n=4, k=32, w=P(16), cb=P(16), pr=None, it=25)
+    call = lambda **kw: f(*[{**ok, **kw}[a] for a in ("n", "k", "w", "cb", "pr", "it")], None)
+    assert call(n=-1) == 1 and call(k=-32) == 1
+    assert call(k=48) == 2
+    assert call(it=-1) == 1 and call(it=1025) == 1
+    assert call(w=None) == 1 and call(cb=None) == 1
+    assert call(w=P(8)) == 3 and call(cb=P(24)) == 3
+    assert call(n=0, w=None, cb=None) == 0
+    assert call(k=0, w=None, cb=None) == 0
+    assert call(n=1 << 33, k=64) == 2          # 2^34 groups: more than 2 * (2^31 - 1)
 
 
 def test_quantize_dyadic5_validation(w4):

@@ -181,6 +181,23 @@ def test_fullsize_lut16s_batched():
         _check_outputs(pr["y"], rows, host_bits(pr["x"]), w_hat)
 
 
+# ------------------------------------------------------------ 2B SIGNMAG8, warm start
+def test_fullsize_signmag8_warm():
+    """The warm-start fit on two whole 2048^2 Student-t (nu = 5) matrices in
+    one call each; 1024 sampled groups of each against the oracle."""
+    import weight_only_bit_unpack_amd as w4
+    from tests.test_gpu_parity import _warm_check
+    report("fullsize_signmag8_warm")
+    for i in range(2):
+        w = synthetic.student_t_bf16_device((2048, 2048), 5, 0.02, synthetic.seed(4, i, 0))
+        cb, pr = w4.w4_signmag8_fit_warm(w)
+        torch.cuda.synchronize()
+        groups = np.random.default_rng(9100 + i).choice(2048 * 64, 1024, replace=False)
+        wb = host_bits(w).reshape(-1, 32)[groups]
+        _warm_check(wb, host_bits(cb).reshape(-1, 8)[groups],
+                    host_u8(pr).reshape(-1)[groups], 25, max_mismatch=0.01)
+
+
 # ------------------------------------------------------------ 2B SIGNMAG8
 def test_fullsize_signmag8_stack(w4):
     """2048^2 matrices, Student-t nu = 5 at sigma 0.02, group 32 sign +

@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import synthetic
-from oracle import bits, dyadic, dyadic5, lut16, matmul, native, packing, signmag8
+from oracle import bits, dyadic, dyadic5, lut16, matmul, native, packing, signmag8, warmstart
 from tests.gpu_util import dev_bf16, dev_f16, dev_u8, host_bits, host_f32, host_u8, report
 
 pytestmark = pytest.mark.gpu
@@ -256,6 +256,59 @@ def test_signmag8_fit_bitexact(w4, iters):
         cb = w4.w4_signmag8_fit(dev_bf16(w), iters)
         torch.cuda.synchronize()
         assert np.array_equal(host_bits(cb), cb_o), w.shape
+
+
+def _warm_check(w, cb, params, iters, max_mismatch):
+    """GPU warm-start fit against the oracle.  Chosen candidates: equal, or a
+    near-tie of the oracle's own candidate errors (relative 1e-9, or 1e-28
+    gmax^2 absolute), on at most
+    max_mismatch of the groups; codebooks: bit-identical wherever the chosen
+    candidates are; elsewhere the GPU's levels, used as a codebook, do no
+    worse than its chosen candidate's start (up to fp16 rounding)."""
+    a = np.abs(bits.bf16_to_f64(w)).reshape(-1, 32)
+    lev, code_o, sses = warmstart.warm_start(a)
+    M_o = bits.rne_fp16(lut16.lloyd(a, lev, iters))
+    code_g = np.asarray(params).reshape(-1) if isinstance(params, np.ndarray) else \
+        host_u8(params).reshape(-1)
+    M_g = np.asarray(cb).reshape(-1, 8) if isinstance(cb, np.ndarray) else \
+        host_bits(cb).reshape(-1, 8)
+    index = {c[0]: i for i, c in enumerate(warmstart.candidates())}
+    live = a.max(axis=-1) > 0
+    assert np.all(code_g[~live] == 0) and np.all(M_g[~live] == 0)
+    gi = np.array([index[int(c)] for c in code_g])
+    s_g = sses[np.arange(a.shape[0]), gi]
+    s_min = sses.min(axis=-1)
+    # a near-tie: relative 1e-9, or a few ulps of gmax in every level (an exact
+    # zero error on one side can be 1e-32 * gmax^2 on the other)
+    slack = s_min * 1e-9 + 1e-28 * a.max(axis=-1) ** 2
+    assert np.all(s_g[live] <= (s_min + slack)[live]), "GPU picked a worse candidate"
+    same = code_g == code_o
+    assert np.array_equal(M_g[same], M_o[same])
+    diff = ~same
+    print(f"  {a.shape[0]} groups, {int(diff.sum())} with another near-tie candidate")
+    assert diff.sum() <= max_mismatch * a.shape[0], diff.sum()
+    if diff.any():
+        e_g = warmstart.group_sse(a[diff], bits.f16_to_f64(M_g[diff]))
+        assert np.all(e_g <= s_g[diff] * (1 + 2.0 ** -9) + 1e-30)
+
+
+@pytest.mark.parametrize("iters", [0, 25])
+def test_signmag8_fit_warm(w4, iters):
+    """Warm-start magnitude fit (112 transforms, then Lloyd) on the GPU vs the
+    oracle: tie and fp16-rounding groups (equal magnitudes, signed zeros,
+    subnormals, overflow; near-ties of candidates allowed there), Student-t
+    and Gaussian groups with a ragged last block and k a multiple of 32 only."""
+    from tests.test_oracle_lut16 import signmag8_tie_groups
+    report("signmag8_fit_warm", iters=iters)
+    ties = signmag8_tie_groups()
+    cb, pr = w4.w4_signmag8_fit_warm(dev_bf16(ties), iters)
+    torch.cuda.synchronize()
+    _warm_check(ties, cb, pr, iters, max_mismatch=1.0)
+    for w in (synthetic.student_t_bf16((37, 352), 5, 0.02, 81),
+              synthetic.normal_bf16((8, 1024), 0.02, 82)):
+        cb, pr = w4.w4_signmag8_fit_warm(dev_bf16(w), iters)
+        torch.cuda.synchronize()
+        _warm_check(w, cb, pr, iters, max_mismatch=0.01)
 
 
 @pytest.mark.parametrize("m", [1, 4, 16])

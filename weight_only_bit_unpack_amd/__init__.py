@@ -48,6 +48,7 @@ _SIGS = {
     "w4_unpack_dequant": ([_I32, _I64, _I64, _P, _P, _P, _P, _P], _I32),
     "w4_lut16_fit": ([_I64, _I64, _P, _P, _P, _I32, _P], _I32),
     "w4_signmag8_fit": ([_I64, _I64, _P, _P, _I32, _P], _I32),
+    "w4_signmag8_fit_warm": ([_I64, _I64, _P, _P, _P, _I32, _P], _I32),
     "w4_quantize_dyadic5": ([_I64, _I64, _P, _P, _P, _P, _P, _P], _I32),
     "w4_gemv": ([_I32, _I64, _I64, _P, _P, _P, _P, _I32, _P, _I32, _P], _I32),
     "w4_gemm": ([_I32, _I64, _I64, _P, _P, _P, _P, _I32, _P, _I32, _P], _I32),
@@ -211,6 +212,23 @@ def w4_signmag8_fit(w, iters=25, *, codebook=None, stream=None):
     _need(codebook, "codebook", _U16, (n, k // 32, 8))
     _check(_lib.w4_signmag8_fit(n, k, _ptr(w), _ptr(codebook), iters, _stream(stream)))
     return codebook
+
+
+def w4_signmag8_fit_warm(w, iters=25, *, codebook=None, params=None, stream=None):
+    """Warm-start fit of the SIGNMAG8 magnitudes (the best of 112 parametric
+    transforms per group of 32, then Lloyd rounds) on the GPU.  Returns
+    (codebook float16 [n, k/32, 8], parameter codes uint8 [n, k/32])."""
+    _need(w, "w", _U16)
+    n, k = w.shape
+    if codebook is None:
+        codebook = torch.empty((n, k // 32, 8), dtype=torch.float16, device=w.device)
+    if params is None:
+        params = torch.empty((n, k // 32), dtype=torch.uint8, device=w.device)
+    _need(codebook, "codebook", _U16, (n, k // 32, 8))
+    _need(params, "params", (torch.uint8,), (n, k // 32))
+    _check(_lib.w4_signmag8_fit_warm(n, k, _ptr(w), _ptr(codebook), _ptr(params), iters,
+                                     _stream(stream)))
+    return codebook, params
 
 
 def _matmul(fn, packed, x, codec, scales, codebook, y, y_dtype, stream):

@@ -170,6 +170,19 @@ w4_status w4_signmag8_fit(int64_t n, int64_t k, const uint16_t* w, uint16_t* cod
                                           static_cast<hipStream_t>(stream)));
 }
 
+w4_status w4_signmag8_fit_warm(int64_t n, int64_t k, const uint16_t* w, uint16_t* codebook,
+                               uint8_t* params, int32_t iters, void* stream) {
+  if (n < 0 || k < 0 || iters < 0 || iters > W4_MAX_FIT_ITERS) return W4_EINVAL;
+  if (k % 32 != 0) return W4_ESHAPE;
+  if (n == 0 || k == 0) return W4_OK;
+  if (!w || !codebook) return W4_EINVAL;
+  if (!aligned(w, 16) || !aligned(codebook, 16)) return W4_EALIGN;
+  // one block per 2 groups: at most 2^31 - 1 blocks
+  if (n > ((INT64_C(1) << 31) - 1) * 2 / (k / 32)) return W4_ESHAPE;
+  return launched(w4::launch_signmag8_warm_fit(n, k, w, codebook, params, iters,
+                                               static_cast<hipStream_t>(stream)));
+}
+
 w4_status w4_gemv(int32_t codec, int64_t n, int64_t k, const uint8_t* packed,
                   const uint16_t* scales, const uint16_t* codebook, const uint16_t* x,
                   int32_t m, void* y, int32_t y_dtype, void* stream) {

@@ -35,6 +35,8 @@ hipError_t launch_lut16_fit(int64_t n, int64_t k, const uint16_t* w, uint16_t* s
                             uint16_t* lut, int iters, hipStream_t stream);
 hipError_t launch_signmag8_fit(int64_t n, int64_t k, const uint16_t* w, uint16_t* codebook,
                                int iters, hipStream_t stream);
+hipError_t launch_signmag8_warm_fit(int64_t n, int64_t k, const uint16_t* w, uint16_t* codebook,
+                                    uint8_t* params, int iters, hipStream_t stream);
 
 hipError_t launch_gemv(int codec, const GemvProblem& p, int m, int y_bf16, hipStream_t stream);
 

@@ -12,10 +12,11 @@
  *        16-centre 1D k-means codebook + 16-bit scale, nearest-centre index;
  *        sec. 2.2 decode by table lookup; sec. 4.1 kernel choice by batch m
  *        (a LUT kernel for m <= 16, a mixed 4-bit kernel up to 256).
- *  [G32] "int4-g32+warm 裸量化：原理与实验报告": sec. 1.3 nearest of 8 levels
- *        per group of 32 with a separate sign bit; sec. 2 1 sign bit + 3-bit
- *        level index per weight, dense fp16 rebuild or a fused int4 kernel
- *        with the 8-value codebook in registers.
+ *  [G32] "int4-g32+warm 裸量化：原理与实验报告": sec. 1.2 the transform
+ *        families of the warm start; sec. 1.3 nearest of 8 levels per group
+ *        of 32 with a separate sign bit, Lloyd refinement; sec. 2 1 sign bit +
+ *        3-bit level index per weight, dense fp16 rebuild or a fused int4
+ *        kernel with the 8-value codebook in registers.
  *
  * Conventions shared by every call
  * --------------------------------
@@ -32,7 +33,8 @@
  *    (fixed reduction order, no atomics).
  *  - Weights are row-major [n][k] (n = output features, k = input features,
  *    the layout of a PyTorch Linear weight).  A group is `group` consecutive
- *    weights along k; k must be a multiple of 64 for every codec.
+ *    weights along k; k must be a multiple of 64 for every codec in the
+ *    quantize, dequant and matrix calls (the SIGNMAG8 fits need 32).
  *  - Preconditions that are not checked: finite inputs; buffers contiguous,
  *    of the sizes stated, and not overlapping one another.
  *
@@ -69,8 +71,8 @@ extern "C" {
 typedef enum {
   W4_OK = 0,
   W4_EINVAL = 1,       /* NULL pointer for a non-empty buffer, bad enum, negative size */
-  W4_ESHAPE = 2,       /* k not a multiple of 64, m outside the call's range, k above
-                          W4_MAX_MATMUL_K for w4_gemv / w4_gemm / the batched GEMV     */
+  W4_ESHAPE = 2,       /* k not a multiple of the call's group, m outside the call's
+                          range, or a size above the call's stated limit               */
   W4_EALIGN = 3,       /* a pointer not aligned as the call states                      */
   W4_EUNSUPPORTED = 4, /* a codec / dtype combination the call does not provide         */
   W4_EHIP = 5          /* the kernel launch failed (hipGetLastError)                    */
@@ -102,7 +104,8 @@ typedef enum { W4_F32 = 0, W4_BF16 = 1, W4_F16 = 2 } w4_dtype;
 /* Human-readable name of a status code (static string, never NULL). */
 const char* w4_status_str(int32_t status);
 
-/* Weights per group of a codec: 64 (DYADIC, LUT16), 32 (SIGNMAG8); -1 if unknown. */
+/* Weights per group of a codec: 64 (DYADIC, LUT16, LUT16S, DYADIC5), 32 (SIGNMAG8);
+ * -1 if unknown. */
 int32_t w4_group_size(int32_t codec);
 
 /*

@@ -88,7 +88,7 @@ const char* w4_status_str(int32_t status) {
   switch (status) {
     case W4_OK: return "W4_OK";
     case W4_EINVAL: return "W4_EINVAL: null pointer, bad enum or negative size";
-    case W4_ESHAPE: return "W4_ESHAPE: k not a multiple of 64 or m out of range";
+    case W4_ESHAPE: return "W4_ESHAPE: k not a multiple of the group, m out of range, or too large";
     case W4_EALIGN: return "W4_EALIGN: pointer not aligned as required";
     case W4_EUNSUPPORTED: return "W4_EUNSUPPORTED: codec / dtype combination not provided";
     case W4_EHIP: return "W4_EHIP: kernel launch failed";

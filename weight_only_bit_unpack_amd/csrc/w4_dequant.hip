@@ -3,8 +3,8 @@
 // DyadicGumbel page, section 2.5: the unpack kernel loads a packed byte,
 // splits the nibbles, looks up the step and rebuilds bf16 (there: 1024
 // elements per program, one launch per layer).  k-means page, section 2.2:
-// decode by table lookup (LUT16, and LUT16S with one table for every group).  int4-g32 page, section 2: (level table, sign) per
-// group -> dense fp16 weight.
+// decode by table lookup (LUT16, and LUT16S with one table for every group).
+// int4-g32 page, section 2: (level table, sign) per group -> dense fp16 weight.
 //
 // One thread rebuilds 16 packed bytes (32 weights): a 16-byte load and four
 // 16-byte stores, so a wave moves 1 KiB in and 4 KiB out with full lines.

@@ -327,6 +327,24 @@ def main():
         rows["gemv_m1_stack_per_call"] = {"ms": ms_pc, "GB/s": gemv_bytes / (ms_pc * 1e-3) / 1e9,
                                           "launches": len(shapes)}
 
+        # the same 168 launches captured once into a HIP graph and replayed
+        cap = torch.cuda.Stream()
+        with torch.cuda.stream(cap):
+            for m in mats:
+                w4.w4_gemv(m["packed"], m["x"], w4.W4_DYADIC, scales=m["scales"], y=m["y"],
+                           stream=cap)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=cap):
+            for m in mats:
+                w4.w4_gemv(m["packed"], m["x"], w4.W4_DYADIC, scales=m["scales"], y=m["y"],
+                           stream=cap)
+        ms_g = timed(graph.replay, stream, max(3, args.steps // 4), 2)
+        rows["gemv_m1_stack_per_call_graph"] = {"ms": ms_g,
+                                                "GB/s": gemv_bytes / (ms_g * 1e-3) / 1e9,
+                                                "launches": len(shapes)}
+        del graph
+
         # quantize_pack and unpack_dequant over the stack
         q_bytes = sum(2 * n * k + n * k // 2 + 2 * n * (k // 64) for n, k in shapes)
 

@@ -274,6 +274,10 @@ w4_status w4_gemv(int32_t codec, int64_t n, int64_t k, const uint8_t* packed,
  * such buffer per (device, stream), grown on demand with hipMalloc (growing
  * waits for the stream and frees the old buffer) and never freed, so calls on
  * one stream are ordered and calls on different streams never share it.
+ * Graph capture: a call that would create or grow the buffer cannot be
+ * captured (hipMalloc); make one call of the largest size on the capture
+ * stream before capturing.  After that, calls only enqueue kernels (no
+ * memset, no allocation).
  * Additional error: W4_EHIP when the workspace cannot be allocated.
  */
 w4_status w4_gemm(int32_t codec, int64_t n, int64_t k, const uint8_t* packed,

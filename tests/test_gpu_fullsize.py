@@ -19,7 +19,7 @@ import pytest
 import torch
 
 import synthetic
-from oracle import bits, lut16, matmul, native, packing, signmag8
+from oracle import bits, dyadic5, lut16, matmul, native, packing, signmag8
 from tests.gpu_util import dev_bf16, dev_f16, dev_u8, host_bits, host_f32, host_u8, report
 
 pytestmark = pytest.mark.gpu
@@ -103,6 +103,39 @@ def test_fullsize_decode_stack_batched_gemv(w4):
         probs.append({"packed": p, "scales": s, "x": x, "y": y})
         checks.append((rows, w_hat))
     batch = w4.w4_gemv_batched_plan(probs, w4.W4_DYADIC)
+    batch()
+    torch.cuda.synchronize()
+    for pr, (rows, w_hat) in zip(probs, checks):
+        _check_outputs(pr["y"], rows, host_bits(pr["x"]), w_hat)
+
+
+# ------------------------------------------------------------ the 1B stack as DYADIC5
+def test_fullsize_dyadic5_stack_batched(w4):
+    """The 168 decode-stack matrices quantized to W4_DYADIC5 with a random
+    width of 3, 4 or 5 bits per group (as bench.py draws them): both index
+    planes and the scales bit-exact on sampled rows, then the one batched
+    m = 1 launch."""
+    shapes = synthetic.llama1b_stack_shapes()
+    report("fullsize_dyadic5_stack", matrices=len(shapes))
+    gen = torch.Generator(device="cuda").manual_seed(synthetic.seed(7, 0, 0))
+    probs, checks = [], []
+    for i, (n, k) in enumerate(shapes):
+        w = synthetic.student_t_bf16_device((n, k), 4, 0.02, synthetic.seed(2, i, 0))
+        wd = torch.randint(3, 6, (n, k // 64), dtype=torch.uint8, device="cuda", generator=gen)
+        p, msb, s = w4.w4_quantize_dyadic5(w, wd)
+        rows = _rows(n, 7900 + i, count=8)
+        sel = torch.as_tensor(rows, device="cuda")
+        idx5, s_o = dyadic5.quantize(_host_rows(w, rows), host_u8(wd.index_select(0, sel)))
+        nib, hi = dyadic5.planes(idx5)
+        assert np.array_equal(_host_rows(s, rows), s_o)
+        assert np.array_equal(host_u8(p.index_select(0, sel)), nib)
+        assert np.array_equal(host_u8(msb.index_select(0, sel)), hi)
+        del w, wd
+        x = synthetic.normal_bf16_device((1, k), 1.0, synthetic.seed(2, i, 1))
+        y = torch.full((1, n), float("nan"), device="cuda")
+        probs.append({"packed": p, "codebook": msb, "scales": s, "x": x, "y": y})
+        checks.append((rows, bits.bf16_to_f64(dyadic5.dequant_from_indices(idx5, s_o))))
+    batch = w4.w4_gemv_batched_plan(probs, w4.W4_DYADIC5)
     batch()
     torch.cuda.synchronize()
     for pr, (rows, w_hat) in zip(probs, checks):

@@ -6,77 +6,88 @@
 // decode by table lookup (LUT16, and LUT16S with one table for every group).
 // int4-g32 page, section 2: (level table, sign) per group -> dense fp16 weight.
 //
-// One thread rebuilds 16 packed bytes (32 weights): a 16-byte load and four
-// 16-byte stores, so a wave moves 1 KiB in and 4 KiB out with full lines.
-// 32 weights are half a 64-group (one scale / one LUT) or one 32-group.
+// One thread rebuilds four packed dwords (8 weights each), 64 dwords apart,
+// so that each of a wave's loads and stores covers whole lines (below).
 #include "w4_device.h"
 #include "w4_launch.h"
 
 namespace w4 {
 namespace {
 
-__global__ __launch_bounds__(256) void dequant_dyadic_kernel(const u32x4* __restrict__ packed,
+// Packed dword d of the flat weight holds weights 8d .. 8d+7 (one 16-byte
+// output chunk).  A wave takes 256 consecutive dwords; lane l rebuilds dwords
+// 64 i + l (i = 0..3), so every load instruction reads 256 contiguous bytes
+// and every store instruction writes 1 KiB of whole 128-byte lines.  (Four
+// chunks of one lane side by side would make each store instruction write a
+// quarter of every line it touches; with streaming stores the partial lines
+// go to memory one by one, at half the bandwidth or less.)
+__device__ __forceinline__ int64_t wave_dword(int i) {
+  return ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 256 + 64 * i + (threadIdx.x & 63);
+}
+
+__global__ __launch_bounds__(256) void dequant_dyadic_kernel(const uint32_t* __restrict__ packed,
                                                              const uint16_t* __restrict__ scales,
-                                                             u32x4* __restrict__ out,
-                                                             int64_t nchunks) {
-  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const bool live = c < nchunks;
-  u32x4 p = {0u, 0u, 0u, 0u};
-  uint32_t sb = 0;
-  if (live) {
-    p = __builtin_nontemporal_load(&packed[c]);
-    sb = scales[c >> 1];
-  }
-  const DyadicScale d = dyadic_scale(sb);
-  const uint32_t m0 = 0x000F000Fu, m1 = 0x00F000F0u, mg = kMagic;
-  const uint32_t pw[4] = {p.x, p.y, p.z, p.w};
-  u32x4 o[4];
-  if (__builtin_expect(__any(dyadic_scale_is_wide(sb)), 0)) {
+                                                             u32x4* __restrict__ out, int64_t ndw) {
+  uint32_t pw[4], sb[4];
+  bool wide = false;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = sigma_to_natural(dyadic_rebuild_wide(pw[i], d, m0, m1, mg));
+  for (int i = 0; i < 4; ++i) {
+    const int64_t d = wave_dword(i);
+    const bool live = d < ndw;
+    pw[i] = live ? __builtin_nontemporal_load(&packed[d]) : 0u;
+    sb[i] = live ? scales[d >> 3] : 0u;  // 8 dwords per group of 64
+    wide |= dyadic_scale_is_wide(sb[i]);
+  }
+  const uint32_t m0 = 0x000F000Fu, m1 = 0x00F000F0u, mg = kMagic;
+  u32x4 o[4];
+  if (__builtin_expect(__any(wide), 0)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      o[i] = sigma_to_natural(dyadic_rebuild_wide(pw[i], dyadic_scale(sb[i]), m0, m1, mg));
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = sigma_to_natural(dyadic_rebuild(pw[i], d, m0, m1, mg));
+    for (int i = 0; i < 4; ++i)
+      o[i] = sigma_to_natural(dyadic_rebuild(pw[i], dyadic_scale(sb[i]), m0, m1, mg));
   }
-  if (live) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) __builtin_nontemporal_store(o[i], &out[4 * c + i]);
+  for (int i = 0; i < 4; ++i) {
+    const int64_t d = wave_dword(i);
+    if (d < ndw) __builtin_nontemporal_store(o[i], &out[d]);
   }
 }
 
 // shared: one table for every group (LUT16S)
-__global__ __launch_bounds__(256) void dequant_lut16_kernel(const u32x4* __restrict__ packed,
+__global__ __launch_bounds__(256) void dequant_lut16_kernel(const uint32_t* __restrict__ packed,
                                                             const uint16_t* __restrict__ scales,
                                                             const u32x4* __restrict__ lut,
-                                                            u32x4* __restrict__ out,
-                                                            int64_t nchunks, int shared) {
-  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (c >= nchunks) return;
-  const int64_t g = c >> 1, gt = shared ? 0 : g;
-  const u32x4 p = __builtin_nontemporal_load(&packed[c]);
-  const Lut16Table t = lut16_table(scales[g], lut[2 * gt], lut[2 * gt + 1]);
-  const uint32_t pw[4] = {p.x, p.y, p.z, p.w};
+                                                            u32x4* __restrict__ out, int64_t ndw,
+                                                            int shared) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    __builtin_nontemporal_store(sigma_to_natural(lut16_rebuild(pw[i], t)), &out[4 * c + i]);
+  for (int i = 0; i < 4; ++i) {
+    const int64_t d = wave_dword(i);
+    if (d < ndw) {
+      const int64_t g = d >> 3, gt = shared ? 0 : g;
+      const uint32_t p = __builtin_nontemporal_load(&packed[d]);
+      const Lut16Table t = lut16_table(scales[g], lut[2 * gt], lut[2 * gt + 1]);
+      __builtin_nontemporal_store(sigma_to_natural(lut16_rebuild(p, t)), &out[d]);
+    }
+  }
 }
 
 // fp16 output: bytes of +-M[mag] straight from an 8-entry byte-plane table.
-__global__ __launch_bounds__(256) void dequant_signmag8_kernel(const u32x4* __restrict__ packed,
+__global__ __launch_bounds__(256) void dequant_signmag8_kernel(const uint32_t* __restrict__ packed,
                                                                const u32x4* __restrict__ cb,
                                                                u32x4* __restrict__ out,
-                                                               int64_t nchunks) {
-  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (c >= nchunks) return;
-  const u32x4 p = __builtin_nontemporal_load(&packed[c]);
-  const u32x4 m = cb[c];
-  // byte planes of the 8 fp16 magnitudes
-  const uint32_t tl0 = perm(m.y, m.x, 0x06040200u), tl1 = perm(m.w, m.z, 0x06040200u);
-  const uint32_t th0 = perm(m.y, m.x, 0x07050301u), th1 = perm(m.w, m.z, 0x07050301u);
-  const uint32_t pw[4] = {p.x, p.y, p.z, p.w};
+                                                               int64_t ndw) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t w = pw[i];
+    const int64_t d = wave_dword(i);
+    if (d >= ndw) continue;
+    const uint32_t w = __builtin_nontemporal_load(&packed[d]);
+    const u32x4 m = cb[d >> 2];  // 4 dwords per group of 32
+    // byte planes of the 8 fp16 magnitudes
+    const uint32_t tl0 = perm(m.y, m.x, 0x06040200u), tl1 = perm(m.w, m.z, 0x06040200u);
+    const uint32_t th0 = perm(m.y, m.x, 0x07050301u), th1 = perm(m.w, m.z, 0x07050301u);
     const uint32_t q = w & 0x07070707u, r = (w >> 4) & 0x07070707u;
     const uint32_t ql = perm(tl1, tl0, q), qh = perm(th1, th0, q) ^ ((w << 4) & 0x80808080u);
     const uint32_t rl = perm(tl1, tl0, r), rh = perm(th1, th0, r) ^ (w & 0x80808080u);
@@ -89,7 +100,7 @@ __global__ __launch_bounds__(256) void dequant_signmag8_kernel(const u32x4* __re
     o.y = perm(r0, q0, 0x07060302u);  // (k2, k3)
     o.z = perm(r1, q1, 0x05040100u);  // (k4, k5)
     o.w = perm(r1, q1, 0x07060302u);  // (k6, k7)
-    __builtin_nontemporal_store(o, &out[4 * c + i]);
+    __builtin_nontemporal_store(o, &out[d]);
   }
 }
 
@@ -100,28 +111,33 @@ __device__ __forceinline__ float opaque_pz() {
   return __builtin_bit_cast(float, v);
 }
 
-// DYADIC5: one thread per run of 32 weights: 16 packed bytes, the run's
-// high-bit word and the group scale -> four 16-byte stores.
-__global__ __launch_bounds__(256) void dequant_dyadic5_kernel(const u32x4* __restrict__ packed,
+// DYADIC5: dword d is dword d % 4 of the run of 32 weights d / 4, whose
+// high-bit word is msb[d / 4]; d % 4 is the lane's own lane % 4 for every i.
+__global__ __launch_bounds__(256) void dequant_dyadic5_kernel(const uint32_t* __restrict__ packed,
                                                               const uint32_t* __restrict__ msb,
                                                               const uint16_t* __restrict__ scales,
                                                               u32x4* __restrict__ out,
-                                                              int64_t nruns) {
-  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (c >= nruns) return;
-  const u32x4 p = __builtin_nontemporal_load(&packed[c]);
-  const uint32_t M = msb[c];
-  const Dyadic5Scale d = dyadic5_scale(scales[c >> 1]);
+                                                              int64_t ndw) {
   const float pz = opaque_pz();
-  uint32_t e0, e1;
-  dyadic5_msb<0>(M, e0, e1);
-  __builtin_nontemporal_store(sigma_to_natural(dyadic5_rebuild(p.x, e0, e1, d, pz)), &out[4 * c]);
-  dyadic5_msb<1>(M, e0, e1);
-  __builtin_nontemporal_store(sigma_to_natural(dyadic5_rebuild(p.y, e0, e1, d, pz)), &out[4 * c + 1]);
-  dyadic5_msb<2>(M, e0, e1);
-  __builtin_nontemporal_store(sigma_to_natural(dyadic5_rebuild(p.z, e0, e1, d, pz)), &out[4 * c + 2]);
-  dyadic5_msb<3>(M, e0, e1);
-  __builtin_nontemporal_store(sigma_to_natural(dyadic5_rebuild(p.w, e0, e1, d, pz)), &out[4 * c + 3]);
+  const int D = threadIdx.x & 3;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t d = wave_dword(i);
+    if (d >= ndw) continue;
+    const uint32_t p = __builtin_nontemporal_load(&packed[d]);
+    const uint32_t M = msb[d >> 2];
+    const Dyadic5Scale sc = dyadic5_scale(scales[d >> 3]);
+    uint32_t e0, e1;
+    if (D == 0)
+      dyadic5_msb<0>(M, e0, e1);
+    else if (D == 1)
+      dyadic5_msb<1>(M, e0, e1);
+    else if (D == 2)
+      dyadic5_msb<2>(M, e0, e1);
+    else
+      dyadic5_msb<3>(M, e0, e1);
+    __builtin_nontemporal_store(sigma_to_natural(dyadic5_rebuild(p, e0, e1, sc, pz)), &out[d]);
+  }
 }
 
 }  // namespace
@@ -129,21 +145,21 @@ __global__ __launch_bounds__(256) void dequant_dyadic5_kernel(const u32x4* __res
 hipError_t launch_dequant(int codec, int64_t n, int64_t k, const uint8_t* packed,
                           const uint16_t* scales, const uint16_t* codebook, void* out,
                           hipStream_t stream) {
-  const int64_t nchunks = n * k / 32;
-  const int64_t blocks = (nchunks + 255) / 256;
-  const auto* pk = reinterpret_cast<const u32x4*>(packed);
+  const int64_t ndw = n * k / 8;                 // packed dwords = 16-byte output chunks
+  const int64_t blocks = (ndw + 1023) / 1024;   // 4 waves x 256 dwords
+  const auto* pk = reinterpret_cast<const uint32_t*>(packed);
   auto* o = reinterpret_cast<u32x4*>(out);
   if (codec == 0)
-    dequant_dyadic_kernel<<<dim3((uint32_t)blocks), dim3(256), 0, stream>>>(pk, scales, o, nchunks);
+    dequant_dyadic_kernel<<<dim3((uint32_t)blocks), dim3(256), 0, stream>>>(pk, scales, o, ndw);
   else if (codec == 1 || codec == 3)
     dequant_lut16_kernel<<<dim3((uint32_t)blocks), dim3(256), 0, stream>>>(
-        pk, scales, reinterpret_cast<const u32x4*>(codebook), o, nchunks, codec == 3);
+        pk, scales, reinterpret_cast<const u32x4*>(codebook), o, ndw, codec == 3);
   else if (codec == 4)
     dequant_dyadic5_kernel<<<dim3((uint32_t)blocks), dim3(256), 0, stream>>>(
-        pk, reinterpret_cast<const uint32_t*>(codebook), scales, o, nchunks);  // chunk = run of 32
+        pk, reinterpret_cast<const uint32_t*>(codebook), scales, o, ndw);
   else
     dequant_signmag8_kernel<<<dim3((uint32_t)blocks), dim3(256), 0, stream>>>(
-        pk, reinterpret_cast<const u32x4*>(codebook), o, nchunks);
+        pk, reinterpret_cast<const u32x4*>(codebook), o, ndw);
   return hipGetLastError();
 }
 

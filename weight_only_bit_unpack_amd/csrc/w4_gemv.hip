@@ -44,6 +44,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_
                                            0x00020000);
 }
 constexpr uint32_t kOOB = 0x80000000u;  // an offset past every slice
+// Cache policy of the packed-weight loads: nontemporal.  Every packed byte is
+// read once per launch; streaming it leaves the caches to the scales and
+// tables, which neighbouring lanes and steps read again (measured on the 1B
+// decode stack: 3-4% faster; the same policy on the scale loads is slower).
+constexpr int kPackedPolicy = 2;
 
 // Offsets pass through an empty asm so the compiler keeps the select as one
 // v_cndmask instead of splitting the loads into branches (which would make it
@@ -102,8 +107,8 @@ struct Raw<0> {  // DYADIC: one bf16 scale per 64-group
   uint16_t sb;
   __device__ __forceinline__ void fetch(const Slice& S, const LaneBase& L, uint32_t sp,
                                         uint32_t ss) {
-    a0 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, L.pa + sp, 0, 0);
-    a1 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, L.pb + sp, 0, 0);
+    a0 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, L.pa + sp, 0, kPackedPolicy);
+    a1 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, L.pb + sp, 0, kPackedPolicy);
     sb = __builtin_amdgcn_raw_buffer_load_b16(S.side, L.s + ss, 0, 0);
   }
   template <typename F>
@@ -130,8 +135,8 @@ struct Raw<1> {  // LUT16: 16 bf16 levels (side) + bf16 scale (side2) per 64-gro
   uint16_t sb;
   __device__ __forceinline__ void fetch(const Slice& S, const LaneBase& L, uint32_t sp,
                                         uint32_t ss) {
-    a0 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, L.pa + sp, 0, 0);
-    a1 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, L.pb + sp, 0, 0);
+    a0 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, L.pa + sp, 0, kPackedPolicy);
+    a1 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, L.pb + sp, 0, kPackedPolicy);
     const uint32_t loff = L.s + ss;
     l0 = __builtin_amdgcn_raw_buffer_load_b128(S.side, loff, 0, 0);
     l1 = __builtin_amdgcn_raw_buffer_load_b128(S.side, loff + 16, 0, 0);
@@ -155,8 +160,8 @@ struct Raw<2> {  // SIGNMAG8: two 32-groups, 8 fp16 magnitudes each
   u32x4 a0, a1, c0, c1;
   __device__ __forceinline__ void fetch(const Slice& S, const LaneBase& L, uint32_t sp,
                                         uint32_t ss) {
-    a0 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, L.pa + sp, 0, 0);
-    a1 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, L.pb + sp, 0, 0);
+    a0 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, L.pa + sp, 0, kPackedPolicy);
+    a1 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, L.pb + sp, 0, kPackedPolicy);
     const uint32_t coff = L.s + ss;
     c0 = __builtin_amdgcn_raw_buffer_load_b128(S.side, coff, 0, 0);
     c1 = __builtin_amdgcn_raw_buffer_load_b128(S.side, coff + 16, 0, 0);
@@ -184,8 +189,8 @@ struct Raw<3> {  // LUT16S: one bf16 scale per 64-group (side); levels shared
   uint16_t sb;
   __device__ __forceinline__ void fetch(const Slice& S, const LaneBase& L, uint32_t sp,
                                         uint32_t ss) {
-    a0 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, L.pa + sp, 0, 0);
-    a1 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, L.pb + sp, 0, 0);
+    a0 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, L.pa + sp, 0, kPackedPolicy);
+    a1 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, L.pb + sp, 0, kPackedPolicy);
     sb = __builtin_amdgcn_raw_buffer_load_b16(S.side, L.s + ss, 0, 0);
   }
   template <typename F>
@@ -207,8 +212,8 @@ struct Raw<4> {  // DYADIC5: bf16 scale per 64-group (side) + high-bit words (si
   uint16_t sb;
   __device__ __forceinline__ void fetch(const Slice& S, const LaneBase& L, uint32_t sp,
                                         uint32_t ss) {
-    a0 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, L.pa + sp, 0, 0);
-    a1 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, L.pb + sp, 0, 0);
+    a0 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, L.pa + sp, 0, kPackedPolicy);
+    a1 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, L.pb + sp, 0, kPackedPolicy);
     sb = __builtin_amdgcn_raw_buffer_load_b16(S.side, L.s + ss, 0, 0);
     // 8 high-bit bytes per lane per step: offset step = 4 x the scale step
     const auto h = __builtin_amdgcn_raw_buffer_load_b64(S.side2, L.s2 + (ss == kOOB ? kOOB : 4 * ss),

@@ -63,6 +63,28 @@ def test_dyadic_quantize_pack_bitexact(w4, n, k):
         assert np.array_equal(host_u8(p), p2) and np.array_equal(host_bits(s), s2)
 
 
+def test_dyadic_quantize_exhaustive_values(w4):
+    """Every finite bf16 value of magnitude <= s, both signs, in groups whose
+    absmax is s, for scales with plain, full and sparse mantissas, the
+    smallest subnormal and normal, the largest finite value and huge and tiny
+    exponents: indices and scales bit-exact against the oracle (which the CPU
+    tests pin to exact-rational argmin)."""
+    report("dyadic_quantize_exhaustive")
+    allpos = np.arange(0x0000, 0x7F80, dtype=np.uint32)          # +0 .. max finite
+    for sb in (0x3F80, 0x3FFF, 0x3C23, 0x3A5B, 0x0001, 0x0080, 0x00FF, 0x7F7F, 0x7A01, 0x0400):
+        vals = allpos[allpos <= sb].astype(np.uint16)
+        vals = np.concatenate([vals, vals | 0x8000])
+        pad = (-len(vals)) % 63
+        vals = np.concatenate([vals, np.zeros(pad, np.uint16)]).reshape(-1, 63)
+        w = np.concatenate([np.full((vals.shape[0], 1), sb, np.uint16), vals], axis=1)
+        w = np.ascontiguousarray(w)
+        p, s = w4.w4_quantize_pack(dev_bf16(w), w4.W4_DYADIC)
+        torch.cuda.synchronize()
+        idx_o, s_o = native.dyadic_quantize(w)
+        assert np.array_equal(host_bits(s), s_o), hex(sb)
+        assert np.array_equal(host_u8(p), packing.pack(idx_o)), hex(sb)
+
+
 @pytest.mark.parametrize("n,k", [(2048, 2048), (37, 320), (6, 128)])
 def test_dyadic_dequant_bitexact(w4, n, k):
     report("dyadic_dequant", n=n, k=k)

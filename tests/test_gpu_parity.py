@@ -85,6 +85,90 @@ def test_dyadic_quantize_exhaustive_values(w4):
         assert np.array_equal(host_u8(p), packing.pack(idx_o)), hex(sb)
 
 
+def _groups_with_absmax(sb, cols):
+    """Every finite bf16 value of magnitude <= sb (both signs), cols - 1 per
+    row after a leading sb, so that every row's absmax is sb."""
+    allpos = np.arange(0x0000, 0x7F80, dtype=np.uint32)
+    vals = allpos[allpos <= sb].astype(np.uint16)
+    vals = np.concatenate([vals, vals | 0x8000])
+    pad = (-len(vals)) % (cols - 1)
+    vals = np.concatenate([vals, np.zeros(pad, np.uint16)]).reshape(-1, cols - 1)
+    return np.ascontiguousarray(
+        np.concatenate([np.full((vals.shape[0], 1), sb, np.uint16), vals], axis=1))
+
+
+def _all_finite_bf16(cols):
+    v = np.arange(0x0000, 0x7F80, dtype=np.uint32).astype(np.uint16)
+    v = np.concatenate([v, v | 0x8000])
+    pad = (-len(v)) % cols
+    return np.ascontiguousarray(np.concatenate([v, np.zeros(pad, np.uint16)]).reshape(-1, cols))
+
+
+def test_dyadic5_quantize_exhaustive_values(w4):
+    """DYADIC5 at widths 3, 4 and 5: every finite bf16 value of magnitude <= s
+    in groups of absmax s, for the same kinds of scales as the 4-bit test."""
+    report("dyadic5_quantize_exhaustive")
+    for sb in (0x3F80, 0x3FFF, 0x3C23, 0x0001, 0x0080, 0x7F7F, 0x7A01):
+        w = _groups_with_absmax(sb, 64)
+        widths = np.resize(np.array([3, 4, 5], np.uint8), (w.shape[0], 1))
+        p, m, s = w4.w4_quantize_dyadic5(dev_bf16(w), dev_u8(widths))
+        torch.cuda.synchronize()
+        idx5, s_o = dyadic5.quantize(w, widths)
+        nib, hi = dyadic5.planes(idx5)
+        assert np.array_equal(host_bits(s), s_o), hex(sb)
+        assert np.array_equal(host_u8(p), nib), hex(sb)
+        assert np.array_equal(host_u8(m), hi), hex(sb)
+
+
+def test_lut16_quantize_exhaustive_values(w4):
+    """LUT16 and LUT16S nearest level (fp32 decision): every finite bf16
+    weight against tables under scales from the smallest subnormal to the
+    largest finite bf16 (where |w - s L| overflows fp32 on both sides)."""
+    report("lut16_quantize_exhaustive")
+    w = _all_finite_bf16(64)
+    g = np.random.default_rng(71)
+    for sb in (0x3F80, 0x7F7F, 0x0001, 0x3C23):
+        L = bits.rne_bf16(np.sort(g.uniform(-1, 1, (w.shape[0], 16)), axis=-1))
+        L[:, 0] = 0xBF80          # -1
+        L[:, 15] = 0x3F80         # +1
+        L[::7, 3:5] = 0x0000      # duplicated levels
+        s = np.full((w.shape[0], 1), sb, np.uint16)
+        L3 = np.ascontiguousarray(L.reshape(w.shape[0], 1, 16))
+        p, _ = w4.w4_quantize_pack(dev_bf16(w), w4.W4_LUT16, scales=dev_bf16(s), codebook=dev_bf16(L3))
+        torch.cuda.synchronize()
+        assert np.array_equal(host_u8(p), packing.pack(native.lut16_indices(w, s, L))), hex(sb)
+        T = L[5]
+        p, _ = w4.w4_quantize_pack(dev_bf16(w), w4.W4_LUT16S, scales=dev_bf16(s), codebook=dev_bf16(T))
+        torch.cuda.synchronize()
+        tables = np.ascontiguousarray(np.broadcast_to(T, L.shape))
+        assert np.array_equal(host_u8(p), packing.pack(native.lut16_indices(w, s, tables))), hex(sb)
+
+
+def test_signmag8_quantize_exhaustive_values(w4):
+    """SIGNMAG8 sign + nearest magnitude (fp32 decision): every finite bf16
+    weight against codebooks with subnormal, duplicated, zero and maximal
+    (65504) fp16 magnitudes."""
+    report("signmag8_quantize_exhaustive")
+    w = _all_finite_bf16(64)
+    ng = 2 * w.shape[0]  # groups of 32
+    g = np.random.default_rng(72)
+    for kind in range(3):
+        if kind == 0:
+            mags = np.sort(g.uniform(0, 0.1, (ng, 8)), axis=-1)
+        elif kind == 1:
+            mags = np.sort(2.0 ** g.uniform(-26, -10, (ng, 8)), axis=-1)
+        else:
+            mags = np.sort(g.uniform(0, 65504, (ng, 8)), axis=-1)
+            mags[:, 7] = 65504.0
+        cb = bits.rne_fp16(mags)
+        cb[::5, 2] = cb[::5, 1]   # a duplicated level
+        cb[::3, 0] = 0
+        cb = np.ascontiguousarray(cb.reshape(w.shape[0], 2, 8))
+        p, _ = w4.w4_quantize_pack(dev_bf16(w), w4.W4_SIGNMAG8, codebook=dev_f16(cb))
+        torch.cuda.synchronize()
+        assert np.array_equal(host_u8(p), packing.pack(native.signmag8_indices(w, cb))), kind
+
+
 @pytest.mark.parametrize("n,k", [(2048, 2048), (37, 320), (6, 128)])
 def test_dyadic_dequant_bitexact(w4, n, k):
     report("dyadic_dequant", n=n, k=k)

@@ -144,6 +144,32 @@ def test_lut16_quantize_exhaustive_values(w4):
         assert np.array_equal(host_u8(p), packing.pack(native.lut16_indices(w, s, tables))), hex(sb)
 
 
+def test_lut16_dequant_extreme_scales_and_tables(w4):
+    """RNE_bf16(s * L) for every index, tables with entries beyond [-1, 1]
+    (the call takes any finite bf16 table), signed zeros and subnormals,
+    under scales from the smallest subnormal to the largest finite bf16
+    (products that overflow to +-inf, round to the largest finite value or
+    underflow): LUT16 and LUT16S against the oracle, bit for bit."""
+    report("lut16_dequant_extreme")
+    g = np.random.default_rng(73)
+    scales = np.array([0x0001, 0x0080, 0x3F80, 0x7F7F, 0x7F00, 0x4000, 0x00FF, 0x3C23], np.uint16)
+    G = 64 * len(scales)
+    idx = np.tile(np.arange(16, dtype=np.uint8), 4)[None, :].repeat(G, axis=0)   # [G, 64]
+    L = g.choice(np.array([0x3F80, 0xBF80, 0x4000, 0xC0F0, 0x0000, 0x8000, 0x0001, 0x8040,
+                           0x3F7F, 0x3FFF, 0x7F7F, 0x0080], np.uint16), size=(G, 1, 16))
+    L[:, 0, 5] = bits.rne_bf16(g.uniform(-4, 4, G))
+    s = np.repeat(scales, 64)[:, None].astype(np.uint16)
+    pk = dev_u8(packing.pack(idx))
+    out = w4.w4_unpack_dequant(pk, w4.W4_LUT16, scales=dev_bf16(s), codebook=dev_bf16(L))
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(out), lut16.dequant_from_indices(idx, s, L))
+    T = np.ascontiguousarray(L[7, 0])
+    out = w4.w4_unpack_dequant(pk, w4.W4_LUT16S, scales=dev_bf16(s), codebook=dev_bf16(T))
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(out), lut16.dequant_from_indices(
+        idx, s, np.ascontiguousarray(np.broadcast_to(T, L.shape))))
+
+
 def test_signmag8_quantize_exhaustive_values(w4):
     """SIGNMAG8 sign + nearest magnitude (fp32 decision): every finite bf16
     weight against codebooks with subnormal, duplicated, zero and maximal

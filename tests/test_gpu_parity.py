@@ -270,6 +270,67 @@ def test_dyadic_gemv_unit_vectors_exact(w4):
     assert torch.count_nonzero(z).item() == 0
 
 
+_EXTREME_SCALES = np.array([0x0001, 0x0080, 0x00FF, 0x3C23, 0x3F80, 0x4000, 0x7E55, 0x7F7F],
+                           np.uint16)
+
+
+def _extreme_codec_case(codec, n, k, seed):
+    """Random indices with side data at the extremes of bf16 / fp16 (scales
+    from the smallest subnormal to the largest finite bf16, table entries at
+    +-1, +-0 and subnormal, magnitudes up to 65504): (packed, side tables,
+    fp64 dequantized weight).  Every dequantized value is finite."""
+    g = np.random.default_rng(seed)
+    s = g.choice(_EXTREME_SCALES, size=(n, k // 64))
+    if codec == 0:
+        idx = g.integers(0, 16, (n, k)).astype(np.uint8)
+        return (packing.pack(idx), dict(scales=dev_bf16(s)),
+                bits.bf16_to_f64(dyadic.dequant_from_indices(idx, s)))
+    if codec in (1, 3):
+        kinds = np.array([0x3F80, 0xBF80, 0x0000, 0x8000, 0x0001, 0x8001, 0x3F7F, 0xBE00],
+                         np.uint16)
+        L = g.choice(kinds, size=(n, k // 64, 16))
+        L[..., :4] = bits.rne_bf16(g.uniform(-1, 1, (n, k // 64, 4)))
+        idx = g.integers(0, 16, (n, k)).astype(np.uint8)
+        if codec == 3:
+            T = np.ascontiguousarray(L[0, 0])
+            tables = np.ascontiguousarray(np.broadcast_to(T, L.shape))
+            return (packing.pack(idx), dict(scales=dev_bf16(s), codebook=dev_bf16(T)),
+                    bits.bf16_to_f64(lut16.dequant_from_indices(idx, s, tables)))
+        return (packing.pack(idx), dict(scales=dev_bf16(s), codebook=dev_bf16(L)),
+                bits.bf16_to_f64(lut16.dequant_from_indices(idx, s, L)))
+    if codec == 4:
+        idx5 = g.integers(0, 32, (n, k)).astype(np.uint8)
+        nib, msb = dyadic5.planes(idx5)
+        return (nib, dict(scales=dev_bf16(s), codebook=dev_u8(msb)),
+                bits.bf16_to_f64(dyadic5.dequant_from_indices(idx5, s)))
+    cb = g.choice(np.array([0x7BFF, 0x0001, 0x0000, 0x3C00, 0x03FF, 0x0400, 0x5A5A], np.uint16),
+                  size=(n, k // 32, 8))
+    nib = g.integers(0, 16, (n, k)).astype(np.uint8)
+    return packing.pack(nib), dict(codebook=dev_f16(cb)), signmag8.dequant_values(cb, nib)
+
+
+@pytest.mark.parametrize("codec", [0, 1, 2, 3, 4])
+def test_unit_vectors_extreme_side_data(w4, codec):
+    """x = rows of the identity: every output is one rebuilt weight times 1.0
+    plus products with 0, so the GEMV (m = 16) and the GEMM (m = 128) must
+    return the dequantized weights exactly, for every codec's rebuild at the
+    extremes of its side data (the matrix kernels rebuild on their own, apart
+    from the dequant kernel)."""
+    n, k = 64, 128
+    report("unit_vectors_extreme", codec=codec)
+    p, side, w_hat = _extreme_codec_case(codec, n, k, 1700 + codec)
+    pk = dev_u8(p)
+    for c0 in range(0, k, 16):
+        x = np.zeros((16, k), np.uint16)
+        x[np.arange(16), c0 + np.arange(16)] = 0x3F80
+        y = host_f32(w4.w4_gemv(pk, dev_bf16(x), codec, **side))
+        assert np.array_equal(y, w_hat[:, c0:c0 + 16].T), (codec, c0)
+    x = np.zeros((128, k), np.uint16)
+    x[np.arange(128), np.arange(128)] = 0x3F80
+    y = host_f32(w4.w4_gemm(pk, dev_bf16(x), codec, **side))
+    assert np.array_equal(y, w_hat.T), codec
+
+
 @pytest.mark.parametrize("op", ["gemv", "gemm"])
 def test_dyadic_wide_scales(w4, op):
     """Scales >= 2**120 take the wide rebuild; activations ~2**-20 keep the

@@ -52,18 +52,20 @@ __device__ __forceinline__ uint32_t dyadic_idx_exact(float w, float s16) {
 }
 
 // Same count, found from an estimate that is off by at most one and then
-// checked against the two exact midpoints around it.  Both midpoints are
-// formed from s/16 directly: the one below code 0 is -17 s/16, which exceeds
-// the fp32 range for the largest bf16 scales and becomes -inf (nothing lies
-// below it, as it should); the one above a code is at most 15 s/16 in
-// magnitude and always finite.
-__device__ __forceinline__ uint32_t dyadic_idx_fast(float w, float inv8, float s16) {
-  const float z = w * inv8;  // ~ 8 w / s, relative error ~2^-23
-  int i0 = (int)__builtin_ceilf(z + 7.5f);
-  i0 = i0 < 0 ? 0 : (i0 > 15 ? 15 : i0);
-  const float mlo = (float)(2 * i0 - 17) * s16;  // midpoint below code i0 (exact or -inf)
-  const float mhi = (float)(2 * i0 - 15) * s16;  // midpoint above code i0 (exact)
-  int i = i0 - (w <= mlo ? 1 : 0) + (w > mhi ? 1 : 0);
+// checked against the two exact midpoints around it, in fp32 throughout:
+// f0 = clamp(floor(8 w / s + 8), 0, 15) is the true count or one off; the
+// midpoints below and above code f0 are (2 f0 - 17) s/16 and (2 f0 - 15) s/16
+// (exact: at most 12 significant bits).  The one below code 0 exceeds the fp32
+// range for the largest bf16 scales and becomes -inf (nothing lies below it,
+// as it should); the one above is formed by one fma, (2 f0 - 17) s/16 + s/8,
+// whose exact result is at most 15 s/16 in magnitude and so always finite.
+__device__ __forceinline__ uint32_t dyadic_idx_fast(float w, float inv8, float s16, float s8) {
+  float f0 = __builtin_floorf(__builtin_fmaf(w, inv8, 8.0f));
+  f0 = __builtin_amdgcn_fmed3f(f0, 0.0f, 15.0f);
+  const float t = __builtin_fmaf(f0, 2.0f, -17.0f);  // 2 f0 - 17, exact
+  const float mlo = t * s16;                          // exact or -inf
+  const float mhi = __builtin_fmaf(t, s16, s8);       // exact, finite
+  const int i = (int)f0 - (w <= mlo ? 1 : 0) + (w > mhi ? 1 : 0);
   return (uint32_t)(i > 15 ? 15 : i);
 }
 
@@ -84,7 +86,7 @@ __global__ __launch_bounds__(256) void quantize_dyadic_kernel(const u32x4* __res
   a = __builtin_fmaxf(a, dpp_quad_xor2(a));
   a = __builtin_fmaxf(a, dpp_half_mirror(a));
   const float s = a;  // group absmax: a bf16 value, exact in fp32
-  const float s16 = s * 0.0625f;
+  const float s16 = s * 0.0625f, s8 = s * 0.125f;
   uint32_t word = 0x88888888u;  // all-zero group: index 8 everywhere
   const bool tiny = s < 0x1p-120f;  // 8/s would overflow: use the direct count
   if (__builtin_expect(__any(tiny && s != 0.0f), 0)) {
@@ -97,7 +99,7 @@ __global__ __launch_bounds__(256) void quantize_dyadic_kernel(const u32x4* __res
     const float inv8 = 8.0f / s;
     word = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) word |= dyadic_idx_fast(f[i], inv8, s16) << (4 * i);
+    for (int i = 0; i < 8; ++i) word |= dyadic_idx_fast(f[i], inv8, s16, s8) << (4 * i);
   }
   if (live) {
     packed[c] = word;

@@ -40,10 +40,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["headline", "gemm", "copy", "fit"], default=None,
+    ap.add_argument("--only", choices=["headline", "gemm", "copy", "fit", "codec"], default=None,
                     help="run one target only (for profiler runs): the batched decode pass, "
                          "the M=256 GEMM, a 1 GiB device copy that calibrates HBM counters, "
-                         "or the LUT16 k-means fit of the three 3.9B-sized matrices")
+                         "the table / magnitude fits, or quantize + dequant of one 8192^2 "
+                         "weight for every codec")
     ap.add_argument("--only-headline", action="store_true", help="same as --only headline")
     a = ap.parse_args()
     if a.only_headline:
@@ -262,6 +263,40 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
 
+    if args.only == "codec":
+        # quantize_pack (DYADIC) and unpack_dequant (every codec) on one
+        # 8192 x 8192 weight, N(0, 0.02^2): ms per call, read + write bytes
+        n = k = 8192
+        W = synthetic.normal_bf16_device((n, k), 0.02, synthetic.seed(5, 0, 0), dev)
+        P, S = w4.w4_quantize_pack(W, w4.W4_DYADIC)
+        ms = timed(lambda: w4.w4_quantize_pack(W, w4.W4_DYADIC, packed=P, scales=S,
+                                               stream=stream), stream, args.steps, args.warmup)
+        b = 2 * n * k + n * k // 2 + n * k // 32
+        print(json.dumps({"target": "quantize_dyadic", "ms": ms, "GB/s": b / (ms * 1e-3) / 1e9}),
+              flush=True)
+        sl, L = w4.w4_lut16_fit(W, 1)
+        PL, _ = w4.w4_quantize_pack(W, w4.W4_LUT16, scales=sl, codebook=L)
+        cb = w4.w4_signmag8_fit(W, 1)
+        P8, _ = w4.w4_quantize_pack(W, w4.W4_SIGNMAG8, codebook=cb)
+        wd = torch.full((n, k // 64), 4, dtype=torch.uint8, device=dev)
+        P5, M5, S5 = w4.w4_quantize_dyadic5(W, wd)
+        out = torch.empty((n, k), dtype=torch.bfloat16, device=dev)
+        out16 = torch.empty((n, k), dtype=torch.float16, device=dev)
+        cases = [("dequant_dyadic", lambda: w4.w4_unpack_dequant(P, w4.W4_DYADIC, scales=S, out=out,
+                                                                 stream=stream), n * k // 2 + n * k // 32),
+                 ("dequant_lut16", lambda: w4.w4_unpack_dequant(PL, w4.W4_LUT16, scales=sl, codebook=L,
+                                                                out=out, stream=stream),
+                  n * k // 2 + n * k // 32 + n * k // 2),
+                 ("dequant_signmag8", lambda: w4.w4_unpack_dequant(P8, w4.W4_SIGNMAG8, codebook=cb,
+                                                                   out=out16, stream=stream), n * k),
+                 ("dequant_dyadic5", lambda: w4.w4_unpack_dequant(P5, w4.W4_DYADIC5, scales=S5,
+                                                                  codebook=M5, out=out, stream=stream),
+                  n * k // 2 + n * k // 8 + n * k // 32)]
+        for name, fn, rb in cases:
+            ms = timed(fn, stream, args.steps, args.warmup)
+            print(json.dumps({"target": name, "ms": ms, "GB/s": (rb + 2 * n * k) / (ms * 1e-3) / 1e9}),
+                  flush=True)
+        return
     if args.only == "copy":
         # plain device copy of a known size: what FETCH_SIZE / WRITE_SIZE read
         # for it calibrates the counters (bytes per reported KiB)

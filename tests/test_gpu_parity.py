@@ -728,3 +728,31 @@ def test_gemv_batched_codecs(w4, codec, m, shapes):
         torch.cuda.synchronize()
         for pr, (x, w_hat) in zip(probs, refs):
             _gemv_check(pr["y"], x, w_hat, False)
+
+
+@pytest.mark.parametrize("m", [1, 4])
+def test_gemv_batched_many_problems(w4, m):
+    """More problems than a block's 256 threads look up in one round (the
+    block -> problem search loops), including empty ones (n = 0), whose
+    tiles are none."""
+    g = np.random.default_rng(1400 + m)
+    shapes = [(int(g.integers(1, 200)), int(g.choice([64, 128, 320]))) for _ in range(300)]
+    shapes[7] = (0, 64)
+    shapes[290] = (0, 128)
+    report("gemv_batched_many", m=m, count=len(shapes))
+    probs, refs = [], []
+    for i, (n, k) in enumerate(shapes):
+        w = synthetic.normal_bf16((max(n, 1), k), 0.02, 1500 + i)[:n]
+        x = synthetic.normal_bf16((m, k), 1.0, 1800 + i)
+        idx, s = native.dyadic_quantize(np.ascontiguousarray(w))
+        y = torch.full((m, n), float("nan"), device="cuda")
+        probs.append({"packed": dev_u8(packing.pack(idx)) if n else torch.empty((0, k // 2), dtype=torch.uint8, device="cuda"),
+                      "scales": dev_bf16(s) if n else torch.empty((0, k // 64), dtype=torch.bfloat16, device="cuda"),
+                      "x": dev_bf16(x), "y": y})
+        refs.append((x, bits.bf16_to_f64(native.dyadic_dequant(idx, s)) if n else None))
+    batch = w4.w4_gemv_batched_plan(probs, w4.W4_DYADIC)
+    batch()
+    torch.cuda.synchronize()
+    for pr, (x, w_hat) in zip(probs, refs):
+        if w_hat is not None:
+            _gemv_check(pr["y"], x, w_hat, False)

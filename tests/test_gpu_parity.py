@@ -233,10 +233,13 @@ def _gemv_check(y, x_bits, w_hat, bf16_out):
 # m > 1 on few row tiles splits k across blocks (k slices, partial sums added
 # in order by a second kernel): (37, 320, 3) has a ragged last slice, (70,
 # 49472, 16) more activations per slice than fit in LDS (chunks inside a
-# slice), (130, 2944, 7) an odd m over uneven slices.
+# slice), (130, 2944, 7) an odd m over uneven slices; (33, 65600, 1) takes k
+# in three chunks inside each block (the last one ragged), (33, 65600, 2) in
+# slices.
 @pytest.mark.parametrize("n,k,m", [(2048, 2048, 1), (37, 320, 1), (37, 320, 3), (300, 1024, 4),
                                    (300, 1024, 16), (64, 4096, 16), (40000, 128, 2),
-                                   (70000, 64, 1), (70, 49472, 16), (130, 2944, 7)])
+                                   (70000, 64, 1), (70, 49472, 16), (130, 2944, 7),
+                                   (33, 65600, 1), (33, 65600, 2)])
 @pytest.mark.parametrize("ybf16", [False, True])
 def test_dyadic_gemv(w4, n, k, m, ybf16):
     report("dyadic_gemv", n=n, k=k, m=m, ybf16=ybf16)

@@ -383,7 +383,8 @@ def test_dyadic_gemv_batched(w4):
         _gemv_check(pr["y"], x, w_hat, False)
 
 
-@pytest.mark.parametrize("n,k,m", [(200, 576, 1), (200, 576, 130), (1024, 2048, 256), (64, 64, 128)])
+@pytest.mark.parametrize("n,k,m", [(200, 576, 1), (200, 576, 130), (1024, 2048, 256), (64, 64, 128),
+                                   (100, 65600, 130)])
 def test_dyadic_gemm(w4, n, k, m):
     report("dyadic_gemm", n=n, k=k, m=m)
     w = _edge_weight(n, k, 700 + n, huge=False)

@@ -20,8 +20,9 @@
  *
  * Conventions shared by every call
  * --------------------------------
- *  - Pointers are DEVICE pointers owned by the caller; the library keeps none
- *    of them after returning.  It allocates no memory, except w4_gemm and
+ *  - Pointers are DEVICE pointers owned by the caller, all on the current
+ *    device (hipSetDevice), as is `stream`; the library keeps none of them
+ *    after returning.  It allocates no memory, except w4_gemm and
  *    w4_gemv with m >= 2, which keep a device workspace per (device, stream)
  *    for the process's life (see there).
  *  - `stream` is a hipStream_t (NULL = the null stream).  A call only enqueues

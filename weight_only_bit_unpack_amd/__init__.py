@@ -102,6 +102,9 @@ def _need(t, name, dtypes, shape=None):
         raise ValueError(f"{name} is required")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name} is on {t.device}; the library works on the current device "
+                         f"(cuda:{torch.cuda.current_device()})")
     if t.dtype not in dtypes:
         raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
     if not t.is_contiguous():

@@ -126,7 +126,8 @@ __global__ __launch_bounds__(256) void dequant_dyadic5_kernel(const uint32_t* __
     if (d >= ndw) continue;
     const uint32_t p = __builtin_nontemporal_load(&packed[d]);
     const uint32_t M = msb[d >> 2];
-    const Dyadic5Scale sc = dyadic5_scale(scales[d >> 3]);
+    const uint32_t sb = scales[d >> 3];
+    const Dyadic5Scale sc = dyadic5_scale(sb);
     uint32_t e0, e1;
     if (D == 0)
       dyadic5_msb<0>(M, e0, e1);
@@ -136,7 +137,12 @@ __global__ __launch_bounds__(256) void dequant_dyadic5_kernel(const uint32_t* __
       dyadic5_msb<2>(M, e0, e1);
     else
       dyadic5_msb<3>(M, e0, e1);
-    __builtin_nontemporal_store(sigma_to_natural(dyadic5_rebuild(p, e0, e1, sc, pz)), &out[d]);
+    u32x4 v;
+    if (__builtin_expect(__any(dyadic5_scale_is_wide(sb)), 0))
+      v = dyadic5_rebuild(p, e0, e1, sc, pz);
+    else
+      v = dyadic5_rebuild_fma(p, e0, e1, sc);
+    __builtin_nontemporal_store(sigma_to_natural(v), &out[d]);
   }
 }
 

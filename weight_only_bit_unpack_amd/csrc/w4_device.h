@@ -173,15 +173,27 @@ __device__ __forceinline__ uint32_t merge_sel(uint32_t x_shifted_by_1) {
 // products are exact in fp32 for every bf16 scale, and the conversion is the
 // one RNE.  The addend pz is +0.0f hidden from the optimiser: an exact zero
 // product then comes out +0 even for a zero scale.
+// With the offsets folded into one fma, (h - 1040) s/16 = fma(h, s/16, -1040 s/16)
+// and (h - 1280) s/256 = fma(h, s/256, -1280 s/256): the constants are exact
+// (at most 15 significant bits) unless they overflow, which needs a scale of
+// 2^120 or more (dyadic5_scale_is_wide); the fma's exact result has at most
+// 13 significant bits, so its one rounding is exact, and an exact zero comes
+// out +0 (x + (-x)).  Wide scales take the subtract-then-multiply form.
 struct Dyadic5Scale {
-  float s16, s256;
+  float s16, s256, c1, c2;
 };
 
 __device__ __forceinline__ Dyadic5Scale dyadic5_scale(uint32_t sbits) {
   Dyadic5Scale d;
   d.s16 = bf16_bits_to_f32(sbits) * 0.0625f;
   d.s256 = d.s16 * 0.0625f;
+  d.c1 = -1040.0f * d.s16;
+  d.c2 = -1280.0f * d.s256;
   return d;
+}
+
+__device__ __forceinline__ bool dyadic5_scale_is_wide(uint32_t sbits) {
+  return ((sbits >> 7) & 0xFFu) >= 247u;  // |scale| >= 2^120
 }
 
 // High bits of packed dword D (0..3) of a run of 32 weights, from the run's
@@ -205,7 +217,22 @@ __device__ __forceinline__ void dyadic5_msb(uint32_t M, uint32_t& e0, uint32_t& 
   }
 }
 
-// One packed dword + its high bits -> 8 bf16 values in SIGMA order.
+// One packed dword + its high bits -> 8 bf16 values in SIGMA order (scales
+// below 2^120).
+__device__ __forceinline__ u32x4 dyadic5_rebuild_fma(uint32_t p, uint32_t e0, uint32_t e1,
+                                                     const Dyadic5Scale& d) {
+  const uint32_t q = p >> 8;
+  const uint32_t mg = kMagic;
+  u32x4 r;
+  r.x = fma_pair(and_or(p, 0x000F000Fu, and_or(e0, 0x00100010u, mg)), d.s16, d.c1);
+  r.y = fma_pair(and_or(p, 0x00F000F0u, and_or(e0, 0x01000100u, mg)), d.s256, d.c2);
+  r.z = fma_pair(and_or(q, 0x000F000Fu, and_or(e1, 0x00100010u, mg)), d.s16, d.c1);
+  r.w = fma_pair(and_or(q, 0x00F000F0u, and_or(e1, 0x01000100u, mg)), d.s256, d.c2);
+  return r;
+}
+
+// The same for any scale: an exact fp16 subtraction, then one product and one
+// RNE per value.
 __device__ __forceinline__ u32x4 dyadic5_rebuild(uint32_t p, uint32_t e0, uint32_t e1,
                                                  const Dyadic5Scale& d, float pz) {
   const uint32_t q = p >> 8;

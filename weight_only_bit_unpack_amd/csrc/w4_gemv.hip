@@ -227,20 +227,35 @@ struct Raw<4> {  // DYADIC5: bf16 scale per 64-group (side) + high-bit words (si
     sh(a0, a1, p0, p1);
     const uint32_t pw[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
     const Dyadic5Scale d = dyadic5_scale(sb);
-    const float pz = __builtin_bit_cast(float, opaque(0u));
     uint32_t e0, e1;
+    if (__builtin_expect(__any(dyadic5_scale_is_wide(sb)), 0)) {
+      const float pz = __builtin_bit_cast(float, opaque(0u));
 #define W4_DYADIC5_STEP(J)                                         \
   dyadic5_msb<(J) & 3>((J) < 4 ? h0 : h1, e0, e1);                 \
   mma(J, dyadic5_rebuild(pw[J], e0, e1, d, pz));
-    W4_DYADIC5_STEP(0)
-    W4_DYADIC5_STEP(1)
-    W4_DYADIC5_STEP(2)
-    W4_DYADIC5_STEP(3)
-    W4_DYADIC5_STEP(4)
-    W4_DYADIC5_STEP(5)
-    W4_DYADIC5_STEP(6)
-    W4_DYADIC5_STEP(7)
+      W4_DYADIC5_STEP(0)
+      W4_DYADIC5_STEP(1)
+      W4_DYADIC5_STEP(2)
+      W4_DYADIC5_STEP(3)
+      W4_DYADIC5_STEP(4)
+      W4_DYADIC5_STEP(5)
+      W4_DYADIC5_STEP(6)
+      W4_DYADIC5_STEP(7)
 #undef W4_DYADIC5_STEP
+    } else {
+#define W4_DYADIC5_STEP(J)                                         \
+  dyadic5_msb<(J) & 3>((J) < 4 ? h0 : h1, e0, e1);                 \
+  mma(J, dyadic5_rebuild_fma(pw[J], e0, e1, d));
+      W4_DYADIC5_STEP(0)
+      W4_DYADIC5_STEP(1)
+      W4_DYADIC5_STEP(2)
+      W4_DYADIC5_STEP(3)
+      W4_DYADIC5_STEP(4)
+      W4_DYADIC5_STEP(5)
+      W4_DYADIC5_STEP(6)
+      W4_DYADIC5_STEP(7)
+#undef W4_DYADIC5_STEP
+    }
   }
 };
 

@@ -34,6 +34,7 @@
 #include "w4_device.h"
 #include "w4_launch.h"
 
+#include <atomic>
 #include <type_traits>
 
 
@@ -506,12 +507,18 @@ template <int CODEC>
 hipError_t launch_codec(const GemvProblem& p, int m, int y_bf16, const u32x4* xpk, float* partial,
                         uint32_t blocks, hipStream_t stream) {
   constexpr size_t lds = gemm_lds_bytes<CODEC>();
-  static bool configured = false;  // benign race: every caller sets the same value
-  if (!configured) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<CODEC>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  // the LDS limit is raised once per device (one bit each for the first 64);
+  // callers racing here all set the same value
+  static std::atomic<uint64_t> configured{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? uint64_t{1} << dev : 0;
+  if (!(configured.load(std::memory_order_acquire) & bit)) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<CODEC>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    configured = true;
+    configured.fetch_or(bit, std::memory_order_release);
   }
   gemm_kernel<CODEC><<<dim3(blocks), dim3(512), lds, stream>>>(p, m, y_bf16, xpk, partial);
   return hipGetLastError();

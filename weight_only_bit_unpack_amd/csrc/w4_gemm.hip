@@ -15,9 +15,11 @@
 //
 // A wave owns its batch rows, so its activation operands come straight from
 // global memory into registers, from a copy of x rewritten once per call into
-// MFMA operand order (pack_activations); only the rebuilt weights (natural k
-// order) go through LDS: 16 KB of writes and 64 KB of reads per k-step against
-// 4.2 MFLOP of MFMA work.
+// MFMA operand order (pack_activations); only the rebuilt weights go through
+// LDS: 16 KB of writes and 64 KB of reads per k-step against 4.2 MFLOP of MFMA
+// work.  Within every 8 consecutive k both operands hold their values in the
+// rebuild's slot order SIGMA (w4_device.h): the contraction only needs the two
+// sides to agree on the k order, and the weights are then stored as rebuilt.
 //
 // The k range is split over S blocks when the output tiles alone cannot fill
 // the GPU (256 x 8192 outputs are only 64 tiles); each split writes an fp32
@@ -66,7 +68,7 @@ struct RebuildConsts {
 
 // Packed bytes and side data one thread rebuilds per k-step: weight row
 // tid / 4, k = 16 (tid % 4) .. + 15 of the step (8 packed bytes).  The rebuilt
-// values go to LDS in natural k order (the activations stay as loaded).
+// values go to LDS in SIGMA order, as the activations are packed.
 template <int CODEC>
 struct WRaw;
 
@@ -87,7 +89,7 @@ struct WRaw<0> {  // DYADIC: bf16 scale of the row's 64-group
     const DyadicScale d = dyadic_scale(sb);
     const uint32_t m0 = 0x000F000Fu, m1 = 0x00F000F0u, mg = kMagic;
     const float nz = __builtin_bit_cast(float, opaque(0x80000000u));
-    hi = sigma_to_natural(dyadic_rebuild_any(D == 0 ? p0 : p1, d, m0, m1, mg, nz));
+    hi = dyadic_rebuild_any(D == 0 ? p0 : p1, d, m0, m1, mg, nz);
   }
 };
 
@@ -109,7 +111,7 @@ struct WRaw<1> {  // LUT16: 16 bf16 levels + bf16 scale of the row's 64-group
   template <int D>
   __device__ __forceinline__ void rebuild(u32x4& hi, u32x4&, const RebuildConsts&) const {
     const Lut16Table t = lut16_table(sb, l0, l1);
-    hi = sigma_to_natural(lut16_rebuild(D == 0 ? p0 : p1, t));
+    hi = lut16_rebuild(D == 0 ? p0 : p1, t);
   }
 };
 
@@ -128,10 +130,7 @@ struct WRaw<2> {  // SIGNMAG8: 8 fp16 magnitudes of the row's 32-group
   template <int D>
   __device__ __forceinline__ void rebuild(u32x4& hi, u32x4& lo, const RebuildConsts&) const {
     const SignMagTable t = signmag_table(c);
-    u32x4 h, l;
-    signmag_rebuild(D == 0 ? p0 : p1, t, h, l);
-    hi = sigma_to_natural(h);
-    lo = sigma_to_natural(l);
+    signmag_rebuild(D == 0 ? p0 : p1, t, hi, lo);
   }
 };
 
@@ -150,7 +149,7 @@ struct WRaw<3> {  // LUT16S: bf16 scale of the row's 64-group; levels shared
   template <int D>
   __device__ __forceinline__ void rebuild(u32x4& hi, u32x4&, const RebuildConsts& st) const {
     const Lut16Table t = lut16_table(sb, st.l0, st.l1);
-    hi = sigma_to_natural(lut16_rebuild(D == 0 ? p0 : p1, t));
+    hi = lut16_rebuild(D == 0 ? p0 : p1, t);
   }
 };
 
@@ -174,7 +173,7 @@ struct WRaw<4> {  // DYADIC5: bf16 scale of the row's 64-group + high-bit word o
     uint32_t e0, e1;
     dyadic5_msb<D>(h >> c.msb_shift, e0, e1);
     const float pz = __builtin_bit_cast(float, opaque(0u));
-    hi = sigma_to_natural(dyadic5_rebuild(D == 0 ? p0 : p1, e0, e1, dyadic5_scale(sb), pz));
+    hi = dyadic5_rebuild(D == 0 ? p0 : p1, e0, e1, dyadic5_scale(sb), pz);
   }
 };
 
@@ -430,7 +429,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 // Activations in MFMA operand order: for each 32-row tile R and 16-k block B
 // a 1 KB record whose lane l holds x[32 R + l % 32][16 B + 8 (l / 32) .. + 7]
-// (rows past M are zero).  The GEMM then reads every operand as 1 KB of
+// in SIGMA order (rows past M are zero).  The GEMM then reads every operand as 1 KB of
 // contiguous memory; read straight from x, each operand load would touch 32
 // rows and the L1 would stall the address path.
 __global__ __launch_bounds__(256) void pack_activations(const u32x4* __restrict__ x,
@@ -451,7 +450,7 @@ __global__ __launch_bounds__(256) void pack_activations(const u32x4* __restrict_
   }
   __syncthreads();
   const int rec = tid >> 6, lane = tid & 63;  // record rec = 16-k block 4c + rec
-  xpk[(R * kblocks + 4 * c + rec) * 64 + lane] = t[lane & 31][2 * rec + (lane >> 5)];
+  xpk[(R * kblocks + 4 * c + rec) * 64 + lane] = x_to_sigma(t[lane & 31][2 * rec + (lane >> 5)]);
 }
 
 // y = sum of the S split partials, added in split order.  One thread per

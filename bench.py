@@ -419,6 +419,16 @@ def main():
                                                   stream=stream), stream, 10, 2)
         qb = 2 * 8192 * 8192 + 8192 * 4096 + 2 * 8192 * 128
         rows["quantize_pack_8192x8192"] = {"ms": ms_q5, "GB/s": qb / (ms_q5 * 1e-3) / 1e9}
+        # the same weight at other batch sizes (M = 128 takes the 128-row block)
+        for mx in (128, 512, 1024):
+            Xm = synthetic.normal_bf16_device((mx, 8192), 1.0, synthetic.seed(5, 0, 2), dev)
+            Ym = torch.empty((mx, 8192), dtype=torch.float32, device=dev)
+            ms_m = timed(lambda: w4.w4_gemm(P, Xm, w4.W4_DYADIC, scales=S, y=Ym, stream=stream),
+                         stream, 30, 5)
+            tfm = 2 * mx * 8192 * 8192 / (ms_m * 1e-3) / 1e12
+            rows[f"gemm_m{mx}_k8192_n8192"] = {"ms": ms_m, "TFLOP/s": tfm,
+                                               "frac_of_bf16_peak": tfm / BF16_MFMA_PEAK_TFLOPS}
+            del Xm, Ym
         xv = torch.empty((1, 8192), dtype=torch.bfloat16, device=dev).copy_(X[:1])
         yv = torch.empty((1, 8192), dtype=torch.float32, device=dev)
         ms_v5 = timed(lambda: w4.w4_gemv(P, xv, w4.W4_DYADIC, scales=S, y=yv, stream=stream),

@@ -384,7 +384,8 @@ def test_dyadic_gemv_batched(w4):
 
 
 @pytest.mark.parametrize("n,k,m", [(200, 576, 1), (200, 576, 130), (1024, 2048, 256), (64, 64, 128),
-                                   (100, 65600, 130)])
+                                   (100, 65600, 130), (64, 128, 1), (300, 1152, 100),
+                                   (200, 640, 128), (130, 256, 257), (100, 65536, 120)])
 def test_dyadic_gemm(w4, n, k, m):
     report("dyadic_gemm", n=n, k=k, m=m)
     w = _edge_weight(n, k, 700 + n, huge=False)
@@ -562,9 +563,10 @@ def test_lut16s_quantize_dequant_bitexact(w4, n, k):
     assert np.array_equal(host_bits(d), lut16.dequant_from_indices(idx, s, tables))
 
 
-@pytest.mark.parametrize("m", [1, 4, 16, 130])
+@pytest.mark.parametrize("m", [1, 4, 16, 100, 300])
 def test_lut16s_matmul(w4, m):
-    """GEMV (m <= 16: single call, fp32 and bf16 y) or GEMM (m = 130)."""
+    """GEMV (m <= 16: single call, fp32 and bf16 y) or GEMM (m = 100: 128-row
+    blocks; m = 300: 256-row blocks)."""
     n, k = 300, 1024
     report("lut16s_matmul", n=n, k=k, m=m)
     w, s, T, tables, idx = _lut16s_case(n, k, 960 + m)
@@ -621,10 +623,11 @@ def test_dyadic5_dequant_exhaustive_scales(w4):
     assert np.array_equal(host_bits(out), dyadic5.dequant_from_indices(idx, allb[:, None]))
 
 
-@pytest.mark.parametrize("m", [1, 4, 16, 130])
+@pytest.mark.parametrize("m", [1, 4, 16, 100, 300])
 def test_dyadic5_matmul(w4, m):
-    """GEMV (m <= 16: single call, k split for m > 1) or GEMM (m = 130), fp32
-    and bf16 outputs, against the fp64 oracle on the same 5-bit weights."""
+    """GEMV (m <= 16: single call, k split for m > 1) or GEMM (m = 100: 128-row
+    blocks; m = 300: 256-row blocks), fp32 and bf16 outputs, against the fp64
+    oracle on the same 5-bit weights."""
     n, k = 300, 1024
     report("dyadic5_matmul", n=n, k=k, m=m)
     w, widths, idx, s, nib, msb = _d5_case(n, k, 1600 + m)

@@ -43,10 +43,25 @@
 namespace w4 {
 namespace {
 
-constexpr int BM = 256, BN = 128, BK = 64;
+constexpr int BN = 128;  // weight rows per block
 constexpr int kMaxSplits = 8;
-constexpr int STR = BK / 8 + 1;  // 16-byte units per LDS weight row (+1 pad: conflict-free reads)
 constexpr uint32_t kOOB = 0x80000000u;
+
+// Block shapes by batch rows per block.  BMT = 256: four row groups of 64
+// batch rows, each shared by two waves that take the two k halves of a 64-k
+// step.  BMT = 128: two row groups, each shared by four waves that take the
+// four k quarters of a 128-k step.  Either way a wave computes 64 x 128
+// outputs over 32 k per step (16 MFMAs), and each thread rebuilds BK / 4
+// weights of one weight row per step.
+template <int BMT>
+struct Tile {
+  static constexpr int MW = BMT / 64;     // row groups
+  static constexpr int KW = 8 / MW;       // waves (k parts) per row group
+  static constexpr int BK = 32 * KW;      // k per step
+  static constexpr int DW = BK / 32;      // packed dwords a thread rebuilds per step
+  static constexpr int STR = BK / 8 + 1;  // 16-byte units per LDS weight row (+1: conflict-free reads)
+  static constexpr int WS = BN * STR;     // 16-byte units per weight tile plane
+};
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
@@ -67,21 +82,37 @@ struct RebuildConsts {
 };
 
 // Packed bytes and side data one thread rebuilds per k-step: weight row
-// tid / 4, k = 16 (tid % 4) .. + 15 of the step (8 packed bytes).  The rebuilt
-// values go to LDS in SIGMA order, as the activations are packed.
-template <int CODEC>
+// tid / 4, k = 8 DW (tid % 4) .. + 8 DW - 1 of the step (DW packed dwords, all
+// in one 64-group and one 32-group run).  The rebuilt values go to LDS in
+// SIGMA order, as the activations are packed.
+template <int CODEC, int DW>
 struct WRaw;
 
-template <>
-struct WRaw<0> {  // DYADIC: bf16 scale of the row's 64-group
-  uint32_t p0, p1;
+template <int DW>
+__device__ __forceinline__ void load_packed(uint32_t (&p)[DW], __amdgpu_buffer_rsrc_t pk,
+                                            uint32_t po) {
+  static_assert(DW == 2 || DW == 4, "two or four packed dwords");
+  if constexpr (DW == 2) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(pk, po, 0, 0);
+    p[0] = v[0];
+    p[1] = v[1];
+  } else {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(pk, po, 0, 0);
+    p[0] = v[0];
+    p[1] = v[1];
+    p[2] = v[2];
+    p[3] = v[3];
+  }
+}
+
+template <int DW>
+struct WRaw<0, DW> {  // DYADIC: bf16 scale of the row's 64-group
+  uint32_t p[DW];
   uint16_t sb;
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t pk, __amdgpu_buffer_rsrc_t s0,
                                        __amdgpu_buffer_rsrc_t, uint32_t po, uint32_t so,
                                        uint32_t) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b64(pk, po, 0, 0);
-    p0 = v[0];
-    p1 = v[1];
+    load_packed<DW>(p, pk, po);
     sb = __builtin_amdgcn_raw_buffer_load_b16(s0, so, 0, 0);
   }
   template <int D>
@@ -89,21 +120,19 @@ struct WRaw<0> {  // DYADIC: bf16 scale of the row's 64-group
     const DyadicScale d = dyadic_scale(sb);
     const uint32_t m0 = 0x000F000Fu, m1 = 0x00F000F0u, mg = kMagic;
     const float nz = __builtin_bit_cast(float, opaque(0x80000000u));
-    hi = dyadic_rebuild_any(D == 0 ? p0 : p1, d, m0, m1, mg, nz);
+    hi = dyadic_rebuild_any(p[D], d, m0, m1, mg, nz);
   }
 };
 
-template <>
-struct WRaw<1> {  // LUT16: 16 bf16 levels + bf16 scale of the row's 64-group
-  uint32_t p0, p1;
+template <int DW>
+struct WRaw<1, DW> {  // LUT16: 16 bf16 levels + bf16 scale of the row's 64-group
+  uint32_t p[DW];
   u32x4 l0, l1;
   uint16_t sb;
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t pk, __amdgpu_buffer_rsrc_t s0,
                                        __amdgpu_buffer_rsrc_t s1, uint32_t po, uint32_t so,
                                        uint32_t co) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b64(pk, po, 0, 0);
-    p0 = v[0];
-    p1 = v[1];
+    load_packed<DW>(p, pk, po);
     l0 = __builtin_amdgcn_raw_buffer_load_b128(s1, co, 0, 0);
     l1 = __builtin_amdgcn_raw_buffer_load_b128(s1, co + 16, 0, 0);
     sb = __builtin_amdgcn_raw_buffer_load_b16(s0, so, 0, 0);
@@ -111,113 +140,116 @@ struct WRaw<1> {  // LUT16: 16 bf16 levels + bf16 scale of the row's 64-group
   template <int D>
   __device__ __forceinline__ void rebuild(u32x4& hi, u32x4&, const RebuildConsts&) const {
     const Lut16Table t = lut16_table(sb, l0, l1);
-    hi = lut16_rebuild(D == 0 ? p0 : p1, t);
+    hi = lut16_rebuild(p[D], t);
   }
 };
 
-template <>
-struct WRaw<2> {  // SIGNMAG8: 8 fp16 magnitudes of the row's 32-group
-  uint32_t p0, p1;
+template <int DW>
+struct WRaw<2, DW> {  // SIGNMAG8: 8 fp16 magnitudes of the row's 32-group
+  uint32_t p[DW];
   u32x4 c;
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t pk, __amdgpu_buffer_rsrc_t,
                                        __amdgpu_buffer_rsrc_t s1, uint32_t po, uint32_t,
                                        uint32_t co) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b64(pk, po, 0, 0);
-    p0 = v[0];
-    p1 = v[1];
+    load_packed<DW>(p, pk, po);
     c = __builtin_amdgcn_raw_buffer_load_b128(s1, co, 0, 0);
   }
   template <int D>
   __device__ __forceinline__ void rebuild(u32x4& hi, u32x4& lo, const RebuildConsts&) const {
     const SignMagTable t = signmag_table(c);
-    signmag_rebuild(D == 0 ? p0 : p1, t, hi, lo);
+    signmag_rebuild(p[D], t, hi, lo);
   }
 };
 
-template <>
-struct WRaw<3> {  // LUT16S: bf16 scale of the row's 64-group; levels shared
-  uint32_t p0, p1;
+template <int DW>
+struct WRaw<3, DW> {  // LUT16S: bf16 scale of the row's 64-group; levels shared
+  uint32_t p[DW];
   uint16_t sb;
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t pk, __amdgpu_buffer_rsrc_t s0,
                                        __amdgpu_buffer_rsrc_t, uint32_t po, uint32_t so,
                                        uint32_t) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b64(pk, po, 0, 0);
-    p0 = v[0];
-    p1 = v[1];
+    load_packed<DW>(p, pk, po);
     sb = __builtin_amdgcn_raw_buffer_load_b16(s0, so, 0, 0);
   }
   template <int D>
   __device__ __forceinline__ void rebuild(u32x4& hi, u32x4&, const RebuildConsts& st) const {
     const Lut16Table t = lut16_table(sb, st.l0, st.l1);
-    hi = lut16_rebuild(D == 0 ? p0 : p1, t);
+    hi = lut16_rebuild(p[D], t);
   }
 };
 
-template <>
-struct WRaw<4> {  // DYADIC5: bf16 scale of the row's 64-group + high-bit word of its run of 32
-  uint32_t p0, p1, h;
+template <int DW>
+struct WRaw<4, DW> {  // DYADIC5: bf16 scale of the row's 64-group + high-bit word of its run of 32
+  uint32_t p[DW], h;
   uint16_t sb;
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t pk, __amdgpu_buffer_rsrc_t s0,
                                        __amdgpu_buffer_rsrc_t s1, uint32_t po, uint32_t so,
                                        uint32_t co) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b64(pk, po, 0, 0);
-    p0 = v[0];
-    p1 = v[1];
+    load_packed<DW>(p, pk, po);
     sb = __builtin_amdgcn_raw_buffer_load_b16(s0, so, 0, 0);
     h = __builtin_amdgcn_raw_buffer_load_b32(s1, co, 0, 0);
   }
-  // dword D of the thread's 16 weights is dword 2 (wq % 2) + D of the run;
-  // msb_shift (0 or 8) folds the 2 (wq % 2) into the shifts of dwords 0, 1
+  // DW = 2: dword D of the thread's 16 weights is dword 2 (wq % 2) + D of the
+  // run, and msb_shift (0 or 8) folds the 2 (wq % 2) into the shifts of dwords
+  // 0, 1.  DW = 4: the thread's dwords are the whole run, msb_shift 0.
   template <int D>
   __device__ __forceinline__ void rebuild(u32x4& hi, u32x4&, const RebuildConsts& c) const {
     uint32_t e0, e1;
     dyadic5_msb<D>(h >> c.msb_shift, e0, e1);
     const float pz = __builtin_bit_cast(float, opaque(0u));
-    hi = dyadic5_rebuild(D == 0 ? p0 : p1, e0, e1, dyadic5_scale(sb), pz);
+    hi = dyadic5_rebuild(p[D], e0, e1, dyadic5_scale(sb), pz);
   }
 };
 
 // LDS: two rebuilt weight tiles during the k loop; after it, the same bytes
-// hold the k-half partial sums that the waves of one row group exchange.
-constexpr int kWsUnits = BN * STR;                  // 16-byte units per weight tile plane
-constexpr size_t kRedBytes = 4 * 32 * 64 * 16;      // 4 row groups x 128 floats x 64 lanes
-template <int CODEC>
+// hold the k-part partial sums that the waves of one row group exchange (one
+// 32 KB slot per writing wave: four row groups x one for BMT = 256, two row
+// groups x two for BMT = 128).
+constexpr size_t kRedSlotBytes = 32 * 64 * 16;  // 128 floats x 64 lanes
+template <int CODEC, int BMT>
 constexpr size_t gemm_lds_bytes() {
-  const size_t w = (size_t)2 * (CODEC == 2 ? 2 : 1) * kWsUnits * 16;
-  return w > kRedBytes ? w : kRedBytes;
+  const size_t w = (size_t)2 * (CODEC == 2 ? 2 : 1) * Tile<BMT>::WS * 16;
+  const size_t r = (size_t)4 * kRedSlotBytes;
+  return w > r ? w : r;
 }
 
-template <int CODEC>
+template <int D>
+using DI = std::integral_constant<int, D>;
+
+template <int CODEC, int BMT>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_kernel(
     GemvProblem P, int M, int y_bf16, const u32x4* __restrict__ xpk, float* __restrict__ partial) {
+  using TL = Tile<BMT>;
+  constexpr int MW = TL::MW, KW = TL::KW, BK = TL::BK, DW = TL::DW, STR = TL::STR;
   constexpr int NPL = CODEC == 2 ? 2 : 1;  // SIGNMAG8: high and low bf16 planes
   extern __shared__ u32x4 lds[];
-  auto wtile = [&](int buf, int pl) { return lds + (buf * NPL + pl) * kWsUnits; };
+  auto wtile = [&](int buf, int pl) { return lds + (buf * NPL + pl) * TL::WS; };
 
   const int64_t N = P.n, K = P.k;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int mw = wave & 3, kh = wave >> 2;  // row group, k half
-  // Block -> (split, m tile, n tile).  Blocks are dealt to the 8 XCDs round
-  // robin; renumbering them so that each XCD gets a contiguous range of the
-  // split-major order keeps one split's activations (256 x k / S bf16) in that
-  // XCD's L2 instead of all of them.
+  const int mw = wave % MW, kh = wave / MW;  // row group, k part
+  // Block -> (split, n tile, m tile), m fastest.  Blocks are dealt to the 8
+  // XCDs round robin; renumbering them so that each XCD gets a contiguous
+  // range of this order keeps one split's activations (BMT x k / S bf16 per m
+  // tile) in that XCD's L2 instead of all of them, and the m tiles of one
+  // weight tile on the same XCD, which then reads those weights from HBM once.
   const uint32_t G = gridDim.x, b = blockIdx.x;
   const uint32_t L = (G & 7u) == 0 ? (b & 7u) * (G >> 3) + (b >> 3) : b;
-  const uint32_t tiles_n = (uint32_t)((P.n + BN - 1) / BN), tiles_m = (uint32_t)((M + BM - 1) / BM);
+  const uint32_t tiles_n = (uint32_t)((P.n + BN - 1) / BN), tiles_m = (uint32_t)((M + BMT - 1) / BMT);
   const uint32_t tile = L % (tiles_n * tiles_m);
-  const uint32_t nt = tile % tiles_n, mt = tile / tiles_n;
+  const uint32_t nt = tile / tiles_m, mt = tile % tiles_m;
   const int s = (int)(L / (tiles_n * tiles_m));
-  const int64_t n0 = (int64_t)nt * BN, m0 = (int64_t)mt * BM;
+  const int64_t n0 = (int64_t)nt * BN, m0 = (int64_t)mt * BMT;
   const int rows_n = (int)(N - n0 < BN ? N - n0 : BN);
-  const int rows_m = (int)(M - m0 < BM ? M - m0 : BM);
+  const int rows_m = (int)(M - m0 < BMT ? M - m0 : BMT);
 
-  // k range of this split, in 64-k steps
+  // k range of this split, in BK steps (k is a multiple of BK)
   const int T = (int)(K / BK), S = (int)(G / (tiles_n * tiles_m));
   const int ks0 = (int)((int64_t)s * T / S), ks1 = (int)((int64_t)(s + 1) * T / S);
   const int nsteps = ks1 - ks0;
 
-  // weight rebuild role: row wr, quarter wq of the 64-k step
+  // weight rebuild role: row wr, part wq (DW packed dwords) of the step
   const int wr = tid >> 2, wq = tid & 3;
   const uint32_t row_bytes = (uint32_t)(K >> 1);
   const __amdgpu_buffer_rsrc_t pk = rsrc(P.packed + n0 * (K >> 1), (uint32_t)rows_n * row_bytes);
@@ -234,39 +266,44 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   } else {
     s1 = rsrc(P.codebook + n0 * (K >> 5) * 8, (uint32_t)(rows_n * (K >> 5) * 16));
   }
-  const uint32_t p_lane = (uint32_t)wr * row_bytes + 8u * (uint32_t)wq;
-  const uint32_t g64_lane = (uint32_t)wr * (uint32_t)(K >> 6);
-  const uint32_t g32_lane = (uint32_t)wr * (uint32_t)(K >> 5) + (uint32_t)(wq >> 1);
+  // the thread's bytes of a step and their 64-group and run of 32; per step
+  // these advance by BK / 2 bytes, BK / 64 groups and BK / 32 runs
+  constexpr uint32_t kPkStep = BK / 2, kG64Step = BK / 64, kG32Step = BK / 32;
+  const uint32_t p_lane = (uint32_t)wr * row_bytes + 4u * DW * (uint32_t)wq;
+  const uint32_t g64_lane = (uint32_t)wr * (uint32_t)(K >> 6) + (uint32_t)(wq * DW / 8);
+  const uint32_t g32_lane = (uint32_t)wr * (uint32_t)(K >> 5) + (uint32_t)(wq * DW / 4);
   // DYADIC5: byte offset of the high-bit word of the thread's run of 32
-  const uint32_t h_lane = (uint32_t)wr * (uint32_t)(K >> 3) + 4u * (uint32_t)(wq >> 1);
+  const uint32_t h_lane = (uint32_t)wr * (uint32_t)(K >> 3) + 4u * (uint32_t)(wq * DW / 4);
 
-  // activation role: the block's 8 row tiles of 32 in the packed layout
+  // activation role: the block's BMT / 32 row tiles of 32 in the packed layout
   // (pack_activations); wave (mw, kh) takes row tiles 2 mw + i and, within a
   // step, 16-k blocks kb = 2 kh + kk
   const int r32 = lane & 31, h = lane >> 5;
   const uint32_t kblocks = (uint32_t)(K >> 4);
-  const __amdgpu_buffer_rsrc_t xr = rsrc(xpk + (size_t)(m0 >> 5) * kblocks * 64, 8u * kblocks * 1024u);
+  const __amdgpu_buffer_rsrc_t xr =
+      rsrc(xpk + (size_t)(m0 >> 5) * kblocks * 64, (uint32_t)(BMT / 32) * kblocks * 1024u);
   const uint32_t x_lane = ((uint32_t)(2 * mw) * kblocks + 2u * (uint32_t)kh) * 1024u + 16u * (uint32_t)lane;
   const uint32_t x_i = kblocks * 1024u;  // next row tile
+  constexpr uint32_t kXStep = 64u * BK;  // BK / 16 records of 1 KB per step
 
-  WRaw<CODEC> wqr[4];
+  WRaw<CODEC, DW> wqr[4];
   u32x4 xq[2][2][2];
   // Offsets of a step past the split are kOOB plus at most 2^31 - 1: still
   // past every resource (num_records <= 2^31 since k <= 2^22), so those loads
   // return zero without a branch.
-  auto load_w = [&](WRaw<CODEC>& r, int u) {
+  auto load_w = [&](WRaw<CODEC, DW>& r, int u) {
     const bool in = u < nsteps;
     const uint32_t ks = (uint32_t)(ks0 + u);
     // byte offsets: packed, 64-group scale, codebook (LUT16 levels / SIGNMAG8 magnitudes)
-    const uint32_t co = CODEC == 1   ? 32u * (g64_lane + ks)
-                        : CODEC == 4 ? h_lane + 8u * ks
-                                     : 16u * (g32_lane + 2u * ks);
-    r.load(pk, s0, s1, opaque(in ? p_lane + ks * 32u : kOOB),
-           opaque(in ? 2u * (g64_lane + ks) : kOOB), opaque(in ? co : kOOB));
+    const uint32_t co = CODEC == 1   ? 32u * (g64_lane + kG64Step * ks)
+                        : CODEC == 4 ? h_lane + 4u * kG32Step * ks
+                                     : 16u * (g32_lane + kG32Step * ks);
+    r.load(pk, s0, s1, opaque(in ? p_lane + ks * kPkStep : kOOB),
+           opaque(in ? 2u * (g64_lane + kG64Step * ks) : kOOB), opaque(in ? co : kOOB));
   };
   auto load_x = [&](u32x4 (&xv)[2][2], int u) {
     const bool in = u < nsteps;
-    const uint32_t base = opaque(in ? x_lane + (uint32_t)(ks0 + u) * 4096u : kOOB);
+    const uint32_t base = opaque(in ? x_lane + (uint32_t)(ks0 + u) * kXStep : kOOB);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -275,21 +312,32 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             xr, base + (uint32_t)i * x_i + (uint32_t)kk * 1024u, 0, 0);
   };
   RebuildConsts st{};
-  st.msb_shift = 8u * (uint32_t)(wq & 1);
+  st.msb_shift = DW == 2 ? 8u * (uint32_t)(wq & 1) : 0u;
   if constexpr (CODEC == 3) {
     st.l0 = reinterpret_cast<const u32x4*>(P.codebook)[0];
     st.l1 = reinterpret_cast<const u32x4*>(P.codebook)[1];
   }
-  // rebuild packed dword D (k = 16 wq + 8 D .. + 7 of the step) into LDS
-  auto rebuild = [&](const WRaw<CODEC>& r, int buf, auto dtag) {
+  // rebuild packed dword D (k = 8 (DW wq + D) .. + 7 of the step) into LDS
+  auto rebuild = [&](const WRaw<CODEC, DW>& r, int buf, auto dtag) {
     constexpr int D = decltype(dtag)::value;
     u32x4 hi, lo;
     r.template rebuild<D>(hi, lo, st);
-    wtile(buf, 0)[wr * STR + 2 * wq + D] = hi;
-    if constexpr (NPL == 2) wtile(buf, 1)[wr * STR + 2 * wq + D] = lo;
+    wtile(buf, 0)[wr * STR + DW * wq + D] = hi;
+    if constexpr (NPL == 2) wtile(buf, 1)[wr * STR + DW * wq + D] = lo;
   };
-  using D0 = std::integral_constant<int, 0>;
-  using D1 = std::integral_constant<int, 1>;
+  // the first and the second half of a thread's dwords
+  auto rebuild_first = [&](const WRaw<CODEC, DW>& r, int buf) {
+    rebuild(r, buf, DI<0>{});
+    if constexpr (DW == 4) rebuild(r, buf, DI<1>{});
+  };
+  auto rebuild_second = [&](const WRaw<CODEC, DW>& r, int buf) {
+    if constexpr (DW == 2) {
+      rebuild(r, buf, DI<1>{});
+    } else {
+      rebuild(r, buf, DI<2>{});
+      rebuild(r, buf, DI<3>{});
+    }
+  };
 
   f32x16 acc[2][4];
 #pragma unroll
@@ -299,7 +347,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // B operands of one 16-k block kk of a step (4 weight-row tiles of 32)
+  // B operands of one 16-k block kk of the wave's k part (4 weight-row tiles of 32)
   auto read_b = [&](u32x4 (&bq)[NPL][4], int buf, int kk) {
     const int kb = 2 * kh + kk;
 #pragma unroll
@@ -325,16 +373,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   //         buffer step u has just released.
   // The LDS reads of the next step thus run under the MFMAs of the current
   // one instead of between barriers, and each phase's rebuild work (about
-  // half a step's VALU) fits under its eight MFMAs per wave.
+  // half a step's VALU) runs beside its eight MFMAs per wave.
   u32x4 b0[NPL][4], b1[NPL][4];
   load_w(wqr[0], 0);
   load_w(wqr[1], 1);
   load_w(wqr[2], 2);
   load_w(wqr[3], 3);
   load_x(xq[0], 0);
-  rebuild(wqr[0], 0, D0{});
-  rebuild(wqr[0], 0, D1{});
-  rebuild(wqr[1], 1, D0{});
+  rebuild_first(wqr[0], 0);
+  rebuild_second(wqr[0], 0);
+  rebuild_first(wqr[1], 1);
   lds_barrier();
   read_b(b0, 0, 0);
 
@@ -346,7 +394,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       read_b(b1, cur, 1);
       load_x(xq[nxt], u + v + 1);
       mma_half(xq[cur], b0, 0);
-      rebuild(wqr[(v + 1) & 3], nxt, D1{});
+      rebuild_second(wqr[(v + 1) & 3], nxt);
       load_w(wqr[v & 3], u + v + 4);
       __builtin_amdgcn_sched_barrier(0);
       lds_barrier();
@@ -354,15 +402,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       // phase B
       read_b(b0, nxt, 0);
       mma_half(xq[cur], b1, 1);
-      rebuild(wqr[(v + 2) & 3], cur, D0{});
+      rebuild_first(wqr[(v + 2) & 3], cur);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
   lds_barrier();  // the last phase's LDS traffic is done before LDS is reused
 
-  // the two k halves of a row group meet in LDS (the weight tiles are dead)
-  f32x4* const red = reinterpret_cast<f32x4*>(lds) + mw * 32 * 64 + lane;
-  if (kh == 1) {
+  // the k parts of a row group meet in LDS (the weight tiles are dead):
+  // BMT = 256 adds a0 + a1; BMT = 128 adds (a0 + a1) + (a2 + a3)
+  auto put = [&](int slot) {
+    f32x4* const d = reinterpret_cast<f32x4*>(lds) + slot * 32 * 64 + lane;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -370,28 +419,44 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           const f32x16& a = acc[i][j];
-          red[((i * 4 + j) * 4 + r4) * 64] =
+          d[((i * 4 + j) * 4 + r4) * 64] =
               (f32x4){a[4 * r4], a[4 * r4 + 1], a[4 * r4 + 2], a[4 * r4 + 3]};
         }
+  };
+  auto add = [&](int slot) {
+    const f32x4* const d = reinterpret_cast<const f32x4*>(lds) + slot * 32 * 64 + lane;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4 o = d[((i * 4 + j) * 4 + r4) * 64];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][4 * r4 + e] += o[e];
+        }
+  };
+  if constexpr (KW == 2) {
+    if (kh == 1) put(mw);
+    lds_barrier();
+    if (kh == 1) return;
+    add(mw);
+  } else {
+    if (kh & 1) put(2 * mw + (kh >> 1));
+    lds_barrier();
+    if (!(kh & 1)) add(2 * mw + (kh >> 1));
+    lds_barrier();
+    if (kh == 2) put(mw);  // slots 0, 1: read in the first round already
+    lds_barrier();
+    if (kh != 0) return;
+    add(mw);
   }
-  lds_barrier();
-  if (kh == 1) return;
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x4 o = red[((i * 4 + j) * 4 + r4) * 64];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[i][j][4 * r4 + e] += o[e];
-      }
 
   if (partial) {
     // split partial in the MFMA register layout: 16-byte stores, 1 KB per
     // instruction; the reduction kernel maps it back to rows and columns
     f32x4* dst = reinterpret_cast<f32x4*>(partial) +
-                 (((size_t)s * tiles_m * tiles_n + tile) * 4 + mw) * 32 * 64 + lane;
+                 (((size_t)s * tiles_m * tiles_n + tile) * MW + mw) * 32 * 64 + lane;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -455,11 +520,13 @@ __global__ __launch_bounds__(256) void pack_activations(const u32x4* __restrict_
 
 // y = sum of the S split partials, added in split order.  One thread per
 // (tile, row group, 4-register group, lane) of the GEMM's register layout.
+template <int BMT>
 __global__ __launch_bounds__(256) void splitk_reduce(const f32x4* __restrict__ partial, int S,
-                                                     uint32_t tiles_n, uint32_t tiles,
+                                                     uint32_t tiles_m, uint32_t tiles,
                                                      int64_t M, int64_t N, void* y, int y_bf16) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;  // < tiles * 4 * 32 * 64
-  const int64_t per_split = (int64_t)tiles * 4 * 32 * 64;
+  constexpr int MW = Tile<BMT>::MW;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;  // < tiles * MW * 32 * 64
+  const int64_t per_split = (int64_t)tiles * MW * 32 * 64;
   if (t >= per_split) return;
   // every split's load in flight at once, then the sum in split order
   f32x4 p[kMaxSplits];
@@ -470,12 +537,13 @@ __global__ __launch_bounds__(256) void splitk_reduce(const f32x4* __restrict__ p
 #pragma unroll
   for (int s = 1; s < kMaxSplits; ++s)
     if (s < S) v += p[s];
-  const int lane = (int)(t & 63), r4g = (int)((t >> 6) & 31), mw = (int)((t >> 11) & 3);
-  const uint32_t tile = (uint32_t)(t >> 13);
+  const int lane = (int)(t & 63), r4g = (int)((t >> 6) & 31);
+  const int mw = (int)((t >> 11) % MW);
+  const uint32_t tile = (uint32_t)((t >> 11) / MW);
   const int r32 = lane & 31, h = lane >> 5;
   const int i = r4g >> 4, j = (r4g >> 2) & 3, r4 = r4g & 3;
-  const int64_t row0 = (int64_t)(tile / tiles_n) * BM + 64 * mw + 32 * i + 8 * r4 + 4 * h;
-  const int64_t col = (int64_t)(tile % tiles_n) * BN + 32 * j + r32;
+  const int64_t row0 = (int64_t)(tile % tiles_m) * BMT + 64 * mw + 32 * i + 8 * r4 + 4 * h;
+  const int64_t col = (int64_t)(tile / tiles_m) * BN + 32 * j + r32;
   if (col >= N) return;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -489,23 +557,21 @@ __global__ __launch_bounds__(256) void splitk_reduce(const f32x4* __restrict__ p
   }
 }
 
-}  // namespace
-
 // Splits of the k range: enough blocks for about one per CU, at least eight
 // k-steps per split, at most eight splits.
-int gemm_splits(int64_t n, int64_t k, int m, int cus) {
-  const int64_t tiles = ((n + BN - 1) / BN) * ((m + BM - 1) / BM);
-  const int64_t steps = k / BK;
+int gemm_splits(int64_t n, int64_t k, int m, int cus, int bm, int bk) {
+  const int64_t tiles = ((n + BN - 1) / BN) * ((m + bm - 1) / bm);
+  const int64_t steps = k / bk;
   int64_t s = tiles > 0 ? (cus + tiles - 1) / tiles : 1;
   if (s > kMaxSplits) s = kMaxSplits;
   if (s > steps / 8) s = steps / 8;
   return s < 1 ? 1 : (int)s;
 }
 
-template <int CODEC>
+template <int CODEC, int BMT>
 hipError_t launch_codec(const GemvProblem& p, int m, int y_bf16, const u32x4* xpk, float* partial,
                         uint32_t blocks, hipStream_t stream) {
-  constexpr size_t lds = gemm_lds_bytes<CODEC>();
+  constexpr size_t lds = gemm_lds_bytes<CODEC, BMT>();
   // the LDS limit is raised once per device (one bit each for the first 64);
   // callers racing here all set the same value
   static std::atomic<uint64_t> configured{0};
@@ -514,53 +580,78 @@ hipError_t launch_codec(const GemvProblem& p, int m, int y_bf16, const u32x4* xp
   if (e != hipSuccess) return e;
   const uint64_t bit = dev < 64 ? uint64_t{1} << dev : 0;
   if (!(configured.load(std::memory_order_acquire) & bit)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<CODEC>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<CODEC, BMT>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     configured.fetch_or(bit, std::memory_order_release);
   }
-  gemm_kernel<CODEC><<<dim3(blocks), dim3(512), lds, stream>>>(p, m, y_bf16, xpk, partial);
+  gemm_kernel<CODEC, BMT><<<dim3(blocks), dim3(512), lds, stream>>>(p, m, y_bf16, xpk, partial);
   return hipGetLastError();
 }
 
-hipError_t launch_gemm(int codec, const GemvProblem& p, int m, int y_bf16, hipStream_t stream) {
+// The 128-row block serves batches of at most 128 rows, which would leave half
+// of a 256-row block's MFMA work on zero rows, for the codecs whose side data
+// fits the registers of its four packed dwords per thread (DYADIC, LUT16S,
+// DYADIC5) when k is a multiple of its 128-k step.  Measured at K = N = 8192:
+// M = 128 in 34 us against 45 us; at M = 256 its halved k splits do not make
+// up for the doubled rebuild work per step (about 3% slower), and it is
+// slower still at M = 512 and 1024.
+constexpr int kNarrowMaxM = 128;
+bool gemm_narrow(int codec, int64_t k, int m) {
+  return (codec == 0 || codec == 3 || codec == 4) && k % 128 == 0 && m <= kNarrowMaxM;
+}
+
+template <int BMT>
+hipError_t launch_gemm_shape(int codec, const GemvProblem& p, int m, int y_bf16,
+                             hipStream_t stream) {
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     cus = 256;
-  const int S = gemm_splits(p.n, p.k, m, cus);
-  const uint32_t tiles_n = (uint32_t)((p.n + BN - 1) / BN), tiles_m = (uint32_t)((m + BM - 1) / BM);
+  const int S = gemm_splits(p.n, p.k, m, cus, BMT, Tile<BMT>::BK);
+  const uint32_t tiles_n = (uint32_t)((p.n + BN - 1) / BN), tiles_m = (uint32_t)((m + BMT - 1) / BMT);
   const uint32_t tiles = tiles_n * tiles_m;
-  // workspace: packed activations of tiles_m * 256 rows, then S fp32 partials
-  // of tiles * 256 * 128 when the k range is split
-  const size_t xpk_bytes = (size_t)tiles_m * BM * p.k * 2;
-  const size_t per_split = (size_t)tiles * BM * BN;  // floats
+  // workspace: packed activations of tiles_m * BMT rows, then S fp32 partials
+  // of tiles * BMT * BN when the k range is split
+  const size_t xpk_bytes = (size_t)tiles_m * BMT * p.k * 2;
+  const size_t per_split = (size_t)tiles * BMT * BN;  // floats
   const size_t bytes = xpk_bytes + (S > 1 ? (size_t)S * per_split * sizeof(float) : 0);
   char* ws = nullptr;
   hipError_t e = stream_workspace(kWorkspaceGemm, stream, bytes, &ws);
   if (e != hipSuccess) return e;
   u32x4* xpk = reinterpret_cast<u32x4*>(ws);
   float* partial = S > 1 ? reinterpret_cast<float*>(ws + xpk_bytes) : nullptr;
-  pack_activations<<<dim3((uint32_t)(tiles_m * 8 * (p.k / 64))), dim3(256), 0, stream>>>(
+  pack_activations<<<dim3((uint32_t)(tiles_m * (BMT / 32) * (p.k / 64))), dim3(256), 0, stream>>>(
       reinterpret_cast<const u32x4*>(p.x), xpk, m, p.k);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const uint32_t blocks = tiles * (uint32_t)S;
   if (codec == 0)
-    e = launch_codec<0>(p, m, y_bf16, xpk, partial, blocks, stream);
-  else if (codec == 1)
-    e = launch_codec<1>(p, m, y_bf16, xpk, partial, blocks, stream);
+    e = launch_codec<0, BMT>(p, m, y_bf16, xpk, partial, blocks, stream);
   else if (codec == 3)
-    e = launch_codec<3>(p, m, y_bf16, xpk, partial, blocks, stream);
+    e = launch_codec<3, BMT>(p, m, y_bf16, xpk, partial, blocks, stream);
   else if (codec == 4)
-    e = launch_codec<4>(p, m, y_bf16, xpk, partial, blocks, stream);
-  else
-    e = launch_codec<2>(p, m, y_bf16, xpk, partial, blocks, stream);
+    e = launch_codec<4, BMT>(p, m, y_bf16, xpk, partial, blocks, stream);
+  else if constexpr (BMT == 256) {
+    if (codec == 1)
+      e = launch_codec<1, 256>(p, m, y_bf16, xpk, partial, blocks, stream);
+    else
+      e = launch_codec<2, 256>(p, m, y_bf16, xpk, partial, blocks, stream);
+  } else {
+    return hipErrorInvalidValue;  // LUT16 and SIGNMAG8 use the 256-row block only
+  }
   if (e != hipSuccess || S == 1) return e;
   const size_t threads = per_split / 4;
-  splitk_reduce<<<dim3((uint32_t)((threads + 255) / 256)), dim3(256), 0, stream>>>(
-      reinterpret_cast<const f32x4*>(partial), S, tiles_n, tiles, m, p.n, p.y, y_bf16);
+  splitk_reduce<BMT><<<dim3((uint32_t)((threads + 255) / 256)), dim3(256), 0, stream>>>(
+      reinterpret_cast<const f32x4*>(partial), S, tiles_m, tiles, m, p.n, p.y, y_bf16);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm(int codec, const GemvProblem& p, int m, int y_bf16, hipStream_t stream) {
+  if (gemm_narrow(codec, p.k, m)) return launch_gemm_shape<128>(codec, p, m, y_bf16, stream);
+  return launch_gemm_shape<256>(codec, p, m, y_bf16, stream);
 }
 
 }  // namespace w4

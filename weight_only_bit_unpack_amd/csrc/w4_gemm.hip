@@ -591,14 +591,14 @@ hipError_t launch_codec(const GemvProblem& p, int m, int y_bf16, const u32x4* xp
 
 // The 128-row block serves batches of at most 128 rows, which would leave half
 // of a 256-row block's MFMA work on zero rows, for the codecs whose side data
-// fits the registers of its four packed dwords per thread (DYADIC, LUT16S,
-// DYADIC5) when k is a multiple of its 128-k step.  Measured at K = N = 8192:
+// fits the registers of its four packed dwords per thread (all but SIGNMAG8,
+// whose two operand planes leave none) when k is a multiple of its 128-k step.  Measured at K = N = 8192:
 // M = 128 in 34 us against 45 us; at M = 256 its halved k splits do not make
 // up for the doubled rebuild work per step (about 3% slower), and it is
 // slower still at M = 512 and 1024.
 constexpr int kNarrowMaxM = 128;
 bool gemm_narrow(int codec, int64_t k, int m) {
-  return (codec == 0 || codec == 3 || codec == 4) && k % 128 == 0 && m <= kNarrowMaxM;
+  return (codec == 0 || codec == 1 || codec == 3 || codec == 4) && k % 128 == 0 && m <= kNarrowMaxM;
 }
 
 template <int BMT>
@@ -632,13 +632,12 @@ hipError_t launch_gemm_shape(int codec, const GemvProblem& p, int m, int y_bf16,
     e = launch_codec<3, BMT>(p, m, y_bf16, xpk, partial, blocks, stream);
   else if (codec == 4)
     e = launch_codec<4, BMT>(p, m, y_bf16, xpk, partial, blocks, stream);
+  else if (codec == 1)
+    e = launch_codec<1, BMT>(p, m, y_bf16, xpk, partial, blocks, stream);
   else if constexpr (BMT == 256) {
-    if (codec == 1)
-      e = launch_codec<1, 256>(p, m, y_bf16, xpk, partial, blocks, stream);
-    else
-      e = launch_codec<2, 256>(p, m, y_bf16, xpk, partial, blocks, stream);
+    e = launch_codec<2, 256>(p, m, y_bf16, xpk, partial, blocks, stream);
   } else {
-    return hipErrorInvalidValue;  // LUT16 and SIGNMAG8 use the 256-row block only
+    return hipErrorInvalidValue;  // SIGNMAG8 uses the 256-row block only
   }
   if (e != hipSuccess || S == 1) return e;
   const size_t threads = per_split / 4;

@@ -270,15 +270,17 @@ w4_status w4_gemv(int32_t codec, int64_t n, int64_t k, const uint8_t* packed,
  * band, m up to 256).  Same arguments as w4_gemv; m >= 1 (tuned for m >= 128).
  * Workspace: the call enqueues up to three kernels (an activation re-layout,
  * the product, and an in-order sum of the k-split partials) that use a device
- * buffer of ceil(m/256) * 256 * k * 2 bytes plus, when k is split S ways,
- * S * ceil(m/256) * 256 * ceil(n/128) * 128 * 4 bytes.  The library keeps one
- * such buffer per (device, stream), grown on demand with hipMalloc (growing
- * waits for the stream and frees the old buffer) and never freed, so calls on
- * one stream are ordered and calls on different streams never share it.
+ * buffer of ceil(m/B) * B * k * 2 bytes plus, when k is split S <= 8 ways,
+ * S * ceil(m/B) * B * ceil(n/128) * 128 * 4 bytes, where B, the batch rows
+ * of a block, is 128 when m <= 128, k is a multiple of 128 and the codec is
+ * not SIGNMAG8, and 256 otherwise.  The library keeps one such buffer per
+ * (device, stream), grown on demand with hipMalloc (growing waits for the
+ * stream and frees the old buffer) and never freed, so calls on one stream
+ * are ordered and calls on different streams never share it.
  * Graph capture: a call that would create or grow the buffer cannot be
- * captured (hipMalloc); make one call of the largest size on the capture
- * stream before capturing.  After that, calls only enqueue kernels (no
- * memset, no allocation).
+ * captured (hipMalloc); make one call of each shape to be captured on the
+ * capture stream before capturing.  After that, calls only enqueue kernels
+ * (no memset, no allocation).
  * Additional error: W4_EHIP when the workspace cannot be allocated.
  */
 w4_status w4_gemm(int32_t codec, int64_t n, int64_t k, const uint8_t* packed,

@@ -11,7 +11,9 @@
 // v_mfma_f32_32x32x16_bf16 (128 fp32 accumulators per lane), for half of each
 // k-step (w / 4); the two halves are added through LDS after the k loop.  Two
 // waves per SIMD let one wave's MFMAs run while the other waits on memory,
-// LDS or the rebuild, which a single wave cannot overlap.
+// LDS or the rebuild, which a single wave cannot overlap.  Batches of at most
+// 128 rows use a 128 x 128 block with 128-k steps instead: four waves share a
+// row group, one k quarter each, so every wave's work per step is the same.
 //
 // A wave owns its batch rows, so its activation operands come straight from
 // global memory into registers, from a copy of x rewritten once per call into

@@ -11,10 +11,11 @@
  *    absmax, codes (s/8)(j-8), index = lowest j minimising |w - c_j| over the
  *    16 codes in double, all-zero group -> index 8, dequant RNE_bf16 of the
  *    exact product with a zero result stored as +0;
- *  - LUT16 codec (k-means page, sections 1.2, 2.2): levels v_j = s*L_j in
- *    float (exact), index = lowest j minimising |fl32(w - v_j)|;
+ *  - LUT16 codec (k-means page, sections 1.2, 2.2): levels v_j = s*L_j
+ *    (exact in double), index = lowest j minimising the exact |w - v_j|;
  *  - sign + magnitude codec (int4-g32 page, sections 1.3, 2): sign = (w < 0),
- *    magnitude index = lowest j minimising |fl32(|w| - M_j)|;
+ *    magnitude index = lowest j minimising the exact ||w| - M_j| (a +inf
+ *    magnitude is infinitely far from every finite weight);
  *  - the 1D Lloyd fit (k-means page section 1.2; int4-g32 page section 1.3):
  *    quantile start sorted[k*stride + stride/2], then `iters` rounds of
  *    nearest-centre assignment (double, lowest index on a tie) and member
@@ -134,6 +135,43 @@ int oracle_dyadic_dequant(const uint8_t* idx, const uint16_t* scales, int64_t n,
   return 0;
 }
 
+/* ------------------------------------------------------------ nearest level */
+/* Exact rounding error of a + b for finite a, b (Knuth's two-sum):
+ * (a + b) - fl(a + b), itself a double.  sum = fl(a + b). */
+static double two_sum_err(double a, double b, double sum) {
+  const double bp = sum - a;
+  const double ap = sum - bp;
+  return (a - ap) + (b - bp);
+}
+
+/* Lowest index j minimising the exact |x - v[j]|, for values held exactly in
+ * double (bf16 weights, products of two bf16 numbers, fp16 magnitudes, +inf).
+ * The rounded distance fl(|x - v_j|) is monotone in the exact one, so only
+ * the levels that share the smallest rounded distance can be the nearest.
+ * Their exact distance is |h| + sgn(h) e with h = fl(x - v_j) and e the exact
+ * error of that subtraction; with |h| equal for all of them, the term
+ * sgn(h) e orders them exactly.  If the smallest rounded distance is +inf,
+ * every level is +inf away and the lowest index wins. */
+static int nearest_level(double x, const double* v, int nl) {
+  int best = 0;
+  double bd = fabs(x - v[0]);
+  for (int j = 1; j < nl; ++j) {
+    const double d = fabs(x - v[j]);
+    if (d < bd) { bd = d; best = j; }
+  }
+  if (!isfinite(bd)) return best;
+  int have = 0;
+  double bk = 0.0;
+  for (int j = 0; j < nl; ++j) {
+    const double h = x - v[j];
+    if (fabs(h) != bd) continue;
+    const double e = two_sum_err(x, -v[j], h);
+    const double key = h < 0.0 ? -e : e;   /* h == 0 gives e == 0 */
+    if (!have || key < bk) { bk = key; best = j; have = 1; }
+  }
+  return best;
+}
+
 /* ------------------------------------------------------------ LUT16 */
 int oracle_lut16_indices(const uint16_t* w, const uint16_t* scales, const uint16_t* lut,
                          int64_t n, int64_t k, uint8_t* idx) {
@@ -142,19 +180,11 @@ int oracle_lut16_indices(const uint16_t* w, const uint16_t* scales, const uint16
 #pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < n; ++r)
     for (int64_t gi = 0; gi < g; ++gi) {
-      float v[16];
-      double s = bf16_val(scales[r * g + gi]);
-      for (int j = 0; j < 16; ++j) v[j] = (float)(s * bf16_val(lut[(r * g + gi) * 16 + j]));
-      for (int i = 0; i < 64; ++i) {
-        float wi = (float)bf16_val(w[r * k + gi * 64 + i]);
-        int best = 0;
-        float bd = fabsf(wi - v[0]);
-        for (int j = 1; j < 16; ++j) {
-          float d = fabsf(wi - v[j]);
-          if (d < bd) { bd = d; best = j; }
-        }
-        idx[r * k + gi * 64 + i] = (uint8_t)best;
-      }
+      double v[16];
+      const double s = bf16_val(scales[r * g + gi]);
+      for (int j = 0; j < 16; ++j) v[j] = s * bf16_val(lut[(r * g + gi) * 16 + j]); /* exact */
+      for (int i = 0; i < 64; ++i)
+        idx[r * k + gi * 64 + i] = (uint8_t)nearest_level(bf16_val(w[r * k + gi * 64 + i]), v, 16);
     }
   return 0;
 }
@@ -167,18 +197,12 @@ int oracle_signmag8_indices(const uint16_t* w, const uint16_t* cb, int64_t n, in
 #pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < n; ++r)
     for (int64_t gi = 0; gi < g; ++gi) {
-      float m[8];
-      for (int j = 0; j < 8; ++j) m[j] = (float)f16_val(cb[(r * g + gi) * 8 + j]);
+      double m[8];
+      for (int j = 0; j < 8; ++j) m[j] = f16_val(cb[(r * g + gi) * 8 + j]);
       for (int i = 0; i < 32; ++i) {
-        float wi = (float)bf16_val(w[r * k + gi * 32 + i]);
-        float a = fabsf(wi);
-        int best = 0;
-        float bd = fabsf(a - m[0]);
-        for (int j = 1; j < 8; ++j) {
-          float d = fabsf(a - m[j]);
-          if (d < bd) { bd = d; best = j; }
-        }
-        nib[r * k + gi * 32 + i] = (uint8_t)(((wi < 0.0f) ? 8 : 0) | best);
+        const double wi = bf16_val(w[r * k + gi * 32 + i]);
+        const int best = nearest_level(fabs(wi), m, 8);
+        nib[r * k + gi * 32 + i] = (uint8_t)(((wi < 0.0) ? 8 : 0) | best);
       }
     }
   return 0;

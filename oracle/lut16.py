@@ -10,14 +10,14 @@ Oracle (test infrastructure).  K-means page:
 
 Format (one reading, listed in the design notes): per group a bf16 scale
 ``s`` (the group's absmax) and 16 bf16 normalised levels ``L_j`` in [-1, 1];
-the group's levels are ``v_j = s * L_j`` (exact in fp32: 8 x 8 significant
-bits) and the reconstructed weight is ``RNE_bf16(v_idx)``.
+the group's levels are the exact products ``v_j = s * L_j`` (8 x 8
+significant bits) and the reconstructed weight is ``RNE_bf16(v_idx)``.
 
-The nearest-level decision is taken in fp32: ``d_j = |fl32(w - v_j)|`` and the
-lowest j with the smallest ``d_j`` wins.  fp32 is the precision the GPU kernel
-decides in; the subtraction is exact unless w and v_j are more than ~2**16
-apart in magnitude, and ``tests/test_oracle_lut16.py`` shows that the fp32
-decision equals the exact-rational argmin on the configs' distributions.
+The index of a weight is the lowest j minimising the exact distance
+``|w - v_j|`` (``oracle.nearest``), for every finite weight, scale and table:
+also for weights far outside the levels' range and for tables whose levels
+are far apart in magnitude, where a distance rounded to fp32 or fp64 no
+longer separates the levels.
 
 The fit (used only to make test data) is the k-means page's per-block 1D
 k-means with the seeding and iteration count that the int4-g32 page
@@ -35,6 +35,7 @@ are "parity unpinned".
 import numpy as np
 
 from .bits import bf16_to_f64, f32_to_bf16_bits_exact, rne_bf16
+from .nearest import nearest
 from .packing import pack, unpack
 
 GROUP = 64
@@ -42,25 +43,25 @@ N_LEVELS = 16
 LLOYD_ITERS = 25
 
 
-def levels32(s_bits, lut_bits):
-    """Group levels ``v_j = s * L_j`` as float32 (exact).  s [N, G], L [N, G, 16]."""
+def levels(s_bits, lut_bits):
+    """Group levels ``v_j = s * L_j`` as fp64 (exact: at most 16 significant
+    bits, exponents between -266 and 255).  s [N, G], L [N, G, 16]."""
     s = bf16_to_f64(s_bits)[..., None]
     L = bf16_to_f64(lut_bits)
-    return (s * L).astype(np.float32)
+    return s * L
 
 
 def indices(w_bits, s_bits, lut_bits, chunk_rows=256):
-    """Nearest level with the fp32 decision rule; w [N, K] -> idx uint8 [N, K]."""
+    """Exact nearest level, lowest index on ties; w [N, K] -> idx uint8 [N, K]."""
     w_bits = np.asarray(w_bits)
     n, k = w_bits.shape
     g = k // GROUP
     out = np.empty((n, k), dtype=np.uint8)
     for r0 in range(0, n, chunk_rows):
         r1 = min(n, r0 + chunk_rows)
-        w = bf16_to_f64(w_bits[r0:r1]).astype(np.float32).reshape(r1 - r0, g, GROUP)
-        v = levels32(s_bits[r0:r1], lut_bits[r0:r1])                   # [r, G, 16]
-        d = np.abs(w[..., :, None] - v[..., None, :])                   # fp32 subtraction
-        out[r0:r1] = np.argmin(d, axis=-1).astype(np.uint8).reshape(r1 - r0, k)
+        w = bf16_to_f64(w_bits[r0:r1]).reshape(r1 - r0, g, GROUP)
+        v = levels(s_bits[r0:r1], lut_bits[r0:r1])                     # [r, G, 16]
+        out[r0:r1] = nearest(w, v).astype(np.uint8).reshape(r1 - r0, k)
     return out
 
 

@@ -14,9 +14,11 @@ Readings (listed in the design notes): the group's 8 magnitudes are stored
 as fp16 (the page's 8-bit parameter code that regenerates a parametric table
 is not stored; the Lloyd-refined levels are); inside the nibble bit 3 is the
 sign and bits 0..2 the magnitude index; the sign bit is ``w < 0`` (so -0.0
-gets sign 0); the nearest-magnitude decision is taken in fp32,
-``d_j = |fl32(|w| - M_j)|``, lowest j on a tie; dequant is exactly
-``±M[mag]`` in fp16 (so sign 1 with M = 0 gives -0.0).
+gets sign 0); the magnitude index is the lowest j minimising the exact
+distance ``||w| - M_j|`` (``oracle.nearest``; a magnitude of +inf, which the
+fit produces for groups beyond the fp16 range, is infinitely far from every
+finite weight); dequant is exactly ``±M[mag]`` in fp16 (so sign 1 with M = 0
+gives -0.0).
 
 The fit (test data only) is the page's "cold start" (section 1.4: quantile
 initial levels, then Lloyd): ``c_k = sorted(|w|)[4k + 2]``, 25 Lloyd rounds
@@ -28,6 +30,7 @@ import numpy as np
 
 from .bits import bf16_to_f64, f16_to_f64, rne_fp16
 from .lut16 import lloyd, quantile_init, LLOYD_ITERS
+from .nearest import nearest
 from .packing import pack, unpack
 
 GROUP = 32
@@ -42,10 +45,9 @@ def indices(w_bits, cb_bits, chunk_rows=256):
     out = np.empty((n, k), dtype=np.uint8)
     for r0 in range(0, n, chunk_rows):
         r1 = min(n, r0 + chunk_rows)
-        w = bf16_to_f64(w_bits[r0:r1]).astype(np.float32).reshape(r1 - r0, g, GROUP)
-        m = f16_to_f64(cb_bits[r0:r1]).astype(np.float32)               # [r, G, 8]
-        d = np.abs(np.abs(w)[..., :, None] - m[..., None, :])           # fp32
-        mag = np.argmin(d, axis=-1).astype(np.uint8)
+        w = bf16_to_f64(w_bits[r0:r1]).reshape(r1 - r0, g, GROUP)
+        m = f16_to_f64(cb_bits[r0:r1])                                  # [r, G, 8]
+        mag = nearest(np.abs(w), m).astype(np.uint8)
         sign = (w < 0).astype(np.uint8)
         out[r0:r1] = ((sign << 3) | mag).reshape(r1 - r0, k)
     return out

@@ -107,3 +107,63 @@ def bf16_int_parts(bits):
     a = np.where(e == 0, -133, e - 127 - 7)
     sig = np.where(b & 0x8000, -sig, sig)
     return sig, a
+
+
+def _scaled_ints(sig, a, shift):
+    """Python integers sig * 2**(a + shift) (exact; a + shift >= 0)."""
+    sig = np.asarray(sig, dtype=object)
+    e = np.asarray(a + shift, dtype=np.int64)
+    assert np.all(e >= 0)
+    return sig * np.vectorize(lambda t: 1 << int(t), otypes=[object])(e)
+
+
+def f16_int_parts(bits):
+    """Vectorised: fp16 bits -> (signed integer significand, exponent) with
+    value = sig * 2**a exactly (zeros give 0).  Infinities are not decoded:
+    callers replace them."""
+    b = np.asarray(bits, dtype=np.int64)
+    e = (b >> 10) & 0x1F
+    m = b & 0x3FF
+    sig = np.where(e == 0, m, m + 1024)
+    a = np.where(e == 0, -24, e - 15 - 10)
+    sig = np.where(b & 0x8000, -sig, sig)
+    return sig, a
+
+
+def nearest_int_argmin(x_int, lev_int):
+    """Lowest index of the smallest |x - v| on Python integers.
+    x_int [..., G], lev_int [..., L] (object arrays) -> int64 [..., G]."""
+    d = np.abs(x_int[..., :, None] - lev_int[..., None, :])
+    return np.argmin(d, axis=-1).astype(np.int64)
+
+
+# Every bf16 value times 2**133 and every product of two bf16 values times
+# 2**266 is an integer; fp16 values times 2**24 are integers.
+BIG_INF = 1 << 2000   # stands for +inf: farther than any finite level
+
+
+def lut16_exact_indices(w_bits, s_bits, lut_bits):
+    """Brute-force exact nearest level of LUT16 on integers: w [rows, 64],
+    s [rows, 1], L [rows, 1, 16] (one group per row)."""
+    ws, wa = bf16_int_parts(w_bits)
+    X = _scaled_ints(ws, wa, 266)                                     # w * 2**266
+    ss, sa = bf16_int_parts(np.asarray(s_bits)[:, 0])
+    ls, la = bf16_int_parts(np.asarray(lut_bits)[:, 0, :])
+    V = _scaled_ints(ss[:, None] * ls, sa[:, None] + la, 266)         # s L * 2**266
+    return nearest_int_argmin(X, V)
+
+
+def signmag8_exact_indices(w_bits, cb_bits):
+    """Brute-force exact sign + nearest magnitude on integers: w [rows, 64]
+    (two groups of 32 per row), cb [rows, 2, 8] fp16 bits (+inf allowed)."""
+    w_bits = np.asarray(w_bits)
+    rows = w_bits.shape[0]
+    ws, wa = bf16_int_parts(w_bits)
+    A = np.abs(_scaled_ints(ws, wa, 133)).reshape(rows, 2, 32)        # |w| * 2**133
+    cb = np.asarray(cb_bits)
+    ms, ma = f16_int_parts(cb)
+    M = _scaled_ints(ms, ma, 133)                                     # M * 2**133
+    M = np.where(cb == 0x7C00, BIG_INF, M)
+    mag = nearest_int_argmin(A, M).reshape(rows, 64)
+    neg = ((w_bits & 0x8000) != 0) & ((w_bits & 0x7FFF) != 0)   # w < 0 (-0.0 is not)
+    return (mag | np.where(neg, 8, 0)).astype(np.uint8)

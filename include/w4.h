@@ -34,8 +34,10 @@
  *    (fixed reduction order, no atomics).
  *  - Weights are row-major [n][k] (n = output features, k = input features,
  *    the layout of a PyTorch Linear weight).  A group is `group` consecutive
- *    weights along k; k must be a multiple of 64 for every codec in the
- *    quantize, dequant and matrix calls (the SIGNMAG8 fits need 32).
+ *    weights along k; k must be a multiple of the codec's group (64, or 32
+ *    for SIGNMAG8) in the quantize, dequant and fit calls, and a multiple of
+ *    64 for every codec in the matrix calls (w4_gemv, w4_gemm, w4_linear and
+ *    the batched GEMV), whose kernels step over k in 64-weight units.
  *  - Preconditions that are not checked: finite inputs; buffers contiguous,
  *    of the sizes stated, and not overlapping one another.
  *
@@ -116,12 +118,18 @@ int32_t w4_group_size(int32_t codec);
  *             idx = the lowest j minimising |w - (s/8)(j-8)| over the exact
  *             codes; an all-zero group gets s = +0 and idx 8.  codebook: NULL.
  *   LUT16:    reads scales (bf16 [n][k/64]) and codebook (bf16 [n][k/64][16]);
- *             idx = the lowest j minimising |fl32(w - s*L_j)| (fp32 decision).
+ *             idx = the lowest j minimising the exact distance |w - s*L_j|
+ *             (the levels s*L_j as exact real products), for every finite
+ *             weight, scale and table: also weights beyond the levels' range
+ *             and levels far apart in magnitude.
  *   LUT16S:   as LUT16 with the one table codebook (bf16 [16]) for every group.
  *   DYADIC5:  not provided here (W4_EUNSUPPORTED): w4_quantize_dyadic5 writes
  *             both of its index planes.
- *   SIGNMAG8: reads codebook (fp16 [n][k/32][8]); scales: NULL;
- *             nibble = (w < 0) << 3 | the lowest j minimising |fl32(|w| - M_j)|.
+ *   SIGNMAG8: reads codebook (fp16 [n][k/32][8], finite or +inf, the fit's
+ *             output beyond the fp16 range); scales: NULL;
+ *             nibble = (w < 0) << 3 | the lowest j minimising the exact
+ *             ||w| - M_j| (a +inf magnitude is never nearer than a finite one;
+ *             a group of only +inf magnitudes gives index 0).
  * w: bf16 [n][k], 16-byte aligned.  packed: uint8 [n][k/2], 16-byte aligned.
  * scales: 2-byte aligned.  codebook: 16-byte aligned.
  * n == 0 or k == 0: nothing to do, returns W4_OK.
@@ -134,7 +142,8 @@ w4_status w4_quantize_pack(int32_t codec, int64_t n, int64_t k, const uint16_t* 
  * w4_unpack_dequant -- rebuild the dense weight.  [DG] sec. 2.2, 2.5 (unpack
  * kernel: packed byte -> nibble split -> step -> bf16); [KM] sec. 2.2 (LUT
  * decode); [G32] sec. 2 (dense fp16 weight).
- * out: bf16 [n][k] for DYADIC and LUT16, fp16 [n][k] for SIGNMAG8; 16-byte aligned.
+ * out: bf16 [n][k] for DYADIC, LUT16, LUT16S and DYADIC5, fp16 [n][k] for
+ * SIGNMAG8; 16-byte aligned.
  * packed and codebook 16-byte aligned, scales 2-byte aligned.
  */
 w4_status w4_unpack_dequant(int32_t codec, int64_t n, int64_t k, const uint8_t* packed,
@@ -251,12 +260,12 @@ w4_status w4_signmag8_fit_warm(int64_t n, int64_t k, const uint16_t* w, uint16_t
  * x: bf16 [m][k], 16-byte aligned.  m: 1..16 (m == 0: nothing to do).
  * y: [m][n] of y_dtype W4_F32 (4-byte aligned) or W4_BF16 (RNE, 2-byte aligned).
  * The result is within 1e-3 * sum_c |x w_hat| + 1e-6 of the exact sum, and the
- * same inputs always give the same bits.
+ * same inputs always give the same bits.  k == 0 (with m, n > 0): y = +0.
  * Workspace: with m >= 2 and n <= 65536 the call may split k into S <= 32
  * slices across blocks and enqueue a second kernel that adds the slices' fp32
  * partial sums in slice order; the partials use a device buffer of
- * S * m * n * 4 bytes that the library keeps per (device, stream) as for
- * w4_gemm (grown on demand with hipMalloc, never freed).  m == 1 uses none.
+ * S * m * n * 4 bytes that the library keeps per (device, stream) exactly as
+ * for w4_gemm (see there).  m == 1 uses none.
  * Additional error: W4_EHIP when that buffer cannot be allocated.
  */
 w4_status w4_gemv(int32_t codec, int64_t n, int64_t k, const uint8_t* packed,
@@ -268,19 +277,26 @@ w4_status w4_gemv(int32_t codec, int64_t n, int64_t k, const uint8_t* packed,
  * Y[i][r] = sum_c X[i][c] * w_hat[r][c] with bf16 MFMA and fp32 accumulation;
  * the weight tiles are rebuilt into LDS.  [KM] sec. 4.1 (the 4-bit mixed kernel
  * band, m up to 256).  Same arguments as w4_gemv; m >= 1 (tuned for m >= 128).
+ * k == 0 (with m, n > 0): y = +0.
  * Workspace: the call enqueues up to three kernels (an activation re-layout,
  * the product, and an in-order sum of the k-split partials) that use a device
  * buffer of ceil(m/B) * B * k * 2 bytes plus, when k is split S <= 8 ways,
  * S * ceil(m/B) * B * ceil(n/128) * 128 * 4 bytes, where B, the batch rows
  * of a block, is 128 when m <= 128, k is a multiple of 128 and the codec is
  * not SIGNMAG8, and 256 otherwise.  The library keeps one such buffer per
- * (device, stream), grown on demand with hipMalloc (growing waits for the
- * stream and frees the old buffer) and never freed, so calls on one stream
- * are ordered and calls on different streams never share it.
+ * (device, stream): allocated with hipMalloc on first use, replaced by a new
+ * one at least twice as large when a call needs more.  Replaced buffers are
+ * never freed (work enqueued earlier, or a graph captured earlier, may still
+ * use them), so growing never waits for the stream; nothing is freed before
+ * the process ends, also for streams the caller destroys.  Calls on one
+ * stream are ordered and share the buffer; calls on different streams never
+ * do.
  * Graph capture: a call that would create or grow the buffer cannot be
  * captured (hipMalloc); make one call of each shape to be captured on the
  * capture stream before capturing.  After that, calls only enqueue kernels
- * (no memset, no allocation).
+ * (no memset, no allocation).  A captured graph keeps using the buffer of
+ * its capture stream whatever stream it is replayed on: replays must not
+ * overlap one another or eager calls on the capture stream.
  * Additional error: W4_EHIP when the workspace cannot be allocated.
  */
 w4_status w4_gemm(int32_t codec, int64_t n, int64_t k, const uint8_t* packed,
@@ -338,7 +354,9 @@ typedef struct {
   int32_t m;           /* the plan's m; w4_gemv_batched must be called with it */
   int32_t tile_rows;   /* rows per work tile: 64, or 32 / 16 (m == 1 only)
                           when 64-row tiles would give fewer than 1024 */
-  int32_t reserved;    /* 0 */
+  int32_t flags;       /* bit 0: some problem's k is not a multiple of 256
+                          (the kernel then zeroes the lanes past its k);
+                          written by the plan like the rest of the record */
 } w4_gemv_batch_info;
 
 w4_status w4_gemv_batched_plan(int32_t codec, int32_t m, int32_t y_dtype,

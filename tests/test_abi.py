@@ -195,3 +195,23 @@ def test_batched_plan_validation(w4):
     assert w4._lib.w4_gemv_batched(0, 16, 0, ctypes.c_void_p(16), ctypes.byref(m16_rows), None) == 1
     empty = w4.W4BatchInfo(0, 0, 0, 0, 1)
     assert w4._lib.w4_gemv_batched(0, 1, 0, None, ctypes.byref(empty), None) == 0
+
+
+def test_signmag8_group_rule(w4):
+    """SIGNMAG8 takes k a multiple of its group of 32 in quantize and dequant
+    (a null buffer then is the first error), but the matrix calls need 64."""
+    E = {"inval": 1, "shape": 2}
+    P = ctypes.c_void_p
+    assert w4._lib.w4_quantize_pack(2, 4, 96, None, None, None, None, None) == E["inval"]
+    assert w4._lib.w4_unpack_dequant(2, 4, 96, None, None, None, None, None) == E["inval"]
+    assert w4._lib.w4_quantize_pack(2, 4, 80, None, None, None, None, None) == E["shape"]
+    assert w4._lib.w4_quantize_pack(0, 4, 96, None, None, None, None, None) == E["shape"]
+    assert _gemv(w4, codec=2, k=96, scales=None) == E["shape"]
+    assert _gemv(w4, codec=2, k=96, scales=None, fn="w4_gemm") == E["shape"]
+
+
+def test_batched_flags_checked(w4):
+    """w4_gemv_batched rejects an info record whose flags hold bits the plan
+    never writes (before any launch)."""
+    info = w4.W4BatchInfo(total_tiles=1, k_min=64, k_max=64, count=1, m=1, tile_rows=64, flags=2)
+    assert w4._lib.w4_gemv_batched(0, 1, 0, ctypes.c_void_p(16), ctypes.byref(info), None) == 1

@@ -10,8 +10,8 @@ quantized by the library; the oracle then checks, on the host:
   fp64 oracle on the same dequantized weights, for every sampled output,
   computed one row at a time.
 Codebooks that the library takes as inputs (LUT16 levels, SIGNMAG8
-magnitudes) come from the oracle's fit.  The 2B model's 224 square matrices
-are represented by 16 of them (same shape, same kernels, same launch).
+magnitudes) come from the oracle's fit, or from the library's fit checked
+against the oracle's.
 """
 
 import numpy as np
@@ -233,35 +233,47 @@ def test_fullsize_signmag8_warm():
 
 # ------------------------------------------------------------ 2B SIGNMAG8
 def test_fullsize_signmag8_stack(w4):
-    """2048^2 matrices, Student-t nu = 5 at sigma 0.02, group 32 sign +
-    3-bit magnitude: the fp16 codebooks fitted on the GPU, equal to the
-    oracle's fit on every group; dense dequant and one batched m = 1 GEMV
-    launch over 16 matrices."""
+    """The 2B model's 224 matrices of 2048^2, Student-t nu = 5 at sigma 0.02,
+    group 32 sign + 3-bit magnitude, exactly as bench.py times them: fp16
+    codebooks fitted on the GPU (equal to the oracle's fit on every group of
+    the first 16 matrices and on the sampled rows of the others), packed
+    bytes and dense dequant bit-exact on sampled rows, then the one batched
+    m = 1 launch over all 224 (7168 tiles of 64 rows: the plan keeps 64-row
+    tiles, so this runs gemv_kernel<SIGNMAG8, 1, true, 1, false>)."""
     n = k = 2048
-    count = 16
+    count = 224
     report("fullsize_signmag8", matrices=count)
     probs, checks = [], []
     for i in range(count):
         w = synthetic.student_t_bf16_device((n, k), 5, 0.02, synthetic.seed(4, i, 0))
-        cb = native.signmag8_fit(host_bits(w))
         cb_dev = w4.w4_signmag8_fit(w)
-        torch.cuda.synchronize()
-        assert np.array_equal(host_bits(cb_dev), cb)
         p, _ = w4.w4_quantize_pack(w, w4.W4_SIGNMAG8, codebook=cb_dev)
-        d = w4.w4_unpack_dequant(p, w4.W4_SIGNMAG8, codebook=cb_dev)
         torch.cuda.synchronize()
-        rows = _rows(n, 7600 + i)
+        rows = _rows(n, 7600 + i, count=24 if i < 16 else 6)
         sel = torch.as_tensor(rows, device="cuda")
-        nib = native.signmag8_indices(_host_rows(w, rows), cb[rows])
+        w_rows = _host_rows(w, rows)
+        if i < 16:
+            cb = native.signmag8_fit(host_bits(w))
+            assert np.array_equal(host_bits(cb_dev), cb)
+            cb_rows = cb[rows]
+        else:
+            cb_rows = native.signmag8_fit(w_rows)
+            assert np.array_equal(host_bits(cb_dev.index_select(0, sel)), cb_rows)
+        nib = native.signmag8_indices(w_rows, cb_rows)
         assert np.array_equal(host_u8(p.index_select(0, sel)), packing.pack(nib))
-        assert np.array_equal(host_bits(d.index_select(0, sel)),
-                              signmag8.dequant_from_indices(nib, cb[rows]))
-        del w, d
+        if i < 16:
+            d = w4.w4_unpack_dequant(p, w4.W4_SIGNMAG8, codebook=cb_dev)
+            torch.cuda.synchronize()
+            assert np.array_equal(host_bits(d.index_select(0, sel)),
+                                  signmag8.dequant_from_indices(nib, cb_rows))
+            del d
+        del w
         x = synthetic.normal_bf16_device((1, k), 1.0, synthetic.seed(4, i, 1))
         y = torch.full((1, n), float("nan"), device="cuda")
         probs.append({"packed": p, "codebook": cb_dev, "x": x, "y": y})
-        checks.append((rows, signmag8.dequant_values(cb[rows], nib)))
+        checks.append((rows, signmag8.dequant_values(cb_rows, nib)))
     batch = w4.w4_gemv_batched_plan(probs, w4.W4_SIGNMAG8)
+    assert batch.info.tile_rows == 64 and batch.info.total_tiles == count * n // 64
     batch()
     torch.cuda.synchronize()
     for pr, (rows, w_hat) in zip(probs, checks):

@@ -13,6 +13,7 @@ import torch
 
 import synthetic
 from oracle import bits, dyadic, dyadic5, lut16, matmul, native, packing, signmag8, warmstart
+from tests import sweeps
 from tests.gpu_util import dev_bf16, dev_f16, dev_u8, host_bits, host_f32, host_u8, report
 
 pytestmark = pytest.mark.gpu
@@ -67,17 +68,11 @@ def test_dyadic_quantize_exhaustive_values(w4):
     """Every finite bf16 value of magnitude <= s, both signs, in groups whose
     absmax is s, for scales with plain, full and sparse mantissas, the
     smallest subnormal and normal, the largest finite value and huge and tiny
-    exponents: indices and scales bit-exact against the oracle (which the CPU
-    tests pin to exact-rational argmin)."""
+    exponents: indices and scales bit-exact against the C oracle, which the
+    CPU tests check against the numpy oracle on these same inputs
+    (tests/sweeps.py; the numpy oracle is pinned to exact-rational argmin)."""
     report("dyadic_quantize_exhaustive")
-    allpos = np.arange(0x0000, 0x7F80, dtype=np.uint32)          # +0 .. max finite
-    for sb in (0x3F80, 0x3FFF, 0x3C23, 0x3A5B, 0x0001, 0x0080, 0x00FF, 0x7F7F, 0x7A01, 0x0400):
-        vals = allpos[allpos <= sb].astype(np.uint16)
-        vals = np.concatenate([vals, vals | 0x8000])
-        pad = (-len(vals)) % 63
-        vals = np.concatenate([vals, np.zeros(pad, np.uint16)]).reshape(-1, 63)
-        w = np.concatenate([np.full((vals.shape[0], 1), sb, np.uint16), vals], axis=1)
-        w = np.ascontiguousarray(w)
+    for sb, w in sweeps.dyadic_cases():
         p, s = w4.w4_quantize_pack(dev_bf16(w), w4.W4_DYADIC)
         torch.cuda.synchronize()
         idx_o, s_o = native.dyadic_quantize(w)
@@ -85,31 +80,12 @@ def test_dyadic_quantize_exhaustive_values(w4):
         assert np.array_equal(host_u8(p), packing.pack(idx_o)), hex(sb)
 
 
-def _groups_with_absmax(sb, cols):
-    """Every finite bf16 value of magnitude <= sb (both signs), cols - 1 per
-    row after a leading sb, so that every row's absmax is sb."""
-    allpos = np.arange(0x0000, 0x7F80, dtype=np.uint32)
-    vals = allpos[allpos <= sb].astype(np.uint16)
-    vals = np.concatenate([vals, vals | 0x8000])
-    pad = (-len(vals)) % (cols - 1)
-    vals = np.concatenate([vals, np.zeros(pad, np.uint16)]).reshape(-1, cols - 1)
-    return np.ascontiguousarray(
-        np.concatenate([np.full((vals.shape[0], 1), sb, np.uint16), vals], axis=1))
-
-
-def _all_finite_bf16(cols):
-    v = np.arange(0x0000, 0x7F80, dtype=np.uint32).astype(np.uint16)
-    v = np.concatenate([v, v | 0x8000])
-    pad = (-len(v)) % cols
-    return np.ascontiguousarray(np.concatenate([v, np.zeros(pad, np.uint16)]).reshape(-1, cols))
-
-
 def test_dyadic5_quantize_exhaustive_values(w4):
     """DYADIC5 at widths 3, 4 and 5: every finite bf16 value of magnitude <= s
     in groups of absmax s, for the same kinds of scales as the 4-bit test."""
     report("dyadic5_quantize_exhaustive")
     for sb in (0x3F80, 0x3FFF, 0x3C23, 0x0001, 0x0080, 0x7F7F, 0x7A01):
-        w = _groups_with_absmax(sb, 64)
+        w = sweeps.groups_with_absmax(sb, 64)
         widths = np.resize(np.array([3, 4, 5], np.uint8), (w.shape[0], 1))
         p, m, s = w4.w4_quantize_dyadic5(dev_bf16(w), dev_u8(widths))
         torch.cuda.synchronize()
@@ -121,27 +97,23 @@ def test_dyadic5_quantize_exhaustive_values(w4):
 
 
 def test_lut16_quantize_exhaustive_values(w4):
-    """LUT16 and LUT16S nearest level (fp32 decision): every finite bf16
-    weight against tables under scales from the smallest subnormal to the
-    largest finite bf16 (where |w - s L| overflows fp32 on both sides)."""
+    """LUT16 and LUT16S exact nearest level: every finite bf16 weight against
+    sorted tables, tables with levels far apart in magnitude, symmetric pairs
+    and unsorted entries beyond [-1, 1], under scales from the smallest
+    subnormal to the largest finite bf16 (tests/sweeps.py; the CPU tests pin
+    the C checker to integer brute force on exactly these inputs)."""
     report("lut16_quantize_exhaustive")
-    w = _all_finite_bf16(64)
-    g = np.random.default_rng(71)
-    for sb in (0x3F80, 0x7F7F, 0x0001, 0x3C23):
-        L = bits.rne_bf16(np.sort(g.uniform(-1, 1, (w.shape[0], 16)), axis=-1))
-        L[:, 0] = 0xBF80          # -1
-        L[:, 15] = 0x3F80         # +1
-        L[::7, 3:5] = 0x0000      # duplicated levels
-        s = np.full((w.shape[0], 1), sb, np.uint16)
-        L3 = np.ascontiguousarray(L.reshape(w.shape[0], 1, 16))
-        p, _ = w4.w4_quantize_pack(dev_bf16(w), w4.W4_LUT16, scales=dev_bf16(s), codebook=dev_bf16(L3))
+    for name, w, s, L in sweeps.lut16_cases():
+        p, _ = w4.w4_quantize_pack(dev_bf16(w), w4.W4_LUT16, scales=dev_bf16(s),
+                                   codebook=dev_bf16(L))
         torch.cuda.synchronize()
-        assert np.array_equal(host_u8(p), packing.pack(native.lut16_indices(w, s, L))), hex(sb)
-        T = L[5]
-        p, _ = w4.w4_quantize_pack(dev_bf16(w), w4.W4_LUT16S, scales=dev_bf16(s), codebook=dev_bf16(T))
+        assert np.array_equal(host_u8(p), packing.pack(native.lut16_indices(w, s, L))), name
+    for name, w, s, T in sweeps.lut16s_cases():
+        p, _ = w4.w4_quantize_pack(dev_bf16(w), w4.W4_LUT16S, scales=dev_bf16(s),
+                                   codebook=dev_bf16(T))
         torch.cuda.synchronize()
-        tables = np.ascontiguousarray(np.broadcast_to(T, L.shape))
-        assert np.array_equal(host_u8(p), packing.pack(native.lut16_indices(w, s, tables))), hex(sb)
+        tables = np.ascontiguousarray(np.broadcast_to(T, (w.shape[0], 1, 16)))
+        assert np.array_equal(host_u8(p), packing.pack(native.lut16_indices(w, s, tables))), name
 
 
 def test_lut16_dequant_extreme_scales_and_tables(w4):
@@ -171,28 +143,14 @@ def test_lut16_dequant_extreme_scales_and_tables(w4):
 
 
 def test_signmag8_quantize_exhaustive_values(w4):
-    """SIGNMAG8 sign + nearest magnitude (fp32 decision): every finite bf16
-    weight against codebooks with subnormal, duplicated, zero and maximal
-    (65504) fp16 magnitudes."""
+    """SIGNMAG8 sign + exact nearest magnitude: every finite bf16 weight
+    against codebooks with subnormal, duplicated, zero, unsorted, maximal
+    (65504) and +inf fp16 magnitudes (tests/sweeps.py, pinned on the CPU)."""
     report("signmag8_quantize_exhaustive")
-    w = _all_finite_bf16(64)
-    ng = 2 * w.shape[0]  # groups of 32
-    g = np.random.default_rng(72)
-    for kind in range(3):
-        if kind == 0:
-            mags = np.sort(g.uniform(0, 0.1, (ng, 8)), axis=-1)
-        elif kind == 1:
-            mags = np.sort(2.0 ** g.uniform(-26, -10, (ng, 8)), axis=-1)
-        else:
-            mags = np.sort(g.uniform(0, 65504, (ng, 8)), axis=-1)
-            mags[:, 7] = 65504.0
-        cb = bits.rne_fp16(mags)
-        cb[::5, 2] = cb[::5, 1]   # a duplicated level
-        cb[::3, 0] = 0
-        cb = np.ascontiguousarray(cb.reshape(w.shape[0], 2, 8))
+    for name, w, cb in sweeps.signmag8_cases():
         p, _ = w4.w4_quantize_pack(dev_bf16(w), w4.W4_SIGNMAG8, codebook=dev_f16(cb))
         torch.cuda.synchronize()
-        assert np.array_equal(host_u8(p), packing.pack(native.signmag8_indices(w, cb))), kind
+        assert np.array_equal(host_u8(p), packing.pack(native.signmag8_indices(w, cb))), name
 
 
 @pytest.mark.parametrize("n,k", [(2048, 2048), (37, 320), (6, 128)])
@@ -210,15 +168,19 @@ def test_dyadic_dequant_bitexact(w4, n, k):
 
 
 def test_dyadic_dequant_exhaustive_scales(w4):
-    """Every finite non-negative bf16 scale x every index, on the GPU."""
+    """Every finite bf16 scale of either sign x every index, on the GPU (a
+    caller may pass its own scales; code 8 rebuilds to +0 for every scale,
+    also for the negative ones of 2**120 and more, which take the wide
+    rebuild).  Rows are ordered so that waves mix plain and wide scales."""
     allb = bits.all_finite_bf16()
-    pos = allb[(allb & 0x8000) == 0]
-    n = len(pos)
+    n = len(allb)
     idx = np.tile(np.arange(16, dtype=np.uint8), (n, 4))
     report("dyadic_dequant_exhaustive", n=n)
-    out = w4.w4_unpack_dequant(dev_u8(packing.pack(idx)), w4.W4_DYADIC, scales=dev_bf16(pos[:, None]))
+    out = w4.w4_unpack_dequant(dev_u8(packing.pack(idx)), w4.W4_DYADIC, scales=dev_bf16(allb[:, None]))
     torch.cuda.synchronize()
-    assert np.array_equal(host_bits(out), dyadic.dequant_from_indices(idx, pos[:, None]))
+    got = host_bits(out)
+    assert np.array_equal(got, dyadic.dequant_from_indices(idx, allb[:, None]))
+    assert np.all(got[:, 8::16] == 0)
 
 
 def _gemv_check(y, x_bits, w_hat, bf16_out):
@@ -766,3 +728,154 @@ def test_gemv_batched_many_problems(w4, m):
     for pr, (x, w_hat) in zip(probs, refs):
         if w_hat is not None:
             _gemv_check(pr["y"], x, w_hat, False)
+
+
+def _random_codec_case(codec, n, k, seed):
+    """Random indices with ordinary side data (scales of Gaussian weights'
+    groups, sorted tables in [-1, 1], fp16 magnitudes below 0.1): (packed,
+    side tables, fp64 dequantized weight), cheap to build for many rows."""
+    g = np.random.default_rng(seed)
+    s = bits.rne_bf16(np.abs(g.normal(0.05, 0.01, (n, k // 64))))
+    if codec == 0:
+        idx = g.integers(0, 16, (n, k)).astype(np.uint8)
+        return (packing.pack(idx), dict(scales=dev_bf16(s)),
+                bits.bf16_to_f64(dyadic.dequant_from_indices(idx, s)))
+    if codec in (1, 3):
+        idx = g.integers(0, 16, (n, k)).astype(np.uint8)
+        if codec == 3:
+            T = bits.rne_bf16(np.sort(g.uniform(-1, 1, 16)))
+            tables = np.ascontiguousarray(np.broadcast_to(T, (n, k // 64, 16)))
+            return (packing.pack(idx), dict(scales=dev_bf16(s), codebook=dev_bf16(T)),
+                    bits.bf16_to_f64(lut16.dequant_from_indices(idx, s, tables)))
+        L = bits.rne_bf16(np.sort(g.uniform(-1, 1, (n, k // 64, 16)), axis=-1))
+        return (packing.pack(idx), dict(scales=dev_bf16(s), codebook=dev_bf16(L)),
+                bits.bf16_to_f64(lut16.dequant_from_indices(idx, s, L)))
+    if codec == 4:
+        idx5 = g.integers(0, 32, (n, k)).astype(np.uint8)
+        nib, msb = dyadic5.planes(idx5)
+        return (nib, dict(scales=dev_bf16(s), codebook=dev_u8(msb)),
+                bits.bf16_to_f64(dyadic5.dequant_from_indices(idx5, s)))
+    cb = bits.rne_fp16(np.sort(g.uniform(0, 0.1, (n, k // 32, 8)), axis=-1))
+    nib = g.integers(0, 16, (n, k)).astype(np.uint8)
+    return packing.pack(nib), dict(codebook=dev_f16(cb)), signmag8.dequant_values(cb, nib)
+
+
+# every m = 1 batched instantiation: the plan's tile height follows the total
+# row count (64-row tiles from 1024 tiles up, then 32, then 16), and each
+# height is its own kernel, gemv_kernel<CODEC, 64 / height, true, 1, RAGGED>
+@pytest.mark.parametrize("codec", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("height,rows", [(64, 65536 + 640), (32, 40000), (16, 3000)])
+@pytest.mark.parametrize("k", [128, 256])
+def test_gemv_batched_tile_heights(w4, codec, height, rows, k):
+    """m = 1 batched GEMV at every tile height for every codec, with k = 128
+    (a partial 256-k step: the RAGGED kernels) and k = 256 (whole steps);
+    small k keeps the oracle cheap.  The rows are split over 8 problems of
+    uneven height."""
+    report("gemv_batched_heights", codec=codec, height=height, rows=rows, k=k)
+    g = np.random.default_rng(3000 + codec)
+    cuts = np.sort(g.choice(np.arange(1, rows), 7, replace=False))
+    ns = np.diff(np.concatenate([[0], cuts, [rows]]))
+    probs, refs = [], []
+    for i, n in enumerate(ns):
+        p, side, w_hat = _random_codec_case(codec, int(n), k, 3100 + 10 * codec + i)
+        x = synthetic.normal_bf16((1, k), 1.0, 3200 + 10 * codec + i)
+        y = torch.full((1, int(n)), float("nan"), device="cuda")
+        probs.append(dict(packed=dev_u8(p), x=dev_bf16(x), y=y, **side))
+        refs.append((x, w_hat))
+    batch = w4.w4_gemv_batched_plan(probs, codec)
+    assert batch.info.tile_rows == height and batch.info.flags == (k % 256 != 0)
+    batch()
+    torch.cuda.synchronize()
+    for pr, (x, w_hat) in zip(probs, refs):
+        _gemv_check(pr["y"], x, w_hat, False)
+
+
+def _overflowing_case(codec, n, k, seed):
+    """Rows alternate between ordinary side data and side data whose first
+    three 64-groups rebuild to +-inf (LUT16 / LUT16S: scale and levels at the
+    bf16 maximum; SIGNMAG8: +inf magnitudes).  Returns packed, side tables and
+    the fp64 dequantized weight (inf on the overflowing rows)."""
+    g = np.random.default_rng(seed)
+    idx = g.integers(0, 16, (n, k)).astype(np.uint8)
+    if codec in (1, 3):
+        s = bits.rne_bf16(g.uniform(0.01, 0.05, (n, k // 64)))
+        s[1::2, :3] = 0x7F7F
+        L = bits.rne_bf16(np.sort(g.uniform(-1, 1, (n, k // 64, 16)), axis=-1))
+        L[1::2, :3, :] = np.where(g.integers(0, 2, (16,)) == 1, 0x7F7F, 0xFF7F)
+        if codec == 3:
+            T = bits.rne_bf16(np.sort(g.uniform(-1, 1, 16)))
+            T[[0, 15]] = [0xFF7F, 0x7F7F]   # s * T overflows for these two
+            # the ordinary rows use the same table: scales near 2^-120 keep
+            # their weights (at most about 2^8) and their sums well inside fp32
+            s[0::2] = bits.rne_bf16(g.uniform(1, 2, s[0::2].shape) * 2.0 ** -120)
+            tables = np.ascontiguousarray(np.broadcast_to(T, (n, k // 64, 16)))
+            return (packing.pack(idx), dict(scales=dev_bf16(s), codebook=dev_bf16(T)),
+                    bits.bf16_to_f64(lut16.dequant_from_indices(idx, s, tables)))
+        return (packing.pack(idx), dict(scales=dev_bf16(s), codebook=dev_bf16(L)),
+                bits.bf16_to_f64(lut16.dequant_from_indices(idx, s, L)))
+    cb = bits.rne_fp16(np.sort(g.uniform(0, 0.1, (n, k // 32, 8)), axis=-1))
+    cb[1::2, :6, :] = 0x7C00
+    return packing.pack(idx), dict(codebook=dev_f16(cb)), signmag8.dequant_values(cb, idx)
+
+
+@pytest.mark.parametrize("codec", [1, 2, 3])
+@pytest.mark.parametrize("k,m", [(320, 1), (576, 1), (2112, 1), (320, 4), (2112, 7)])
+def test_gemv_ragged_k_next_row_overflow(w4, codec, k, m):
+    """k not a multiple of 256: the last step of every row has lanes past k,
+    which would read the next row's bytes.  Here every other row rebuilds to
+    +-inf in its first groups; the finite rows must still match the oracle
+    (their padded lanes contribute exact zeros, not inf * 0 = NaN).  Single
+    calls (m = 4 and 7 also split k across blocks) and the batched launch."""
+    n = 96
+    report("gemv_ragged_overflow", codec=codec, k=k, m=m)
+    p, side, w_hat = _overflowing_case(codec, n, k, 3300 + k + m + codec)
+    x = synthetic.normal_bf16((m, k), 1.0, 3400 + k + m)
+    finite = np.all(np.isfinite(w_hat), axis=1)
+    assert finite.sum() == n // 2
+    y = w4.w4_gemv(dev_u8(p), dev_bf16(x), codec, **side)
+    yb = torch.full((m, n), float("nan"), device="cuda")
+    batch = w4.w4_gemv_batched_plan([dict(packed=dev_u8(p), x=dev_bf16(x), y=yb, **side)], codec)
+    batch()
+    torch.cuda.synchronize()
+    for out in (y, yb):
+        got = host_f32(out)[:, finite]
+        y_ref, bound = matmul.gemm_ref(x, w_hat[finite])
+        assert matmul.within_tolerance(got, y_ref, bound).all()
+
+
+@pytest.mark.parametrize("m", [1, 2, 16, 200])
+def test_matmul_k_zero_writes_zeros(w4, m):
+    """k = 0: y is the empty sum, +0 everywhere (GEMV for m <= 16, GEMM for
+    every m, fp32 and bf16)."""
+    n = 70
+    report("matmul_k0", m=m)
+    p = torch.empty((n, 0), dtype=torch.uint8, device="cuda")
+    s = torch.empty((n, 0), dtype=torch.bfloat16, device="cuda")
+    x = torch.empty((m, 0), dtype=torch.bfloat16, device="cuda")
+    fns = [w4.w4_gemm] + ([w4.w4_gemv] if m <= 16 else [])
+    for fn in fns:
+        for dt in (torch.float32, torch.bfloat16):
+            y = fn(p, x, w4.W4_DYADIC, scales=s, y_dtype=dt)
+            torch.cuda.synchronize()
+            assert y.shape == (m, n)
+            raw = y.view(torch.int16 if dt == torch.bfloat16 else torch.int32).cpu().numpy()
+            assert np.all(raw == 0)   # +0 bit patterns
+
+
+def test_signmag8_k_multiple_of_32_only(w4):
+    """SIGNMAG8 quantize and dequant take k a multiple of the group of 32
+    (here k = 96, an odd number of groups per row); the matrix calls still
+    need k % 64 == 0."""
+    n, k = 37, 96
+    report("signmag8_k32", n=n, k=k)
+    w = synthetic.student_t_bf16((n, k), 5, 0.02, 3500)
+    cb = native.signmag8_fit(w)
+    p, _ = w4.w4_quantize_pack(dev_bf16(w), w4.W4_SIGNMAG8, codebook=dev_f16(cb))
+    d = w4.w4_unpack_dequant(p, w4.W4_SIGNMAG8, codebook=dev_f16(cb))
+    torch.cuda.synchronize()
+    nib = native.signmag8_indices(w, cb)
+    assert np.array_equal(host_u8(p), packing.pack(nib))
+    assert np.array_equal(host_bits(d), signmag8.dequant_from_indices(nib, cb))
+    with pytest.raises(w4.W4Error):
+        w4.w4_gemv(p, dev_bf16(synthetic.normal_bf16((1, k), 1.0, 3501)), w4.W4_SIGNMAG8,
+                   codebook=dev_f16(cb))

@@ -38,7 +38,7 @@ class W4Problem(ctypes.Structure):
 class W4BatchInfo(ctypes.Structure):
     """Mirror of ``w4_gemv_batch_info``."""
     _fields_ = [("total_tiles", _I64), ("k_min", _I64), ("k_max", _I64), ("count", _I32),
-                ("m", _I32), ("tile_rows", _I32), ("reserved", _I32)]
+                ("m", _I32), ("tile_rows", _I32), ("flags", _I32)]
 
 
 _SIGS = {

@@ -1,6 +1,8 @@
 // C ABI of libw4 (declared in include/w4.h): argument validation on the host,
-// then one kernel launch on the caller's stream.  Nothing is allocated,
-// nothing is synchronised, and an error return leaves every buffer untouched.
+// then the kernel launches on the caller's stream.  Nothing is synchronised,
+// and an error return leaves every buffer untouched.  The only allocation is
+// the device workspace that w4_gemm and the m >= 2 GEMV keep per (device,
+// stream) (w4_workspace.cpp).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -19,12 +21,14 @@ bool valid_codec(int32_t c) {
          c == W4_DYADIC5;
 }
 
-// Checks the quantized-weight triple of a codec for an [n][k] weight.
+// Checks the quantized-weight triple of a codec for an [n][k] weight.  k must
+// be a multiple of 64, or for SIGNMAG8 outside the matrix calls (whose kernels
+// step over k in 64-weight units) of its group of 32.
 w4_status check_weight(int32_t codec, int64_t n, int64_t k, const void* packed, const void* scales,
-                       const void* codebook) {
+                       const void* codebook, bool matmul = false) {
   if (!valid_codec(codec)) return W4_EINVAL;
   if (n < 0 || k < 0) return W4_EINVAL;
-  if (k % 64) return W4_ESHAPE;
+  if (k % ((codec == W4_SIGNMAG8 && !matmul) ? 32 : 64)) return W4_ESHAPE;
   if (n == 0 || k == 0) return W4_OK;
   if (!packed) return W4_EINVAL;
   if (!aligned(packed, 16)) return W4_EALIGN;
@@ -42,7 +46,7 @@ w4_status check_weight(int32_t codec, int64_t n, int64_t k, const void* packed, 
 w4_status check_matmul(int32_t codec, int64_t n, int64_t k, const uint8_t* packed,
                        const uint16_t* scales, const uint16_t* codebook, const uint16_t* x,
                        int32_t m, void* y, int32_t y_dtype, int32_t m_max) {
-  w4_status st = check_weight(codec, n, k, packed, scales, codebook);
+  w4_status st = check_weight(codec, n, k, packed, scales, codebook, true);
   if (st != W4_OK) return st;
   if (m < 0) return W4_EINVAL;
   if (m > m_max) return W4_ESHAPE;
@@ -189,6 +193,9 @@ w4_status w4_gemv(int32_t codec, int64_t n, int64_t k, const uint8_t* packed,
   w4_status st = check_matmul(codec, n, k, packed, scales, codebook, x, m, y, y_dtype, kGemvMaxM);
   if (st != W4_OK) return st;
   if (m == 0 || n == 0) return W4_OK;
+  if (k == 0)  // the empty sum
+    return launched(w4::launch_zero(y, (int64_t)m * n, y_dtype == W4_BF16,
+                                    static_cast<hipStream_t>(stream)));
   return launched(w4::launch_gemv(codec, problem(n, k, packed, scales, codebook, x, y), m,
                                   y_dtype == W4_BF16, static_cast<hipStream_t>(stream)));
 }
@@ -199,6 +206,9 @@ w4_status w4_gemm(int32_t codec, int64_t n, int64_t k, const uint8_t* packed,
   w4_status st = check_matmul(codec, n, k, packed, scales, codebook, x, m, y, y_dtype, kGemmMaxM);
   if (st != W4_OK) return st;
   if (m == 0 || n == 0) return W4_OK;
+  if (k == 0)  // the empty sum
+    return launched(w4::launch_zero(y, (int64_t)m * n, y_dtype == W4_BF16,
+                                    static_cast<hipStream_t>(stream)));
   return launched(w4::launch_gemm(codec, problem(n, k, packed, scales, codebook, x, y), m,
                                   y_dtype == W4_BF16, static_cast<hipStream_t>(stream)));
 }
@@ -257,7 +267,9 @@ w4_status w4_gemv_batched_plan(int32_t codec, int32_t m, int32_t y_dtype,
   info->count = count;
   info->m = m;
   info->tile_rows = (int32_t)rows;
-  info->reserved = 0;
+  bool ragged = false;
+  for (int32_t i = 0; i < count; ++i) ragged = ragged || (problems[i].k % 256 != 0);
+  info->flags = ragged ? 1 : 0;
   return W4_OK;
 }
 
@@ -265,7 +277,8 @@ w4_status w4_gemv_batched(int32_t codec, int32_t m, int32_t y_dtype,
                           w4_gemv_problem* problems_device, const w4_gemv_batch_info* info,
                           void* stream) {
   if (!info || !valid_codec(codec)) return W4_EINVAL;
-  if (info->count < 0 || info->total_tiles < 0 || info->k_max < 0 || info->k_min < 0)
+  if (info->count < 0 || info->total_tiles < 0 || info->k_max < 0 || info->k_min < 0 ||
+      (info->flags & ~1) != 0)
     return W4_EINVAL;
   if (info->m != m) return W4_EINVAL;  // the work numbering depends on m
   if (m < 1) return m < 0 ? W4_EINVAL : W4_ESHAPE;
@@ -280,7 +293,7 @@ w4_status w4_gemv_batched(int32_t codec, int32_t m, int32_t y_dtype,
   return launched(w4::launch_gemv_batched(
       codec, reinterpret_cast<const w4::GemvProblem*>(problems_device), info->count,
       info->total_tiles, info->k_max, info->tile_rows, m, y_dtype == W4_BF16,
-      static_cast<hipStream_t>(stream)));
+      (info->flags & 1) != 0, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

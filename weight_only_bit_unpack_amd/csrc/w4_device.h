@@ -85,11 +85,20 @@ __device__ __forceinline__ uint32_t fma_pair(uint32_t h2, float s, float c) {
   return cvt_pk_bf16(__builtin_fmaf((float)h.x, s, c), __builtin_fmaf((float)h.y, s, c));
 }
 
-__device__ __forceinline__ uint32_t wide_pair(uint32_t h2, float off, float s) {
+// +0.0f that the optimiser cannot fold: fma(d, s, +0) is d * s for every
+// nonzero product and +0 for an exact zero of either sign ((-0) + (+0) = +0).
+__device__ __forceinline__ float hidden_pos_zero() {
+  uint32_t z = 0u;
+  asm volatile("" : "+v"(z));
+  return __builtin_bit_cast(float, z);
+}
+
+__device__ __forceinline__ uint32_t wide_pair(uint32_t h2, float off, float s, float pz) {
   f16x2 h = __builtin_bit_cast(f16x2, h2);
   f16x2 o = {(_Float16)off, (_Float16)off};
-  f16x2 d = h - o;  // exact: small integers (times 16)
-  return cvt_pk_bf16((float)d.x * s, (float)d.y * s);
+  f16x2 d = h - o;  // exact: small integers (times 16); code 8 gives +0
+  // the +0 addend keeps code 8 at +0 for a negative scale as well
+  return cvt_pk_bf16(__builtin_fmaf((float)d.x, s, pz), __builtin_fmaf((float)d.y, s, pz));
 }
 
 // Branch-free form valid for every scale: d = h - off in fp16 (exact small
@@ -139,11 +148,12 @@ __device__ __forceinline__ u32x4 dyadic_rebuild(uint32_t p, const DyadicScale& d
 __device__ __forceinline__ u32x4 dyadic_rebuild_wide(uint32_t p, const DyadicScale& d, uint32_t m0,
                                                      uint32_t m1, uint32_t mg) {
   const uint32_t q = p >> 8;
+  const float pz = hidden_pos_zero();
   u32x4 r;
-  r.x = wide_pair(and_or(p, m0, mg), 1032.0f, d.s8);
-  r.y = wide_pair(and_or(p, m1, mg), 1152.0f, d.s8_16);
-  r.z = wide_pair(and_or(q, m0, mg), 1032.0f, d.s8);
-  r.w = wide_pair(and_or(q, m1, mg), 1152.0f, d.s8_16);
+  r.x = wide_pair(and_or(p, m0, mg), 1032.0f, d.s8, pz);
+  r.y = wide_pair(and_or(p, m1, mg), 1152.0f, d.s8_16, pz);
+  r.z = wide_pair(and_or(q, m0, mg), 1032.0f, d.s8, pz);
+  r.w = wide_pair(and_or(q, m1, mg), 1152.0f, d.s8_16, pz);
   return r;
 }
 

@@ -44,6 +44,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_
                                            0x00020000);
 }
 constexpr uint32_t kOOB = 0x80000000u;  // an offset past every slice
+// Per-lane base offset of a load that must read zeros: kOOBLane plus any step
+// offset (below 2^31, or kOOB itself) stays past every slice (slices hold
+// fewer than 2^28 bytes) and below 2^32.
+constexpr uint32_t kOOBLane = 0x40000000u;
 // Cache policy of the packed-weight loads: nontemporal.  Every packed byte is
 // read once per launch; streaming it leaves the caches to the scales and
 // tables, which neighbouring lanes and steps read again (measured on the 1B
@@ -65,8 +69,11 @@ struct Slice {
 
 // Per-lane byte offsets of the lane's first step in the current k-chunk.
 // Rows past the slice give offsets past num_records (reads return zero).
-// In a row's last, partial step the lanes past k read the next row's bytes:
-// finite weights that meet zero activations in LDS, so they add nothing.
+// When the block's k range does not end on a 256-k step (RAGGED kernels), the
+// lanes of its last step whose weights lie past the range get base kOOBLane
+// and read zeros: weights rebuilt from zero bytes and zero side data are
+// finite, and meet zero activations in LDS.  (Read as they lie in memory,
+// they would be the next row's weights, which may rebuild to +-inf.)
 struct LaneBase {
   uint32_t pa, pb, s, s2;
 };
@@ -284,7 +291,7 @@ struct Slicing {
 // XG: x units per thread kept in flight together while staging (after the
 // first).  The batched m = 1 decode pass stages at most a few units per thread
 // and runs fastest with the fewest registers, XG = 1; elsewhere XG = 4.
-template <int CODEC, int KSPLIT, bool BATCHED, int XG>
+template <int CODEC, int KSPLIT, bool BATCHED, int XG, bool RAGGED>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvProblem single, const GemvProblem* probs,
                                                    int count, int m, int y_bf16, int xs_units,
                                                    Slicing sl) {
@@ -386,10 +393,32 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvProblem single, const Gem
       L.s2 = CODEC == 4 ? rloc * (uint32_t)(K >> 3) + (uint32_t)(k0 >> 3) + 8u * (uint32_t)q
                         : g0 * 2;
     }
+    // RAGGED: how far into the chunk each of the lane's loads starts; a load
+    // of step st reads zeros unless 256 st + start < kend - k0
+    uint32_t limA = 0, limB = 0, limS = 0;
+    if constexpr (RAGGED) {
+      const int64_t span = kend - k0;
+      auto lim = [&](int64_t start) -> uint32_t {
+        return span > start ? (uint32_t)(span - start) : 0u;
+      };
+      limA = lim(2 * (int64_t)chA);  // a 16-byte chunk holds 32 weights
+      limB = lim(2 * (int64_t)chB);
+      limS = lim(64 * (int64_t)q);    // the lane's 64-group of the step
+    }
     auto fetch = [&](Raw<CODEC>& r, int i) {
       const bool in = i < nw;
       const uint32_t st = (uint32_t)step_of(i);
-      r.fetch(S, L, in ? st * 128u : kOOB, in ? st * Raw<CODEC>::kSideStep : kOOB);
+      if constexpr (RAGGED) {
+        const uint32_t kst = 256u * st;
+        LaneBase M;
+        M.pa = opaque(kst < limA ? L.pa : kOOBLane);
+        M.pb = opaque(kst < limB ? L.pb : kOOBLane);
+        M.s = opaque(kst < limS ? L.s : kOOBLane);
+        M.s2 = opaque(kst < limS ? L.s2 : kOOBLane);
+        r.fetch(S, M, in ? st * 128u : kOOB, in ? st * Raw<CODEC>::kSideStep : kOOB);
+      } else {
+        r.fetch(S, L, in ? st * 128u : kOOB, in ? st * Raw<CODEC>::kSideStep : kOOB);
+      }
     };
     // x staging slots: (row mrow, pass ip) -> unit tid + 256 ip of that row
     const int ipr = (units + 255) >> 8;
@@ -519,6 +548,17 @@ __global__ __launch_bounds__(256) void gemv_reduce(const float* part, int kslice
     reinterpret_cast<float*>(y)[e] = v;
 }
 
+// y = +0 over `count` outputs (the product of an empty k range).
+__global__ __launch_bounds__(256) void zero_kernel(void* y, int64_t count, int y_bf16) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < count; e += stride) {
+    if (y_bf16)
+      reinterpret_cast<uint16_t*>(y)[e] = 0;
+    else
+      reinterpret_cast<float*>(y)[e] = 0.0f;
+  }
+}
+
 // LDS units for a launch whose blocks each cover `kspan` of k: the whole
 // padded span if it fits, else the cap; never less than the 4 KiB the in-block
 // k-split reduction needs.
@@ -557,11 +597,12 @@ GemvShape gemv_shape(int64_t n, int64_t k, int m) {
   if (ks < fit) ks = fit;
   if (ks > kMaxSlices) ks = kMaxSlices;
   if (ks > steps) ks = steps;
+  if (ks < 1) ks = 1;  // k == 0 never gets here (the call writes zeros instead)
   const int64_t per = (steps + ks - 1) / ks;
   return {1, (int)((steps + per - 1) / per), (int)per};
 }
 
-template <int CODEC, int KSPLIT>
+template <int CODEC, int KSPLIT, bool RAGGED>
 hipError_t launch_one(const GemvProblem& p, int m, int y_bf16, const GemvShape& sh,
                       hipStream_t stream) {
   const int rows = 16 * (4 / KSPLIT);
@@ -575,7 +616,7 @@ hipError_t launch_one(const GemvProblem& p, int m, int y_bf16, const GemvShape& 
     sl.part = reinterpret_cast<float*>(ws);
   }
   const int xu = xs_units_for(m, (int64_t)sh.slice_steps * 256);
-  gemv_kernel<CODEC, KSPLIT, false, 4>
+  gemv_kernel<CODEC, KSPLIT, false, 4, RAGGED>
       <<<dim3((uint32_t)blocks, (uint32_t)sh.kslices), dim3(256), (xu + 512) * 16, stream>>>(
           p, nullptr, 0, m, y_bf16, xu, sl);
   hipError_t e = hipGetLastError();
@@ -586,17 +627,34 @@ hipError_t launch_one(const GemvProblem& p, int m, int y_bf16, const GemvShape& 
   return hipGetLastError();
 }
 
-template <int CODEC>
-hipError_t launch_codec(const GemvProblem& p, int m, int y_bf16, hipStream_t stream) {
-  const GemvShape sh = gemv_shape(p.n, p.k, m);
+template <int CODEC, bool RAGGED>
+hipError_t launch_shape(const GemvProblem& p, int m, int y_bf16, const GemvShape& sh,
+                        hipStream_t stream) {
   switch (sh.ksplit) {
-    case 1: return launch_one<CODEC, 1>(p, m, y_bf16, sh, stream);
-    case 2: return launch_one<CODEC, 2>(p, m, y_bf16, sh, stream);
-    default: return launch_one<CODEC, 4>(p, m, y_bf16, sh, stream);
+    case 1: return launch_one<CODEC, 1, RAGGED>(p, m, y_bf16, sh, stream);
+    case 2: return launch_one<CODEC, 2, RAGGED>(p, m, y_bf16, sh, stream);
+    default: return launch_one<CODEC, 4, RAGGED>(p, m, y_bf16, sh, stream);
   }
 }
 
+// k slices and k chunks are whole 256-k steps, so only a k that is not a
+// multiple of 256 leaves a partial last step.
+template <int CODEC>
+hipError_t launch_codec(const GemvProblem& p, int m, int y_bf16, hipStream_t stream) {
+  const GemvShape sh = gemv_shape(p.n, p.k, m);
+  if (p.k % 256) return launch_shape<CODEC, true>(p, m, y_bf16, sh, stream);
+  return launch_shape<CODEC, false>(p, m, y_bf16, sh, stream);
+}
+
 }  // namespace
+
+hipError_t launch_zero(void* y, int64_t count, int y_bf16, hipStream_t stream) {
+  int64_t blocks = (count + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) return hipSuccess;
+  zero_kernel<<<dim3((uint32_t)blocks), dim3(256), 0, stream>>>(y, count, y_bf16);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemv(int codec, const GemvProblem& p, int m, int y_bf16, hipStream_t stream) {
   if (codec == 0) return launch_codec<0>(p, m, y_bf16, stream);
@@ -606,7 +664,7 @@ hipError_t launch_gemv(int codec, const GemvProblem& p, int m, int y_bf16, hipSt
   return launch_codec<2>(p, m, y_bf16, stream);
 }
 
-template <int CODEC>
+template <int CODEC, bool RAGGED>
 hipError_t launch_batched_codec(const GemvProblem* probs_dev, int count, int64_t total_tiles,
                                 int xu, int tile_rows, int m, int y_bf16, hipStream_t stream) {
   const dim3 block(256), grid((uint32_t)total_tiles);
@@ -616,38 +674,41 @@ hipError_t launch_batched_codec(const GemvProblem* probs_dev, int count, int64_t
   // m == 1: tiles of 64 / 32 / 16 rows = 4 / 2 / 1 row tiles of 16 per block,
   // the block's 4 waves splitting k 1 / 2 / 4 ways
   if (m == 1 && tile_rows == 16)
-    gemv_kernel<CODEC, 4, true, 1>
+    gemv_kernel<CODEC, 4, true, 1, RAGGED>
         <<<grid, block, lds, stream>>>(none, probs_dev, count, m, y_bf16, xu, whole);
   else if (m == 1 && tile_rows == 32)
-    gemv_kernel<CODEC, 2, true, 1>
+    gemv_kernel<CODEC, 2, true, 1, RAGGED>
         <<<grid, block, lds, stream>>>(none, probs_dev, count, m, y_bf16, xu, whole);
   else if (m == 1)
-    gemv_kernel<CODEC, 1, true, 1>
+    gemv_kernel<CODEC, 1, true, 1, RAGGED>
         <<<grid, block, lds, stream>>>(none, probs_dev, count, m, y_bf16, xu, whole);
   else
-    gemv_kernel<CODEC, 1, true, 4>
+    gemv_kernel<CODEC, 1, true, 4, RAGGED>
         <<<grid, block, lds, stream>>>(none, probs_dev, count, m, y_bf16, xu, whole);
   return hipGetLastError();
 }
 
+template <int CODEC>
+hipError_t launch_batched_any(const GemvProblem* probs_dev, int count, int64_t total_tiles, int xu,
+                              int tile_rows, int m, int y_bf16, bool ragged, hipStream_t stream) {
+  if (ragged)
+    return launch_batched_codec<CODEC, true>(probs_dev, count, total_tiles, xu, tile_rows, m,
+                                             y_bf16, stream);
+  return launch_batched_codec<CODEC, false>(probs_dev, count, total_tiles, xu, tile_rows, m,
+                                            y_bf16, stream);
+}
+
 hipError_t launch_gemv_batched(int codec, const GemvProblem* probs_dev, int count,
                                int64_t total_tiles, int64_t k_max, int tile_rows, int m,
-                               int y_bf16, hipStream_t stream) {
+                               int y_bf16, bool ragged, hipStream_t stream) {
   const int xu = xs_units_for(m, k_max);
-  if (codec == 0)
-    return launch_batched_codec<0>(probs_dev, count, total_tiles, xu, tile_rows, m, y_bf16,
-                                     stream);
-  if (codec == 1)
-    return launch_batched_codec<1>(probs_dev, count, total_tiles, xu, tile_rows, m, y_bf16,
-                                     stream);
-  if (codec == 3)
-    return launch_batched_codec<3>(probs_dev, count, total_tiles, xu, tile_rows, m, y_bf16,
-                                     stream);
-  if (codec == 4)
-    return launch_batched_codec<4>(probs_dev, count, total_tiles, xu, tile_rows, m, y_bf16,
-                                     stream);
-  return launch_batched_codec<2>(probs_dev, count, total_tiles, xu, tile_rows, m, y_bf16,
-                                  stream);
+  switch (codec) {
+    case 0: return launch_batched_any<0>(probs_dev, count, total_tiles, xu, tile_rows, m, y_bf16, ragged, stream);
+    case 1: return launch_batched_any<1>(probs_dev, count, total_tiles, xu, tile_rows, m, y_bf16, ragged, stream);
+    case 3: return launch_batched_any<3>(probs_dev, count, total_tiles, xu, tile_rows, m, y_bf16, ragged, stream);
+    case 4: return launch_batched_any<4>(probs_dev, count, total_tiles, xu, tile_rows, m, y_bf16, ragged, stream);
+    default: return launch_batched_any<2>(probs_dev, count, total_tiles, xu, tile_rows, m, y_bf16, ragged, stream);
+  }
 }
 
 }  // namespace w4

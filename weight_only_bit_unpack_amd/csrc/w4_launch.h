@@ -40,17 +40,23 @@ hipError_t launch_signmag8_warm_fit(int64_t n, int64_t k, const uint16_t* w, uin
 
 hipError_t launch_gemv(int codec, const GemvProblem& p, int m, int y_bf16, hipStream_t stream);
 
+// y[0 .. count) = +0 (fp32, or bf16 when y_bf16): the product over k == 0.
+hipError_t launch_zero(void* y, int64_t count, int y_bf16, hipStream_t stream);
+
 // The batched GEMV's plan takes 64-row tiles, or for m == 1 halves them (down
 // to 16) while the launch would have fewer than this many tiles.
 constexpr int64_t kGemvBatchedMinTiles = 1024;
 // probs_dev: count problems with tile_begin set by the plan for tiles of
 // tile_rows (64; 32 or 16 only with m == 1) rows
+// ragged: some problem's k is not a multiple of 256 (its last step is partial)
 hipError_t launch_gemv_batched(int codec, const GemvProblem* probs_dev, int count,
                                int64_t total_tiles, int64_t k_max, int tile_rows, int m,
-                               int y_bf16, hipStream_t stream);
+                               int y_bf16, bool ragged, hipStream_t stream);
 
 // Library-owned device buffer of at least `bytes` for (current device, stream,
-// user); its contents are undefined.  Growing waits for the stream.
+// user); its contents are undefined.  Growing allocates a new buffer and keeps
+// the old one (work already enqueued, or a graph captured earlier, may still
+// use it), so it never waits for the stream.
 enum { kWorkspaceGemm = 0, kWorkspaceGemv = 1 };
 hipError_t stream_workspace(int user, hipStream_t stream, size_t bytes, char** out);
 

@@ -107,8 +107,89 @@ __global__ __launch_bounds__(256) void quantize_dyadic_kernel(const u32x4* __res
   }
 }
 
-// LUT16 / LUT16S: levels v_j = s * L_j (exact in fp32); index = lowest j
-// minimising |fl32(w - v_j)|.  shared: one table for every group (LUT16S).
+// Nearest level, exactly: the lowest j minimising the exact |x - v_j|, for a
+// value x and levels v_j that double holds exactly (bf16 weights, products of
+// two bf16 numbers, fp16 magnitudes, +inf).  The distance rounded to double,
+// fl(|x - v_j|), is monotone in the exact distance, so the first level at the
+// smallest rounded distance is the answer unless another level shares that
+// rounded distance (a true tie, or two distances that round alike because a
+// level is far smaller or larger than x).  nearest_scan reports such a tie;
+// nearest_settle then compares the tied levels' exact distances
+// |h| + sgn(h) e, where h = fl(x - v_j) and e = (x - v_j) - h is the exact
+// error of the subtraction (two-sum), and |h| is the same for all of them.
+template <int NL>
+__device__ __forceinline__ uint32_t nearest_scan(double x, const double (&v)[NL], double& dmin,
+                                                 bool& tie) {
+  double best = __builtin_fabs(x - v[0]);
+  uint32_t bi = 0;
+  bool t = false;
+#pragma unroll
+  for (int j = 1; j < NL; ++j) {
+    const double d = __builtin_fabs(x - v[j]);
+    t = d < best ? false : (t || d == best);
+    if (d < best) {
+      best = d;
+      bi = (uint32_t)j;
+    }
+  }
+  dmin = best;
+  // every level +inf away: all tie exactly, and the lowest index is the answer
+  tie = t && best != __builtin_inf();
+  return bi;
+}
+
+template <int NL>
+__device__ __forceinline__ uint32_t nearest_settle(double x, const double (&v)[NL], double dmin) {
+  uint32_t bi = 0;
+  double bk = __builtin_inf();
+#pragma unroll
+  for (int j = NL - 1; j >= 0; --j) {  // downwards: the lowest index wins equal keys
+    const double h = x - v[j];
+    const double bp = h - x;               // two-sum of x and -v_j
+    const double ap = h - bp;
+    const double e = (x - ap) + (-v[j] - bp);
+    const double key = h < 0.0 ? -e : e;
+    if (__builtin_fabs(h) == dmin && key <= bk) {
+      bk = key;
+      bi = (uint32_t)j;
+    }
+  }
+  return bi;
+}
+
+// Eight weights against NL levels: the packed word of their indices (plus
+// the sign bits for SIGNMAG8, where x = |w|).  The wave settles ties only if
+// one of its lanes has one.
+template <int NL, bool SIGNMAG>
+__device__ __forceinline__ uint32_t nearest8(const float (&f)[8], const double (&v)[NL]) {
+  uint32_t idx[8];
+  double dmin[8];
+  bool any_tie = false;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const double x = SIGNMAG ? (double)__builtin_fabsf(f[i]) : (double)f[i];
+    bool t;
+    idx[i] = nearest_scan<NL>(x, v, dmin[i], t);
+    any_tie = any_tie || t;
+  }
+  if (__builtin_expect(__any(any_tie), 0)) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const double x = SIGNMAG ? (double)__builtin_fabsf(f[i]) : (double)f[i];
+      if (dmin[i] != __builtin_inf()) idx[i] = nearest_settle<NL>(x, v, dmin[i]);
+    }
+  }
+  uint32_t word = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t sign = (SIGNMAG && f[i] < 0.0f) ? 8u : 0u;
+    word |= (sign | idx[i]) << (4 * i);
+  }
+  return word;
+}
+
+// LUT16 / LUT16S: levels v_j = s * L_j (exact in double); index = the exact
+// nearest level.  shared: one table for every group (LUT16S).
 __global__ __launch_bounds__(256) void quantize_lut16_kernel(const u32x4* __restrict__ w,
                                                              uint32_t* __restrict__ packed,
                                                              const uint16_t* __restrict__ scales,
@@ -118,36 +199,21 @@ __global__ __launch_bounds__(256) void quantize_lut16_kernel(const u32x4* __rest
   if (c >= nchunks) return;
   const int64_t g = c >> 3, gt = shared ? 0 : g;
   const u32x4 v = __builtin_nontemporal_load(&w[c]);
-  const float s = bf16_bits_to_f32(scales[g]);
+  const double s = (double)bf16_bits_to_f32(scales[g]);
   const u32x4 l0 = lut[2 * gt], l1 = lut[2 * gt + 1];
   const uint32_t lw[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-  float lv[16];
+  double lv[16];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    lv[2 * i] = bf16_bits_to_f32(lw[i] & 0xFFFFu) * s;
-    lv[2 * i + 1] = __builtin_bit_cast(float, lw[i] & 0xFFFF0000u) * s;
+    lv[2 * i] = (double)bf16_bits_to_f32(lw[i] & 0xFFFFu) * s;
+    lv[2 * i + 1] = (double)__builtin_bit_cast(float, lw[i] & 0xFFFF0000u) * s;
   }
   float f[8];
   unpack8(v, f);
-  uint32_t word = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    float best = __builtin_fabsf(f[i] - lv[0]);
-    uint32_t bi = 0;
-#pragma unroll
-    for (int j = 1; j < 16; ++j) {
-      const float d = __builtin_fabsf(f[i] - lv[j]);
-      if (d < best) {
-        best = d;
-        bi = (uint32_t)j;
-      }
-    }
-    word |= bi << (4 * i);
-  }
-  packed[c] = word;
+  packed[c] = nearest8<16, false>(f, lv);
 }
 
-// SIGNMAG8: nibble = (w < 0) << 3 | lowest j minimising |fl32(|w| - M_j)|.
+// SIGNMAG8: nibble = (w < 0) << 3 | the exact nearest magnitude to |w|.
 __global__ __launch_bounds__(256) void quantize_signmag8_kernel(const u32x4* __restrict__ w,
                                                                 uint32_t* __restrict__ packed,
                                                                 const u32x4* __restrict__ cb,
@@ -157,32 +223,16 @@ __global__ __launch_bounds__(256) void quantize_signmag8_kernel(const u32x4* __r
   const u32x4 v = __builtin_nontemporal_load(&w[c]);
   const u32x4 m = cb[c >> 2];  // group of 32 = 4 chunks
   const uint32_t mw[4] = {m.x, m.y, m.z, m.w};
-  float mv[8];
+  double mv[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     f16x2 h = __builtin_bit_cast(f16x2, mw[i]);
-    mv[2 * i] = (float)h.x;
-    mv[2 * i + 1] = (float)h.y;
+    mv[2 * i] = (double)(float)h.x;
+    mv[2 * i + 1] = (double)(float)h.y;
   }
   float f[8];
   unpack8(v, f);
-  uint32_t word = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float a = __builtin_fabsf(f[i]);
-    float best = __builtin_fabsf(a - mv[0]);
-    uint32_t bi = 0;
-#pragma unroll
-    for (int j = 1; j < 8; ++j) {
-      const float d = __builtin_fabsf(a - mv[j]);
-      if (d < best) {
-        best = d;
-        bi = (uint32_t)j;
-      }
-    }
-    word |= ((f[i] < 0.0f ? 8u : 0u) | bi) << (4 * i);
-  }
-  packed[c] = word;
+  packed[c] = nearest8<8, true>(f, mv);
 }
 
 // Bit of a run's 32-bit high-bit word that holds weight i (0..31) of the run

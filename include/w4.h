@@ -304,6 +304,26 @@ w4_status w4_gemm(int32_t codec, int64_t n, int64_t k, const uint8_t* packed,
                   int32_t m, void* y, int32_t y_dtype, void* stream);
 
 /*
+ * w4_gemm_noalloc -- w4_gemm for callers that cannot allocate device memory
+ * (code under HIP graph capture without a warm-up call, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, results (bit for bit)
+ * and errors as w4_gemm, but the workspace is a fixed device array of
+ * W4_NOALLOC_SCRATCH_BYTES that the library defines and every GPU it runs on
+ * holds until the process ends; the call itself calls no allocating routine.
+ * Every call on a GPU shares that GPU's array: calls that overlap on one GPU
+ * (on different streams, or replays of graphs that contain this call) race
+ * and must be ordered by the caller.  Nothing in the array needs to start at
+ * zero: each call writes the parts it reads.
+ * Additional error: W4_ESHAPE when the call's workspace (the w4_gemm sizes)
+ * exceeds W4_NOALLOC_SCRATCH_BYTES, e.g. m = 256 with k = n = 8192 needs
+ * 36 MiB.
+ */
+#define W4_NOALLOC_SCRATCH_BYTES (64u << 20)
+w4_status w4_gemm_noalloc(int32_t codec, int64_t n, int64_t k, const uint8_t* packed,
+                          const uint16_t* scales, const uint16_t* codebook, const uint16_t* x,
+                          int32_t m, void* y, int32_t y_dtype, void* stream);
+
+/*
  * w4_linear -- the linear layer with the kernel chosen by batch size, as
  * [KM] sec. 4.1 lays out: m <= 16 -> w4_gemv (the table-lookup kernel),
  * larger m -> w4_gemm (the mixed 4-bit x bf16 MFMA kernel; the page's further

@@ -21,7 +21,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["w4_api.cpp", "w4_quantize.hip", "w4_dequant.hip", "w4_gemv.hip", "w4_gemm.hip",
-           "w4_workspace.cpp", "w4_fit.hip"]
+           "w4_workspace.cpp", "w4_fit.hip", "w4_noalloc.hip"]
 
 CFLAGS = [
     f"--offload-arch={ARCH}",

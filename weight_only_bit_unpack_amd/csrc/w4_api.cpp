@@ -85,6 +85,7 @@ constexpr int32_t kGemmMaxM = 65535 * 128;
 
 static_assert(sizeof(w4_gemv_problem) == sizeof(w4::GemvProblem), "problem layout");
 static_assert(sizeof(w4_gemv_batch_info) == 40, "batch info layout");
+static_assert(W4_NOALLOC_SCRATCH_BYTES == w4::kNoallocScratchBytes, "scratch size");
 
 extern "C" {
 
@@ -210,7 +211,23 @@ w4_status w4_gemm(int32_t codec, int64_t n, int64_t k, const uint8_t* packed,
     return launched(w4::launch_zero(y, (int64_t)m * n, y_dtype == W4_BF16,
                                     static_cast<hipStream_t>(stream)));
   return launched(w4::launch_gemm(codec, problem(n, k, packed, scales, codebook, x, y), m,
-                                  y_dtype == W4_BF16, static_cast<hipStream_t>(stream)));
+                                  y_dtype == W4_BF16, static_cast<hipStream_t>(stream), nullptr));
+}
+
+w4_status w4_gemm_noalloc(int32_t codec, int64_t n, int64_t k, const uint8_t* packed,
+                          const uint16_t* scales, const uint16_t* codebook, const uint16_t* x,
+                          int32_t m, void* y, int32_t y_dtype, void* stream) {
+  w4_status st = check_matmul(codec, n, k, packed, scales, codebook, x, m, y, y_dtype, kGemmMaxM);
+  if (st != W4_OK) return st;
+  if (m == 0 || n == 0) return W4_OK;
+  if (k == 0)
+    return launched(w4::launch_zero(y, (int64_t)m * n, y_dtype == W4_BF16,
+                                    static_cast<hipStream_t>(stream)));
+  if (w4::gemm_workspace_bytes(codec, n, k, m) > w4::kNoallocScratchBytes) return W4_ESHAPE;
+  char* ws = nullptr;
+  if (w4::noalloc_scratch(&ws) != hipSuccess) return W4_EHIP;
+  return launched(w4::launch_gemm(codec, problem(n, k, packed, scales, codebook, x, y), m,
+                                  y_dtype == W4_BF16, static_cast<hipStream_t>(stream), ws));
 }
 
 w4_status w4_linear(int32_t codec, int64_t n, int64_t k, const uint8_t* packed,

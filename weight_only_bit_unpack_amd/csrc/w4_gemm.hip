@@ -603,24 +603,46 @@ bool gemm_narrow(int codec, int64_t k, int m) {
   return (codec == 0 || codec == 1 || codec == 3 || codec == 4) && k % 128 == 0 && m <= kNarrowMaxM;
 }
 
-template <int BMT>
-hipError_t launch_gemm_shape(int codec, const GemvProblem& p, int m, int y_bf16,
-                             hipStream_t stream) {
+int device_cus() {
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     cus = 256;
-  const int S = gemm_splits(p.n, p.k, m, cus, BMT, Tile<BMT>::BK);
-  const uint32_t tiles_n = (uint32_t)((p.n + BN - 1) / BN), tiles_m = (uint32_t)((m + BMT - 1) / BMT);
-  const uint32_t tiles = tiles_n * tiles_m;
-  // workspace: packed activations of tiles_m * BMT rows, then S fp32 partials
-  // of tiles * BMT * BN when the k range is split
-  const size_t xpk_bytes = (size_t)tiles_m * BMT * p.k * 2;
-  const size_t per_split = (size_t)tiles * BMT * BN;  // floats
-  const size_t bytes = xpk_bytes + (S > 1 ? (size_t)S * per_split * sizeof(float) : 0);
-  char* ws = nullptr;
-  hipError_t e = stream_workspace(kWorkspaceGemm, stream, bytes, &ws);
-  if (e != hipSuccess) return e;
+  return cus;
+}
+
+// Workspace of one call: packed activations of tiles_m * BMT rows, then S
+// fp32 partials of tiles * BMT * BN when the k range is split.
+template <int BMT>
+struct GemmPlan {
+  int S;
+  uint32_t tiles_m, tiles_n, tiles;
+  size_t xpk_bytes, per_split, bytes;
+  GemmPlan(int64_t n, int64_t k, int m, int cus) {
+    S = gemm_splits(n, k, m, cus, BMT, Tile<BMT>::BK);
+    tiles_n = (uint32_t)((n + BN - 1) / BN);
+    tiles_m = (uint32_t)((m + BMT - 1) / BMT);
+    tiles = tiles_n * tiles_m;
+    xpk_bytes = (size_t)tiles_m * BMT * k * 2;
+    per_split = (size_t)tiles * BMT * BN;  // floats
+    bytes = xpk_bytes + (S > 1 ? (size_t)S * per_split * sizeof(float) : 0);
+  }
+};
+
+// ws: the caller's workspace of at least GemmPlan::bytes, or nullptr for the
+// stream's library-kept one
+template <int BMT>
+hipError_t launch_gemm_shape(int codec, const GemvProblem& p, int m, int y_bf16,
+                             hipStream_t stream, char* ws) {
+  const GemmPlan<BMT> g(p.n, p.k, m, device_cus());
+  const int S = g.S;
+  const uint32_t tiles_m = g.tiles_m, tiles = g.tiles;
+  const size_t xpk_bytes = g.xpk_bytes, per_split = g.per_split;
+  hipError_t e = hipSuccess;
+  if (!ws) {
+    e = stream_workspace(kWorkspaceGemm, stream, g.bytes, &ws);
+    if (e != hipSuccess) return e;
+  }
   u32x4* xpk = reinterpret_cast<u32x4*>(ws);
   float* partial = S > 1 ? reinterpret_cast<float*>(ws + xpk_bytes) : nullptr;
   pack_activations<<<dim3((uint32_t)(tiles_m * (BMT / 32) * (p.k / 64))), dim3(256), 0, stream>>>(
@@ -650,9 +672,15 @@ hipError_t launch_gemm_shape(int codec, const GemvProblem& p, int m, int y_bf16,
 
 }  // namespace
 
-hipError_t launch_gemm(int codec, const GemvProblem& p, int m, int y_bf16, hipStream_t stream) {
-  if (gemm_narrow(codec, p.k, m)) return launch_gemm_shape<128>(codec, p, m, y_bf16, stream);
-  return launch_gemm_shape<256>(codec, p, m, y_bf16, stream);
+hipError_t launch_gemm(int codec, const GemvProblem& p, int m, int y_bf16, hipStream_t stream,
+                       char* ws) {
+  if (gemm_narrow(codec, p.k, m)) return launch_gemm_shape<128>(codec, p, m, y_bf16, stream, ws);
+  return launch_gemm_shape<256>(codec, p, m, y_bf16, stream, ws);
+}
+
+size_t gemm_workspace_bytes(int codec, int64_t n, int64_t k, int m) {
+  if (gemm_narrow(codec, k, m)) return GemmPlan<128>(n, k, m, device_cus()).bytes;
+  return GemmPlan<256>(n, k, m, device_cus()).bytes;
 }
 
 }  // namespace w4

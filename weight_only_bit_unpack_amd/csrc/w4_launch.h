@@ -60,6 +60,15 @@ hipError_t launch_gemv_batched(int codec, const GemvProblem* probs_dev, int coun
 enum { kWorkspaceGemm = 0, kWorkspaceGemv = 1 };
 hipError_t stream_workspace(int user, hipStream_t stream, size_t bytes, char** out);
 
-hipError_t launch_gemm(int codec, const GemvProblem& p, int m, int y_bf16, hipStream_t stream);
+// ws: a workspace of at least gemm_workspace_bytes(...) bytes, or nullptr for
+// the library-kept one of the stream (stream_workspace)
+hipError_t launch_gemm(int codec, const GemvProblem& p, int m, int y_bf16, hipStream_t stream,
+                       char* ws);
+size_t gemm_workspace_bytes(int codec, int64_t n, int64_t k, int m);
+
+// Device address of the current device's copy of the fixed scratch array
+// (w4_noalloc.hip), looked up once per device; its size in bytes.
+hipError_t noalloc_scratch(char** out);
+constexpr size_t kNoallocScratchBytes = size_t{64} << 20;
 
 }  // namespace w4

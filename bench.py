@@ -9,12 +9,14 @@ matrix.  One step = one pass over the stack (one batched launch), inputs
 resident in HBM.  `value` = algorithmic bytes of the pass (packed nibbles +
 bf16 scales + x + fp32 y) / step time, in GB/s.
 
-Also measured in the same run and reported under "rows" (with a plain 1 GiB
-device copy as context for what HBM delivers on the box): the same pass as
-168 separate w4_gemv calls, quantize_pack and unpack_dequant over the stack,
-and the prefill GEMM (M = 256, K = N = 8192, in TFLOP/s) with quantize_pack of
-its 8192^2 weight.  The CPU baseline times the oracle (numpy, one thread) on
-the first eight decoder blocks of the stack.
+Also measured in the same run and reported under "rows": the same pass as
+168 separate w4_gemv calls, quantize_pack and unpack_dequant, the prefill GEMM
+(M = 256, K = N = 8192, in TFLOP/s) with quantize_pack of its 8192^2 weight,
+and the other workloads' rows.  "context" holds what HBM delivers on the box
+in the same run: a plain streaming read of 4 GiB with 16-byte loads (the read
+ceiling the GEMV is set against) and a 1 GiB device copy.  The CPU baseline
+times the C oracle (OpenMP on the host's cores) on the whole decode stack,
+with further rows for the other workloads, each with its GPU:CPU ratio.
 
     python bench.py [--gpus 1] [--steps 1000] [--warmup 200]
 """
@@ -91,6 +93,32 @@ def timed(fn, stream, steps, warmup):
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps  # ms per step
+
+
+def read_ceiling(torch, dev, stream):
+    """GB/s of a plain streaming read of 4 GiB with 16-byte nontemporal loads
+    (libw4ctx.so), best of a few grid sizes: the read rate HBM delivers to a
+    read-only kernel on this machine."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "weight_only_bit_unpack_amd", "libw4ctx.so"))
+    lib.w4ctx_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                      ctypes.c_int32, ctypes.c_void_p]
+    lib.w4ctx_read_stream.restype = ctypes.c_int
+    nbytes = 4 << 30
+    buf = torch.full((nbytes // 4,), 0x01010101, dtype=torch.int32, device=dev)
+    sink = torch.zeros(1024, dtype=torch.int32, device=dev)
+    best = 0.0
+    for blocks in (8192, 16384, 32768):
+        def run():
+            rc = lib.w4ctx_read_stream(ctypes.c_void_p(buf.data_ptr()), nbytes,
+                                       ctypes.c_void_p(sink.data_ptr()), blocks,
+                                       ctypes.c_void_p(stream.cuda_stream))
+            assert rc == 0, rc
+        ms = timed(run, stream, 20, 3)
+        best = max(best, nbytes / (ms * 1e-3) / 1e9)
+    del buf, sink
+    torch.cuda.empty_cache()
+    return best
 
 
 def time_gemm(w4, synthetic, torch, dev, stream, args):
@@ -350,6 +378,10 @@ def main():
     ms = timed(lambda: batch(stream), stream, args.steps, args.warmup)
     gbs = gemv_bytes / (ms * 1e-3) / 1e9
     rows = {}
+    log("HBM read ceiling (4 GiB streaming read)")
+    ceiling = read_ceiling(torch, dev, stream)
+    context = {"read_ceiling_4gib_GB/s": round(ceiling, 1),
+               "value_frac_of_read_ceiling": round(gbs / ceiling, 4)}
     traffic = stored_traffic("gemv_batched_dyadic_m1_llama1b_stack", gemv_bytes)
 
     if args.only is None:
@@ -435,7 +467,12 @@ def main():
                       stream, args.steps, args.warmup)
         vb = 8192 * 4096 + 2 * 8192 * 128 + 2 * 8192 + 4 * 8192
         rows["gemv_m1_8192x8192"] = {"ms": ms_v5, "GB/s": vb / (ms_v5 * 1e-3) / 1e9}
-        del W, X, P, S, Y
+        D = torch.empty((8192, 8192), dtype=torch.bfloat16, device=dev)
+        ms_d5 = timed(lambda: w4.w4_unpack_dequant(P, w4.W4_DYADIC, scales=S, out=D,
+                                                   stream=stream), stream, 50, 5)
+        db = 8192 * 4096 + 2 * 8192 * 128 + 2 * 8192 * 8192
+        rows["unpack_dequant_8192x8192"] = {"ms": ms_d5, "GB/s": db / (ms_d5 * 1e-3) / 1e9}
+        del W, X, P, S, Y, D
 
     if args.only is None:
         rows.update(other_configs(w4, synthetic, torch, dev, stream, args))
@@ -443,14 +480,14 @@ def main():
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
         ms_c = timed(lambda: dst.copy_(src), stream, 20, 5)
-        rows["context_device_copy_1gib"] = {"ms": ms_c,
-                                            "GB/s_read_plus_write": 2 * (1 << 30) / (ms_c * 1e-3) / 1e9}
+        context["device_copy_1gib_GB/s_read_plus_write"] = round(
+            2 * (1 << 30) / (ms_c * 1e-3) / 1e9, 1)
         del src, dst
 
     # ---------------------------------------------------------- CPU baseline
     cpu = None
     if not args.no_cpu_baseline and args.only is None:
-        cpu = cpu_baseline(mats, shapes)
+        cpu = cpu_baseline(mats, shapes, gbs, rows)
 
     out = {
         "metric": METRIC,
@@ -472,48 +509,134 @@ def main():
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
         "cpu_baseline": cpu,
+        "context": context,
         "rows": rows,
     }
     print(json.dumps(out), flush=True)
 
 
-CPU_BLOCKS = 8  # decoder blocks of the stack timed on the CPU (about 10-15 s of work)
+def cpu_model():
+    with open("/proc/cpuinfo") as f:
+        for line in f:
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    return "unknown"
 
 
-def cpu_baseline(mats, shapes):
-    """The oracle (numpy dequant + fp64 GEMV, one thread) on the first
-    CPU_BLOCKS decoder blocks of the stack.  Each weight is regenerated on the
-    device, copied to the host and quantized by the oracle's own C routine
-    (untimed); the timed part is the oracle's dequant + matmul per matrix."""
+def cpu_baseline(mats, shapes, gpu_gbs, rows):
+    """The C oracle (oracle/liboracle.c: OpenMP over rows, fp64 sums) timed on
+    the host's cores in the same run.  The headline entry is its fused
+    dequant + fp64 GEMV over the whole decode stack, on weights the oracle
+    quantizes itself (each regenerated on the device and copied to the host;
+    quantizing is untimed).  "rows" adds the other workloads: the 2048^2
+    GEMV on one thread, quantize_pack and sampled GEMM rows of the 8192^2
+    prefill weight, and the k-means fits; each with the GPU:CPU ratio of the
+    matching GPU row.  A reported baseline, not a target."""
     import numpy as np
     import torch
     import synthetic
-    from threadpoolctl import threadpool_limits
-    from oracle import dyadic, matmul, native, packing
-    from oracle.bits import bf16_to_f64
+    from oracle import native
 
-    sample = list(range(7 * CPU_BLOCKS))
-    log(f"cpu baseline: oracle on {len(sample)} matrices")
+    threads = native.num_threads()
+    log(f"cpu baseline: C oracle, {threads} threads")
+
+    def host(t):
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+    def ratio(gpu, cpu):
+        return round(gpu / cpu, 1) if gpu and cpu else None
+
+    # headline: fused dequant + fp64 GEMV over all 168 matrices
     nbytes, weights, dt = 0, 0, 0.0
-    for i in sample:
-        n, k = shapes[i]
+    for i, (n, k) in enumerate(shapes):
         w = synthetic.student_t_bf16_device((n, k), 4, 0.02, synthetic.seed(2, i, 0), "cuda")
-        wb = w.view(torch.int16).cpu().numpy().view(np.uint16)
+        wb = host(w)
         del w
-        xb = mats[i]["x"].view(torch.int16).cpu().numpy().view(np.uint16)
         idx, s = native.dyadic_quantize(wb)
-        p = packing.pack(idx)
-        del wb, idx
-        with threadpool_limits(limits=1):
-            t0 = time.perf_counter()
-            matmul.gemm_ref(xb, bf16_to_f64(dyadic.dequant(p, s)))
-            dt += time.perf_counter() - t0
+        del wb
+        p = np.ascontiguousarray((idx[:, 0::2] | (idx[:, 1::2] << 4)).astype(np.uint8))
+        del idx
+        xb = host(mats[i]["x"])
+        t0 = time.perf_counter()
+        native.dyadic_matmul(p, s, xb)
+        dt += time.perf_counter() - t0
         nbytes += n * k // 2 + 2 * n * (k // 64) + 2 * k + 4 * n
         weights += n * k
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {CPU_BLOCKS} decoder blocks of the stack ({len(sample)} matrices, "
-                      f"{weights:,} weights): numpy dequant + fp64 GEMV, one thread",
-            "seconds": round(dt, 2)}
+    value = nbytes / dt / 1e9
+    extra = {}
+
+    # the 2048^2 weight (seed 0): quantize + GEMV on one thread
+    w = synthetic.normal_bf16_device((2048, 2048), 0.02, synthetic.seed(0, 0, 0), "cuda")
+    x = synthetic.normal_bf16_device((1, 2048), 1.0, synthetic.seed(0, 0, 1), "cuda")
+    wb, xb = host(w), host(x)
+    native.set_num_threads(1)
+    t0 = time.perf_counter()
+    idx, s = native.dyadic_quantize(wb)
+    p = np.ascontiguousarray((idx[:, 0::2] | (idx[:, 1::2] << 4)).astype(np.uint8))
+    tq = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    native.dyadic_matmul(p, s, xb)
+    tg = time.perf_counter() - t0
+    native.set_num_threads(threads)
+    b = 2048 * 1024 + 2 * 2048 * 32 + 2 * 2048 + 4 * 2048
+    g = rows.get("gemv_m1_2048x2048_single_call", {}).get("GB/s")
+    extra["gemv_m1_2048x2048_1thread"] = {"GB/s": round(b / tg / 1e9, 4), "cores": 1,
+                                          "gpu_ratio": ratio(g, b / tg / 1e9)}
+    extra["quantize_2048x2048_1thread"] = {"s": round(tq, 3), "cores": 1}
+
+    # the 8192^2 prefill weight: quantize (all threads), GEMM on 512 sampled rows
+    w = synthetic.normal_bf16_device((8192, 8192), 0.02, synthetic.seed(5, 0, 0), "cuda")
+    X = synthetic.normal_bf16_device((256, 8192), 1.0, synthetic.seed(5, 0, 1), "cuda")
+    wb, Xb = host(w), host(X)
+    del w, X
+    t0 = time.perf_counter()
+    idx, s = native.dyadic_quantize(wb)
+    tq = time.perf_counter() - t0
+    qb = 2 * 8192 * 8192 + 8192 * 4096 + 2 * 8192 * 128
+    g = rows.get("quantize_pack_8192x8192", {}).get("GB/s")
+    extra["quantize_pack_8192x8192"] = {"GB/s": round(qb / tq / 1e9, 3), "cores": threads,
+                                        "gpu_ratio": ratio(g, qb / tq / 1e9)}
+    sel = np.random.default_rng(0).choice(8192, 512, replace=False)
+    p = np.ascontiguousarray((idx[sel, 0::2] | (idx[sel, 1::2] << 4)).astype(np.uint8))
+    s_sel = np.ascontiguousarray(s[sel])
+    del idx
+    t0 = time.perf_counter()
+    native.dyadic_matmul(p, s_sel, Xb)
+    tgm = time.perf_counter() - t0
+    tf = 2 * 256 * 512 * 8192 / tgm / 1e12
+    g = rows.get("gemm_m256_k8192_n8192", {}).get("TFLOP/s")
+    extra["gemm_m256_k8192_512_of_8192_rows"] = {"TFLOP/s": round(tf, 5), "cores": threads,
+                                                 "gpu_ratio": ratio(g, tf)}
+    del wb, Xb, p
+
+    # k-means fits: one 4096^2 LUT16 weight (3.9B shapes), one 2048^2 SIGNMAG8 weight
+    w = synthetic.normal_outliers_bf16_device((4096, 4096), 0.015, 0.001, 0.15,
+                                              synthetic.seed(3, 0, 0), "cuda")
+    wb = host(w)
+    del w
+    t0 = time.perf_counter()
+    native.lut16_fit(wb, 25)
+    tf = time.perf_counter() - t0
+    g = rows.get("lut16_fit_4096x4096", {}).get("Mgroups/s")
+    mg = 4096 * 64 / tf / 1e6
+    extra["lut16_fit_4096x4096"] = {"Mgroups/s": round(mg, 3), "cores": threads,
+                                    "gpu_ratio": ratio(g, mg)}
+    w = synthetic.student_t_bf16_device((2048, 2048), 5, 0.02, synthetic.seed(4, 0, 0), "cuda")
+    wb = host(w)
+    del w
+    t0 = time.perf_counter()
+    native.signmag8_fit(wb, 25)
+    tf = time.perf_counter() - t0
+    g = rows.get("signmag8_fit_2048x2048", {}).get("Mgroups/s")
+    mg = 2048 * 64 / tf / 1e6
+    extra["signmag8_fit_2048x2048"] = {"Mgroups/s": round(mg, 3), "cores": threads,
+                                       "gpu_ratio": ratio(g, mg)}
+
+    return {"value": round(value, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"the whole decode stack ({len(shapes)} matrices, {weights:,} weights): "
+                      f"C oracle dequant + fp64 GEMV, OpenMP over rows",
+            "cpu_model": cpu_model(), "seconds": round(dt, 2),
+            "gpu_ratio": ratio(gpu_gbs, value), "rows": extra}
 
 
 if __name__ == "__main__":

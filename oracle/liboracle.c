@@ -172,6 +172,47 @@ static int nearest_level(double x, const double* v, int nl) {
   return best;
 }
 
+/* ------------------------------------------------------------ dyadic matmul */
+/* The fp64 reference of the fused dequant-GEMV / GEMM (k-means page section
+ * 4.1; DyadicGumbel page section 2.5: unpack, rebuild, multiply) for the
+ * dyadic codec: y[i][r] = sum over c = 0, 1, ... of x[i][c] * w_hat[r][c],
+ * every product and partial sum in double, where w_hat[r][c] is the bf16
+ * value oracle_dyadic_dequant writes (RNE_bf16((s/8)(idx - 8)), a zero result
+ * +0) and x is bf16 [m][k].  packed: uint8 [n][k/2] (low nibble first);
+ * scales: bf16 [n][k/64]; y: double [m][n]. */
+int oracle_dyadic_matmul(const uint8_t* packed, const uint16_t* scales, const uint16_t* x,
+                         int64_t n, int64_t k, int64_t m, double* y) {
+  if (k % 64) return -1;
+  const int64_t g = k / 64;
+  int bad = 0;
+#pragma omp parallel
+  {
+    double* wrow = (double*)malloc(sizeof(double) * (size_t)(k > 0 ? k : 1));
+    if (!wrow) {
+#pragma omp atomic write
+      bad = 1;
+    }
+#pragma omp for schedule(static)
+    for (int64_t r = 0; r < n; ++r) {
+      if (!wrow) continue;
+      for (int64_t c = 0; c < k; ++c) {
+        const int idx = (packed[r * (k / 2) + c / 2] >> (4 * (c & 1))) & 15;
+        const double s = bf16_val(scales[r * g + c / 64]);
+        double v = (s / 8.0) * (double)(idx - 8);
+        if (v == 0.0) v = 0.0;
+        wrow[c] = bf16_val(rne_bf16(v));
+      }
+      for (int64_t i = 0; i < m; ++i) {
+        double acc = 0.0;
+        for (int64_t c = 0; c < k; ++c) acc += bf16_val(x[i * k + c]) * wrow[c];
+        y[i * n + r] = acc;
+      }
+    }
+    free(wrow);
+  }
+  return bad ? -1 : 0;
+}
+
 /* ------------------------------------------------------------ LUT16 */
 int oracle_lut16_indices(const uint16_t* w, const uint16_t* scales, const uint16_t* lut,
                          int64_t n, int64_t k, uint8_t* idx) {
@@ -283,10 +324,13 @@ int oracle_signmag8_fit(const uint16_t* w, int64_t n, int64_t k, int iters, uint
   return 0;
 }
 
-/* number of OpenMP threads a parallel region uses (reported by the benchmark) */
+/* number of OpenMP threads a parallel region uses (reported by the benchmark),
+ * and a way to change it (the benchmark times one case on a single thread) */
 #ifdef _OPENMP
 #include <omp.h>
 int oracle_num_threads(void) { return omp_get_max_threads(); }
+void oracle_set_num_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
 #else
 int oracle_num_threads(void) { return 1; }
+void oracle_set_num_threads(int n) { (void)n; }
 #endif

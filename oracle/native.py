@@ -43,11 +43,14 @@ def lib():
             "oracle_signmag8_indices": [P, P, I64, I64, P],
             "oracle_lut16_fit": [P, I64, I64, ctypes.c_int, P, P],
             "oracle_signmag8_fit": [P, I64, I64, ctypes.c_int, P],
+            "oracle_dyadic_matmul": [P, P, P, I64, I64, I64, P],
         }.items():
             fn = getattr(L, name)
             fn.argtypes = args
             fn.restype = ctypes.c_int
         L.oracle_num_threads.restype = ctypes.c_int
+        L.oracle_set_num_threads.argtypes = [ctypes.c_int]
+        L.oracle_set_num_threads.restype = None
         _lib = L
     return _lib
 
@@ -69,6 +72,10 @@ def num_threads():
     return lib().oracle_num_threads()
 
 
+def set_num_threads(n):
+    lib().oracle_set_num_threads(int(n))
+
+
 def dyadic_quantize(w_bits):
     w = _c(w_bits, np.uint16)
     n, k = w.shape
@@ -85,6 +92,18 @@ def dyadic_dequant(idx, s_bits):
     out = np.empty((n, k), np.uint16)
     _check(lib().oracle_dyadic_dequant(_p(idx), _p(s), n, k, _p(out)))
     return out
+
+
+def dyadic_matmul(packed, s_bits, x_bits):
+    """y [m, n] (fp64) = x [m, k] @ w_hat [n, k]^T for dyadic (packed, scales)."""
+    p = _c(packed, np.uint8)
+    s = _c(s_bits, np.uint16)
+    x = _c(x_bits, np.uint16)
+    n, k = p.shape[0], 2 * p.shape[1]
+    m = x.shape[0]
+    y = np.empty((m, n), np.float64)
+    _check(lib().oracle_dyadic_matmul(_p(p), _p(s), _p(x), n, k, m, _p(y)))
+    return y
 
 
 def lut16_indices(w_bits, s_bits, lut_bits):

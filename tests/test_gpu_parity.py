@@ -879,3 +879,20 @@ def test_signmag8_k_multiple_of_32_only(w4):
     with pytest.raises(w4.W4Error):
         w4.w4_gemv(p, dev_bf16(synthetic.normal_bf16((1, k), 1.0, 3501)), w4.W4_SIGNMAG8,
                    codebook=dev_f16(cb))
+
+
+# single m = 1 calls on matrices of too few rows for 4-wave blocks take one
+# 16-row tile per block of 8 or 16 waves that split k (gemv_kernel<CODEC, 8 or
+# 16, false, 4, RAGGED>): (2048, 2048) -> 8 waves, (1024, 4096) -> 16,
+# (1000, 2112) -> 8 with a partial last step, (40, 70016) -> 16 with k in
+# chunks of the block's LDS
+@pytest.mark.parametrize("codec", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("n,k", [(2048, 2048), (1024, 4096), (1000, 2112), (40, 70016)])
+def test_gemv_m1_wide_blocks(w4, codec, n, k):
+    report("gemv_m1_wide", codec=codec, n=n, k=k)
+    p, side, w_hat = _random_codec_case(codec, n, k, 3600 + codec + n)
+    x = synthetic.normal_bf16((1, k), 1.0, 3700 + n)
+    for dt in (torch.float32, torch.bfloat16):
+        y = w4.w4_gemv(dev_u8(p), dev_bf16(x), codec, y_dtype=dt, **side)
+        torch.cuda.synchronize()
+        _gemv_check(y, x, w_hat, dt == torch.bfloat16)

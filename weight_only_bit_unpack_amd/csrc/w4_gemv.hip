@@ -21,8 +21,11 @@
 //
 // The activations are staged once per block into LDS in the rebuild's slot
 // order (w4_device.h, SIGMA), in k-chunks when m * k does not fit.
-// A block is 4 waves = KSPLIT waves along k x (4 / KSPLIT) row tiles of 16.
-// With KSPLIT > 1 the waves' partial sums are added in LDS in a fixed order.
+// A block is max(4, KSPLIT) waves = KSPLIT waves along k x (waves / KSPLIT)
+// row tiles of 16.  With KSPLIT > 1 the waves' partial sums are added in LDS
+// in a fixed order.  KSPLIT = 8 and 16 (blocks of 8 and 16 waves, one row
+// tile) serve single m = 1 calls on matrices too short to fill the GPU with
+// 4-wave blocks: the waves of one 16-row tile take every 8th or 16th step.
 #include "w4_device.h"
 #include "w4_launch.h"
 
@@ -30,10 +33,11 @@
 namespace w4 {
 namespace {
 
-// Staged activations: at most 3584 16-byte units (56 KiB), so that with the
-// four 2 KiB shuffle areas a block stays within 64 KiB of LDS and two blocks
-// share a CU.
-constexpr int kXsUnitsMax = 3584;
+// Staged activations: at most 3584 16-byte units (56 KiB) for a 4-wave block,
+// so that with its four 2 KiB shuffle areas it stays within 64 KiB of LDS and
+// two blocks share a CU; blocks of more waves keep the same 64 KiB total.
+constexpr int kLdsBlockUnits = 4096;  // 64 KiB
+constexpr int kXsUnitsMax = kLdsBlockUnits - 128 * 4;
 
 // Buffer resources (V#) over one block's slice of an array: loads at an
 // offset outside [0, num_records) return zero without touching memory, so
@@ -292,10 +296,13 @@ struct Slicing {
 // first).  The batched m = 1 decode pass stages at most a few units per thread
 // and runs fastest with the fewest registers, XG = 1; elsewhere XG = 4.
 template <int CODEC, int KSPLIT, bool BATCHED, int XG, bool RAGGED>
-__global__ __launch_bounds__(256) void gemv_kernel(GemvProblem single, const GemvProblem* probs,
-                                                   int count, int m, int y_bf16, int xs_units,
-                                                   Slicing sl) {
-  constexpr int RW = 4 / KSPLIT;  // row tiles per block
+__global__ __launch_bounds__(64 * (KSPLIT > 4 ? KSPLIT : 4)) void gemv_kernel(
+    GemvProblem single, const GemvProblem* probs, int count, int m, int y_bf16, int xs_units,
+    Slicing sl) {
+  constexpr int WAVES = KSPLIT > 4 ? KSPLIT : 4;
+  constexpr int NT = 64 * WAVES;      // threads per block
+  constexpr int RW = WAVES / KSPLIT;  // row tiles per block
+  static_assert(!BATCHED || WAVES == 4, "the batched launch uses 4-wave blocks");
   extern __shared__ u32x4 xs[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
@@ -420,12 +427,12 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvProblem single, const Gem
         r.fetch(S, L, in ? st * 128u : kOOB, in ? st * Raw<CODEC>::kSideStep : kOOB);
       }
     };
-    // x staging slots: (row mrow, pass ip) -> unit tid + 256 ip of that row
-    const int ipr = (units + 255) >> 8;
+    // x staging slots: (row mrow, pass ip) -> unit tid + NT ip of that row
+    const int ipr = (units + NT - 1) / NT;
     const int nslots = m * ipr;
     auto x_off = [&](int slot, int& mrow, int& uu) -> uint32_t {
       mrow = slot / ipr;  // uniform
-      uu = tid + 256 * (slot - mrow * ipr);
+      uu = tid + NT * (slot - mrow * ipr);
       const int64_t kk = k0 + 8 * (int64_t)uu;
       return (uu < units && kk < kend) ? (uint32_t)((mrow * K + kk) * 2) : kOOB;
     };
@@ -560,21 +567,23 @@ __global__ __launch_bounds__(256) void zero_kernel(void* y, int64_t count, int y
 }
 
 // LDS units for a launch whose blocks each cover `kspan` of k: the whole
-// padded span if it fits, else the cap; never less than the 4 KiB the in-block
-// k-split reduction needs.
-int xs_units_for(int m, int64_t kspan) {
+// padded span if it fits, else the cap; never less than the 1 KiB per wave
+// the in-block k-split reduction needs.
+int xs_units_for(int m, int64_t kspan, int waves = 4) {
   const int64_t kpad = (kspan + 255) & ~(int64_t)255;
   int64_t u = (int64_t)m * (kpad / 8 + 1);
-  if (u > kXsUnitsMax) u = kXsUnitsMax;
-  if (u < 256) u = 256;
+  const int64_t cap = kLdsBlockUnits - 128 * waves;
+  if (u > cap) u = cap;
+  if (u < 64 * waves) u = 64 * waves;
   return (int)u;
 }
 
 constexpr int kMaxSliceTiles = 1024;  // row tiles of a sliced call
+constexpr int64_t kResidentWaves = 4096;  // 16 waves on each of 256 CUs
 constexpr int64_t kTargetBlocks = 512;  // two blocks per CU
 
 struct GemvShape {
-  int ksplit;       // waves along k inside a block (1, 2, 4)
+  int ksplit;       // waves along k inside a block (1, 2, 4, 8, 16)
   int kslices;      // blocks along k
   int slice_steps;  // 256-k steps per slice
 };
@@ -583,10 +592,22 @@ GemvShape gemv_shape(int64_t n, int64_t k, int m) {
   const int64_t steps = (k + 255) / 256;
   const int64_t tiles = (n + 63) / 64;
   if (m == 1 || tiles > kMaxSliceTiles) {
-    // the activations of m = 1 are small: split k between the waves of a block
+    // the activations of m = 1 are small: split k between the waves of a
+    // block.  64-row tiles (4 waves, no split) while they give 1024 blocks,
+    // else 32-row tiles; below that one 16-row tile per block whose 4, 8 or
+    // 16 waves split k: the most waves per tile whose blocks all fit on the
+    // GPU at once (these kernels keep 4 waves per SIMD, 16 per CU, resident;
+    // a second round of blocks would cost more than the extra waves gain),
+    // each wave keeping at least one 256-k step.
     int ks = 4;
-    if (tiles >= 1024) ks = 1;
-    else if ((n + 31) / 32 >= 1024) ks = 2;
+    if (tiles >= 1024) {
+      ks = 1;
+    } else if ((n + 31) / 32 >= 1024) {
+      ks = 2;
+    } else {
+      const int64_t tiles16 = (n + 15) / 16;
+      while (ks < 16 && tiles16 * 2 * ks <= kResidentWaves && 2 * ks <= steps) ks *= 2;
+    }
     if (m > 1) ks = 1;
     return {ks, 1, (int)steps};
   }
@@ -605,7 +626,8 @@ GemvShape gemv_shape(int64_t n, int64_t k, int m) {
 template <int CODEC, int KSPLIT, bool RAGGED>
 hipError_t launch_one(const GemvProblem& p, int m, int y_bf16, const GemvShape& sh,
                       hipStream_t stream) {
-  const int rows = 16 * (4 / KSPLIT);
+  constexpr int WAVES = KSPLIT > 4 ? KSPLIT : 4;
+  const int rows = 16 * (WAVES / KSPLIT);
   const int64_t blocks = (p.n + rows - 1) / rows;
   Slicing sl{sh.kslices, sh.slice_steps, nullptr};
   if (sh.kslices > 1) {
@@ -615,10 +637,10 @@ hipError_t launch_one(const GemvProblem& p, int m, int y_bf16, const GemvShape& 
     if (e != hipSuccess) return e;
     sl.part = reinterpret_cast<float*>(ws);
   }
-  const int xu = xs_units_for(m, (int64_t)sh.slice_steps * 256);
+  const int xu = xs_units_for(m, (int64_t)sh.slice_steps * 256, WAVES);
   gemv_kernel<CODEC, KSPLIT, false, 4, RAGGED>
-      <<<dim3((uint32_t)blocks, (uint32_t)sh.kslices), dim3(256), (xu + 512) * 16, stream>>>(
-          p, nullptr, 0, m, y_bf16, xu, sl);
+      <<<dim3((uint32_t)blocks, (uint32_t)sh.kslices), dim3(64 * WAVES), (xu + 128 * WAVES) * 16,
+         stream>>>(p, nullptr, 0, m, y_bf16, xu, sl);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || sh.kslices == 1) return e;
   const int64_t total = (int64_t)m * p.n;
@@ -633,7 +655,9 @@ hipError_t launch_shape(const GemvProblem& p, int m, int y_bf16, const GemvShape
   switch (sh.ksplit) {
     case 1: return launch_one<CODEC, 1, RAGGED>(p, m, y_bf16, sh, stream);
     case 2: return launch_one<CODEC, 2, RAGGED>(p, m, y_bf16, sh, stream);
-    default: return launch_one<CODEC, 4, RAGGED>(p, m, y_bf16, sh, stream);
+    case 4: return launch_one<CODEC, 4, RAGGED>(p, m, y_bf16, sh, stream);
+    case 8: return launch_one<CODEC, 8, RAGGED>(p, m, y_bf16, sh, stream);
+    default: return launch_one<CODEC, 16, RAGGED>(p, m, y_bf16, sh, stream);
   }
 }
 

@@ -42,11 +42,13 @@ def parse():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["headline", "gemm", "copy", "fit", "codec"], default=None,
+    ap.add_argument("--only", choices=["headline", "gemm", "copy", "fit", "codec", "singles"],
+                    default=None,
                     help="run one target only (for profiler runs): the batched decode pass, "
                          "the M=256 GEMM, a 1 GiB device copy that calibrates HBM counters, "
-                         "the table / magnitude fits, or quantize + dequant of one 8192^2 "
-                         "weight for every codec")
+                         "the table / magnitude fits, quantize + dequant of one 8192^2 "
+                         "weight for every codec, or single m = 1 GEMV calls (DYADIC 8192^2, "
+                         "LUT16 on the 3.9B shapes)")
     ap.add_argument("--only-headline", action="store_true", help="same as --only headline")
     a = ap.parse_args()
     if a.only_headline:
@@ -351,6 +353,31 @@ def main():
                      min(args.steps, FIT_STEPS), 1)
         print(json.dumps({"target": "signmag8_fit_warm", "shape": [2048, 2048], "ms": ms_f,
                           "Mgroups/s": 2048 * 64 / (ms_f * 1e-3) / 1e6}), flush=True)
+        return
+    if args.only == "singles":
+        W = synthetic.normal_bf16_device((8192, 8192), 0.02, synthetic.seed(5, 0, 0), dev)
+        P, S = w4.w4_quantize_pack(W, w4.W4_DYADIC)
+        x = synthetic.normal_bf16_device((1, 8192), 1.0, synthetic.seed(5, 0, 1), dev)
+        y = torch.empty((1, 8192), device=dev)
+        ms = timed(lambda: w4.w4_gemv(P, x, w4.W4_DYADIC, scales=S, y=y, stream=stream),
+                   stream, args.steps, args.warmup)
+        b = 8192 * 4096 + 2 * 8192 * 128 + 2 * 8192 + 4 * 8192
+        print(json.dumps({"target": "gemv_m1_8192x8192", "ms": ms, "GB/s": b / (ms * 1e-3) / 1e9}),
+              flush=True)
+        del W, P, S
+        for i, (n, k) in enumerate([(4096, 4096), (11008, 4096), (4096, 11008)]):
+            W = synthetic.normal_outliers_bf16_device((n, k), 0.015, 0.001, 0.15,
+                                                      synthetic.seed(3, i, 0), dev)
+            sc, L = w4.w4_lut16_fit(W, 1)
+            P, _ = w4.w4_quantize_pack(W, w4.W4_LUT16, scales=sc, codebook=L)
+            x = synthetic.normal_bf16_device((1, k), 1.0, synthetic.seed(3, i, 1), dev)
+            y = torch.empty((1, n), device=dev)
+            ms = timed(lambda: w4.w4_gemv(P, x, w4.W4_LUT16, scales=sc, codebook=L, y=y,
+                                          stream=stream), stream, args.steps, args.warmup)
+            b = n * k // 2 + n * (k // 64) * 34 + 2 * k + 4 * n
+            print(json.dumps({"target": f"lut16_gemv_m1_{n}x{k}", "ms": ms,
+                              "GB/s": b / (ms * 1e-3) / 1e9}), flush=True)
+            del W, P, sc, L
         return
     if args.only == "gemm":
         ms_g, tf = time_gemm(w4, synthetic, torch, dev, stream, args)

@@ -42,13 +42,15 @@ def parse():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["headline", "gemm", "copy", "fit", "codec", "singles"],
+    ap.add_argument("--only", choices=["headline", "gemm", "copy", "fit", "codec", "singles",
+                                       "lut16s"],
                     default=None,
                     help="run one target only (for profiler runs): the batched decode pass, "
                          "the M=256 GEMM, a 1 GiB device copy that calibrates HBM counters, "
                          "the table / magnitude fits, quantize + dequant of one 8192^2 "
-                         "weight for every codec, or single m = 1 GEMV calls (DYADIC 8192^2, "
-                         "LUT16 on the 3.9B shapes)")
+                         "weight for every codec, single m = 1 GEMV calls (DYADIC 8192^2, "
+                         "LUT16 on the 3.9B shapes), or the decode stack as LUT16S in its three "
+                         "decode variants")
     ap.add_argument("--only-headline", action="store_true", help="same as --only headline")
     a = ap.parse_args()
     if a.only_headline:
@@ -209,7 +211,19 @@ def other_configs(w4, synthetic, torch, dev, stream, args):
     batch = w4.w4_gemv_batched_plan(probs, w4.W4_LUT16S)
     ms = timed(lambda: batch(stream), stream, args.steps, args.warmup)
     rows["lut16s_gemv_m1_3.9b_shapes_batched"] = {"ms": ms, "GB/s": total / (ms * 1e-3) / 1e9}
-    del probs, batch
+    # the same three matrices decoded by per-nibble v_perm lookups instead of
+    # the byte -> pair table, and with the scales interleaved into the packed
+    # rows (same algorithmic bytes)
+    batch = w4.w4_gemv_batched_plan(probs, w4.W4_LUT16S_PERM)
+    ms = timed(lambda: batch(stream), stream, args.steps, args.warmup)
+    rows["lut16s_perm_gemv_m1_3.9b_shapes_batched"] = {"ms": ms,
+                                                       "GB/s": total / (ms * 1e-3) / 1e9}
+    il = [dict(packed=w4.w4_lut16s_interleave(p["packed"], p["scales"]), codebook=p["codebook"],
+               x=p["x"], y=p["y"]) for p in probs]
+    batch = w4.w4_gemv_batched_plan(il, w4.W4_LUT16S_IL)
+    ms = timed(lambda: batch(stream), stream, args.steps, args.warmup)
+    rows["lut16s_il_gemv_m1_3.9b_shapes_batched"] = {"ms": ms, "GB/s": total / (ms * 1e-3) / 1e9}
+    del probs, batch, il
 
     # DYADIC5 (3/4/5-bit groups in one 5-bit index space): the 1B decode stack
     # with widths 3, 4, 5 drawn per group, one batched m = 1 launch, and the
@@ -353,6 +367,31 @@ def main():
                      min(args.steps, FIT_STEPS), 1)
         print(json.dumps({"target": "signmag8_fit_warm", "shape": [2048, 2048], "ms": ms_f,
                           "Mgroups/s": 2048 * 64 / (ms_f * 1e-3) / 1e6}), flush=True)
+        return
+    if args.only == "lut16s":
+        # the 1B decode stack as LUT16S (one table of 16 quantiles per matrix),
+        # one batched m = 1 launch per decode variant: byte -> pair table
+        # (LUT16S), per-nibble v_perm lookups (LUT16S_PERM), scales interleaved
+        # into the packed rows (LUT16S_IL)
+        probs, total = [], 0
+        for i, (n, k) in enumerate(synthetic.llama1b_stack_shapes()):
+            W = synthetic.student_t_bf16_device((n, k), 4, 0.02, synthetic.seed(2, i, 0), dev)
+            sc, T = shared_table_levels(W)
+            P, _ = w4.w4_quantize_pack(W, w4.W4_LUT16S, scales=sc, codebook=T)
+            del W
+            x = synthetic.normal_bf16_device((1, k), 1.0, synthetic.seed(2, i, 1), dev)
+            probs.append({"packed": P, "scales": sc, "codebook": T, "x": x,
+                          "y": torch.empty((1, n), device=dev)})
+            total += n * k // 2 + 2 * n * (k // 64) + 32 + 2 * k + 4 * n
+        il = [dict(packed=w4.w4_lut16s_interleave(p["packed"], p["scales"]),
+                   codebook=p["codebook"], x=p["x"], y=p["y"]) for p in probs]
+        for name, codec, pr in (("lut16s", w4.W4_LUT16S, probs),
+                                ("lut16s_perm", w4.W4_LUT16S_PERM, probs),
+                                ("lut16s_il", w4.W4_LUT16S_IL, il)):
+            batch = w4.w4_gemv_batched_plan(pr, codec)
+            ms = timed(lambda: batch(stream), stream, args.steps, args.warmup)
+            print(json.dumps({"target": f"{name}_gemv_m1_llama1b_stack", "ms": ms,
+                              "GB/s": total / (ms * 1e-3) / 1e9}), flush=True)
         return
     if args.only == "singles":
         W = synthetic.normal_bf16_device((8192, 8192), 0.02, synthetic.seed(5, 0, 0), dev)

@@ -89,12 +89,28 @@ typedef enum {
  * 5-bit index space (the b-bit code j is the 5-bit code j * 2^(5-b)), so a
  * group's width only restricts which codes it may take; see
  * w4_quantize_dyadic5.  Reconstruction RNE_bf16((s/16) * (j5 - 16)). */
+/* [KM] sec. 2.2 decodes by looking up precomputed values of every byte and
+ * stores the scales with the indices.  The W4_LUT16S GEMV decodes a packed
+ * byte at a time through a 256-entry table of level pairs (L[b & 15],
+ * L[b >> 4]) held in LDS.  Two variants are kept for comparison:
+ * W4_LUT16S_PERM: the LUT16S storage and results, with a GEMV that looks the
+ *   levels up per nibble from byte-plane tables with v_perm, as LUT16 does.
+ *   Every other call treats it exactly as W4_LUT16S.
+ * W4_LUT16S_IL: the LUT16S weight with each row's scales interleaved into its
+ *   packed bytes (k a multiple of 256): per 256-k block a 144-byte record of
+ *   the block's 128 packed bytes, its four bf16 scales and 8 zero bytes, so
+ *   `packed` is uint8 [n][k/256 * 144] and `scales` is unused.  Built from the
+ *   planar arrays by w4_lut16s_interleave; taken by w4_gemv and the batched
+ *   GEMV (bit-identical to W4_LUT16S); the other calls return
+ *   W4_EUNSUPPORTED. */
 typedef enum {
   W4_DYADIC = 0,
   W4_LUT16 = 1,
   W4_SIGNMAG8 = 2,
   W4_LUT16S = 3,
-  W4_DYADIC5 = 4
+  W4_DYADIC5 = 4,
+  W4_LUT16S_PERM = 5,
+  W4_LUT16S_IL = 6
 } w4_codec;
 
 /* Largest k of a matrix product call: keeps every per-block byte offset of the
@@ -107,8 +123,8 @@ typedef enum { W4_F32 = 0, W4_BF16 = 1, W4_F16 = 2 } w4_dtype;
 /* Human-readable name of a status code (static string, never NULL). */
 const char* w4_status_str(int32_t status);
 
-/* Weights per group of a codec: 64 (DYADIC, LUT16, LUT16S, DYADIC5), 32 (SIGNMAG8);
- * -1 if unknown. */
+/* Weights per group of a codec: 64 (DYADIC, LUT16, LUT16S and its variants,
+ * DYADIC5), 32 (SIGNMAG8); -1 if unknown. */
 int32_t w4_group_size(int32_t codec);
 
 /*
@@ -170,6 +186,19 @@ w4_status w4_unpack_dequant(int32_t codec, int64_t n, int64_t k, const uint8_t* 
  */
 w4_status w4_quantize_dyadic5(int64_t n, int64_t k, const uint16_t* w, const uint8_t* widths,
                               uint8_t* packed, uint8_t* msb, uint16_t* scales, void* stream);
+
+/*
+ * w4_lut16s_interleave -- the W4_LUT16S_IL layout of a W4_LUT16S weight
+ * [n][k]: out[r] holds, for each 256-k block j, packed[r][128 j .. 128 j + 127],
+ * then scales[r][4 j .. 4 j + 3] (bf16, little-endian), then 8 zero bytes.
+ * [KM] sec. 2.2 (scales interleaved with the indices).
+ * packed: uint8 [n][k/2], 16-byte aligned; scales: bf16 [n][k/64], 2-byte
+ * aligned; out: uint8 [n][k/256 * 144], 16-byte aligned.
+ * Errors: W4_EINVAL (negative size, null pointer), W4_ESHAPE (k % 256 != 0),
+ * W4_EALIGN.
+ */
+w4_status w4_lut16s_interleave(int64_t n, int64_t k, const uint8_t* packed,
+                               const uint16_t* scales, uint8_t* out, void* stream);
 
 /*
  * w4_lut16_fit -- fit the LUT16 side tables of a bf16 weight [n][k]: per group

@@ -191,3 +191,34 @@ def fit_shared(w_bits, iters=LLOYD_ITERS):
         cnt = np.bincount(a, minlength=N_LEVELS)
         c = np.where(cnt > 0, sums / np.maximum(cnt, 1), c)
     return s_bits, rne_bf16(c)
+
+
+# ----------------------------------------------------------------- LUT16S_IL
+# The k-means page (section 2.2) suggests storing the scales with the indices
+# so that one read brings both.  Layout only, no arithmetic: per row and
+# 256-k block, a 144-byte record of the block's 128 packed bytes, its four
+# bf16 scales (little-endian) and 8 zero bytes.
+
+IL_RECORD = 144
+
+
+def interleave(packed, s_bits):
+    """packed uint8 [N, K/2], scale bits [N, K/64] (K % 256 == 0) -> uint8 [N, K/256 * 144]."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    n, half = packed.shape
+    nb = 2 * half // 256
+    out = np.zeros((n, nb, IL_RECORD), np.uint8)
+    out[:, :, :128] = packed.reshape(n, nb, 128)
+    sc = np.ascontiguousarray(np.asarray(s_bits, dtype="<u2").reshape(n, nb, 4))
+    out[:, :, 128:136] = sc.view(np.uint8).reshape(n, nb, 8)
+    return out.reshape(n, nb * IL_RECORD)
+
+
+def deinterleave(il):
+    """Inverse of interleave: uint8 [N, K/256 * 144] -> (packed [N, K/2], scale bits [N, K/64])."""
+    il = np.asarray(il, dtype=np.uint8)
+    n = il.shape[0]
+    rec = il.reshape(n, -1, IL_RECORD)
+    packed = np.ascontiguousarray(rec[:, :, :128]).reshape(n, -1)
+    s_bits = np.ascontiguousarray(rec[:, :, 128:136]).view("<u2").reshape(n, -1).astype(np.uint16)
+    return packed, s_bits

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(w4):
 
 
 def test_group_sizes_and_status_strings(w4):
-    assert [w4.w4_group_size(c) for c in (0, 1, 2, 3, 4, 7)] == [64, 64, 32, 64, 64, -1]
+    assert [w4.w4_group_size(c) for c in (0, 1, 2, 3, 4, 5, 6, 7)] == [64, 64, 32, 64, 64, 64, 64, -1]
     for s in range(6):
         assert w4.w4_status_str(s).startswith("W4_")
 
@@ -53,7 +53,7 @@ def _gemv(w4, codec=0, n=16, k=64, packed=16, scales=16, cb=16, x=16, m=1, y=16,
 
 def test_validation_errors(w4):
     E = {"inval": 1, "shape": 2, "align": 3, "unsup": 4}
-    assert _gemv(w4, codec=5) == E["inval"]
+    assert _gemv(w4, codec=7) == E["inval"]
     assert _gemv(w4, n=-1) == E["inval"]
     assert _gemv(w4, k=96) == E["shape"]
     assert _gemv(w4, m=17) == E["shape"]
@@ -215,3 +215,22 @@ def test_batched_flags_checked(w4):
     never writes (before any launch)."""
     info = w4.W4BatchInfo(total_tiles=1, k_min=64, k_max=64, count=1, m=1, tile_rows=64, flags=2)
     assert w4._lib.w4_gemv_batched(0, 1, 0, ctypes.c_void_p(16), ctypes.byref(info), None) == 1
+
+
+def test_lut16s_variants_rules(w4):
+    """W4_LUT16S_PERM takes LUT16S's side data everywhere; W4_LUT16S_IL needs k
+    a multiple of 256 and a codebook, no scales, and only the GEMV takes it;
+    w4_lut16s_interleave validates like the other layout calls."""
+    E = {"inval": 1, "shape": 2, "unsup": 4}
+    assert _gemv(w4, codec=5, scales=None) == E["inval"]
+    assert _gemv(w4, codec=5, cb=None) == E["inval"]
+    assert _gemv(w4, codec=6, k=192, scales=None) == E["shape"]
+    assert _gemv(w4, codec=6, k=256, scales=None, cb=None) == E["inval"]
+    assert _gemv(w4, codec=6, k=256, scales=None, fn="w4_gemm") == E["unsup"]
+    assert w4._lib.w4_quantize_pack(6, 4, 256, ctypes.c_void_p(16), ctypes.c_void_p(16), None,
+                                    ctypes.c_void_p(16), None) == E["unsup"]
+    assert w4._lib.w4_unpack_dequant(6, 4, 256, ctypes.c_void_p(16), None, ctypes.c_void_p(16),
+                                     ctypes.c_void_p(16), None) == E["unsup"]
+    assert w4._lib.w4_lut16s_interleave(4, 192, None, None, None, None) == E["shape"]
+    assert w4._lib.w4_lut16s_interleave(4, 256, None, None, None, None) == E["inval"]
+    assert w4._lib.w4_lut16s_interleave(-1, 256, None, None, None, None) == E["inval"]

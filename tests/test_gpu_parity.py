@@ -896,3 +896,80 @@ def test_gemv_m1_wide_blocks(w4, codec, n, k):
         y = w4.w4_gemv(dev_u8(p), dev_bf16(x), codec, y_dtype=dt, **side)
         torch.cuda.synchronize()
         _gemv_check(y, x, w_hat, dt == torch.bfloat16)
+
+
+# ------------------------------------------------------------------ LUT16S variants
+@pytest.mark.parametrize("n,k", [(300, 1024), (37, 2048), (5, 256)])
+def test_lut16s_interleave_layout(w4, n, k):
+    """w4_lut16s_interleave == the oracle's layout function, byte for byte."""
+    report("lut16s_interleave", n=n, k=k)
+    g = np.random.default_rng(3800 + n)
+    p = g.integers(0, 256, (n, k // 2)).astype(np.uint8)
+    s = g.integers(0, 1 << 16, (n, k // 64)).astype(np.uint16)
+    out = w4.w4_lut16s_interleave(dev_u8(p), dev_bf16(s))
+    torch.cuda.synchronize()
+    assert np.array_equal(host_u8(out), lut16.interleave(p, s))
+
+
+@pytest.mark.parametrize("m", [1, 4, 16])
+@pytest.mark.parametrize("n,k", [(300, 1024), (2048, 2048), (64, 70144)])
+def test_lut16s_perm_and_interleaved_gemv(w4, m, n, k):
+    """The per-nibble v_perm decode (W4_LUT16S_PERM) and the interleaved layout
+    (W4_LUT16S_IL) beside LUT16S's byte -> pair decode: single calls within
+    tolerance of the oracle on the LUT16S weight; the interleaved GEMV, which
+    decodes as LUT16S does, bit-identical to the LUT16S call; the PERM
+    variant's quantize, dequant and GEMM the LUT16S ones, bit for bit."""
+    report("lut16s_variants", n=n, k=k, m=m)
+    w, s, T, tables, idx = _lut16s_case(n, k, 3900 + n + m)
+    w_hat = bits.bf16_to_f64(lut16.dequant_from_indices(idx, s, tables))
+    x = synthetic.normal_bf16((m, k), 1.0, 3901 + m)
+    p = packing.pack(idx)
+    pd, sd, td, xd = dev_u8(p), dev_bf16(s), dev_bf16(T), dev_bf16(x)
+    y3 = w4.w4_gemv(pd, xd, w4.W4_LUT16S, scales=sd, codebook=td)
+    y5 = w4.w4_gemv(pd, xd, w4.W4_LUT16S_PERM, scales=sd, codebook=td)
+    il = w4.w4_lut16s_interleave(pd, sd)
+    y6 = w4.w4_gemv(il, xd, w4.W4_LUT16S_IL, codebook=td)
+    yb = w4.w4_gemv(il, xd, w4.W4_LUT16S_IL, codebook=td, y_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    _gemv_check(y3, x, w_hat, False)
+    _gemv_check(y5, x, w_hat, False)
+    _gemv_check(y6, x, w_hat, False)
+    _gemv_check(yb, x, w_hat, True)
+    assert torch.equal(y6, y3)
+    if n * k <= 1 << 20:
+        q5, _ = w4.w4_quantize_pack(dev_bf16(w), w4.W4_LUT16S_PERM, scales=sd, codebook=td)
+        d5 = w4.w4_unpack_dequant(pd, w4.W4_LUT16S_PERM, scales=sd, codebook=td)
+        g3 = w4.w4_gemm(pd, dev_bf16(synthetic.normal_bf16((130, k), 1.0, 5)), w4.W4_LUT16S,
+                        scales=sd, codebook=td)
+        g5 = w4.w4_gemm(pd, dev_bf16(synthetic.normal_bf16((130, k), 1.0, 5)), w4.W4_LUT16S_PERM,
+                        scales=sd, codebook=td)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_u8(q5), p)
+        assert np.array_equal(host_bits(d5), lut16.dequant_from_indices(idx, s, tables))
+        assert torch.equal(g3, g5)
+
+
+@pytest.mark.parametrize("codec", [5, 6])
+@pytest.mark.parametrize("m", [1, 4])
+def test_lut16s_variants_batched(w4, codec, m):
+    """Both variants through the batched launch: problems of several shapes
+    (64-row tiles and, for m = 1 over few rows, 32 / 16-row tiles)."""
+    report("lut16s_variants_batched", codec=codec, m=m)
+    probs, refs = [], []
+    for i, (n, k) in enumerate([(300, 1024), (129, 2048), (64, 256), (1000, 512)]):
+        w, s, T, tables, idx = _lut16s_case(n, k, 4000 + 10 * codec + i)
+        w_hat = bits.bf16_to_f64(lut16.dequant_from_indices(idx, s, tables))
+        x = synthetic.normal_bf16((m, k), 1.0, 4100 + i)
+        pd, sd = dev_u8(packing.pack(idx)), dev_bf16(s)
+        y = torch.full((m, n), float("nan"), device="cuda")
+        if codec == 6:
+            probs.append(dict(packed=w4.w4_lut16s_interleave(pd, sd), codebook=dev_bf16(T),
+                              x=dev_bf16(x), y=y))
+        else:
+            probs.append(dict(packed=pd, scales=sd, codebook=dev_bf16(T), x=dev_bf16(x), y=y))
+        refs.append((x, w_hat))
+    batch = w4.w4_gemv_batched_plan(probs, codec)
+    batch()
+    torch.cuda.synchronize()
+    for pr, (x, w_hat) in zip(probs, refs):
+        _gemv_check(pr["y"], x, w_hat, False)

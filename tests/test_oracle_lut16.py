@@ -320,3 +320,25 @@ def test_signmag8_c_matches_python_on_ties():
     # 0 rounds: the centres are the magnitudes of sorted rank 4q + 2
     a = np.sort(np.abs(bits.bf16_to_f64(w[0, :32])))
     assert np.array_equal(signmag8.fit(w, 0)[0, 0], bits.rne_fp16(a[2::4]))
+
+
+# ------------------------------------------------------------------ LUT16S_IL layout
+def test_interleave_layout_by_hand():
+    """One row of k = 512: two records of 144 bytes, each the block's 128
+    packed bytes, its four scales little-endian, then 8 zero bytes."""
+    packed = (np.arange(256) % 251).astype(np.uint8)[None, :]
+    scales = np.array([[0x1234, 0xABCD, 0x0001, 0xFF00, 0x0102, 0x0304, 0x0506, 0x0708]], np.uint16)
+    il = lut16.interleave(packed, scales)
+    assert il.shape == (1, 288)
+    assert list(il[0, :128]) == list(packed[0, :128])
+    assert list(il[0, 128:144]) == [0x34, 0x12, 0xCD, 0xAB, 0x01, 0x00, 0x00, 0xFF] + [0] * 8
+    assert list(il[0, 144:272]) == list(packed[0, 128:])
+    assert list(il[0, 272:288]) == [0x02, 0x01, 0x04, 0x03, 0x06, 0x05, 0x08, 0x07] + [0] * 8
+
+
+def test_interleave_roundtrip():
+    g = np.random.default_rng(12)
+    packed = g.integers(0, 256, (7, 1024)).astype(np.uint8)     # k = 2048
+    scales = g.integers(0, 1 << 16, (7, 32)).astype(np.uint16)
+    p2, s2 = lut16.deinterleave(lut16.interleave(packed, scales))
+    assert np.array_equal(p2, packed) and np.array_equal(s2, scales)

@@ -18,8 +18,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libw4.so")
 
 W4_DYADIC, W4_LUT16, W4_SIGNMAG8, W4_LUT16S, W4_DYADIC5 = 0, 1, 2, 3, 4
+W4_LUT16S_PERM, W4_LUT16S_IL = 5, 6
 W4_F32, W4_BF16, W4_F16 = 0, 1, 2
-GROUP = {W4_DYADIC: 64, W4_LUT16: 64, W4_SIGNMAG8: 32, W4_LUT16S: 64, W4_DYADIC5: 64}
+GROUP = {W4_DYADIC: 64, W4_LUT16: 64, W4_SIGNMAG8: 32, W4_LUT16S: 64, W4_DYADIC5: 64,
+         W4_LUT16S_PERM: 64, W4_LUT16S_IL: 64}
+IL_RECORD = 144  # bytes of one W4_LUT16S_IL record (256 weights)
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -50,6 +53,7 @@ _SIGS = {
     "w4_signmag8_fit": ([_I64, _I64, _P, _P, _I32, _P], _I32),
     "w4_signmag8_fit_warm": ([_I64, _I64, _P, _P, _P, _I32, _P], _I32),
     "w4_quantize_dyadic5": ([_I64, _I64, _P, _P, _P, _P, _P, _P], _I32),
+    "w4_lut16s_interleave": ([_I64, _I64, _P, _P, _P, _P], _I32),
     "w4_gemv": ([_I32, _I64, _I64, _P, _P, _P, _P, _I32, _P, _I32, _P], _I32),
     "w4_gemm": ([_I32, _I64, _I64, _P, _P, _P, _P, _I32, _P, _I32, _P], _I32),
     "w4_gemm_noalloc": ([_I32, _I64, _I64, _P, _P, _P, _P, _I32, _P, _I32, _P], _I32),
@@ -115,15 +119,22 @@ def _need(t, name, dtypes, shape=None):
     return t
 
 
+def _k_of(codec, packed):
+    """k of a quantized weight from its packed array's shape."""
+    if codec == W4_LUT16S_IL:
+        return packed.shape[1] // IL_RECORD * 256
+    return 2 * packed.shape[1]
+
+
 def _side_tables(codec, n, k, scales, codebook):
     g = GROUP[codec]
-    if codec in (W4_DYADIC, W4_LUT16, W4_LUT16S, W4_DYADIC5):
+    if codec in (W4_DYADIC, W4_LUT16, W4_LUT16S, W4_DYADIC5, W4_LUT16S_PERM):
         _need(scales, "scales", _U16, (n, k // 64))
     if codec == W4_DYADIC5:
         _need(codebook, "codebook (high-bit plane)", (torch.uint8,), (n, k // 8))
     if codec == W4_LUT16:
         _need(codebook, "codebook", _U16, (n, k // 64, 16))
-    if codec == W4_LUT16S:
+    if codec in (W4_LUT16S, W4_LUT16S_PERM, W4_LUT16S_IL):
         _need(codebook, "codebook", _U16, (16,))
     if codec == W4_SIGNMAG8:
         _need(codebook, "codebook", _U16, (n, k // g, 8))
@@ -150,10 +161,10 @@ def w4_quantize_pack(w, codec=W4_DYADIC, *, scales=None, codebook=None, packed=N
 
 def w4_unpack_dequant(packed, codec=W4_DYADIC, *, scales=None, codebook=None, out=None,
                       stream=None):
-    """Dense rebuilt weight: bf16 [n, k] (DYADIC, LUT16) or fp16 (SIGNMAG8)."""
+    """Dense rebuilt weight: bf16 [n, k] (DYADIC, LUT16, LUT16S and its
+    variants, DYADIC5) or fp16 (SIGNMAG8)."""
     _need(packed, "packed", (torch.uint8,))
-    n, k2 = packed.shape
-    k = 2 * k2
+    n, k = packed.shape[0], _k_of(codec, packed)
     _side_tables(codec, n, k, scales, codebook)
     dt = torch.float16 if codec == W4_SIGNMAG8 else torch.bfloat16
     if out is None:
@@ -237,8 +248,8 @@ def w4_signmag8_fit_warm(w, iters=25, *, codebook=None, params=None, stream=None
 
 def _matmul(fn, packed, x, codec, scales, codebook, y, y_dtype, stream):
     _need(packed, "packed", (torch.uint8,))
-    n, k2 = packed.shape
-    k = 2 * k2
+    n = packed.shape[0]
+    k = _k_of(codec, packed)
     _side_tables(codec, n, k, scales, codebook)
     _need(x, "x", _U16)
     if x.dim() != 2 or x.shape[1] != k:
@@ -252,6 +263,20 @@ def _matmul(fn, packed, x, codec, scales, codebook, y, y_dtype, stream):
     _check(fn(codec, n, k, _ptr(packed), _ptr(scales), _ptr(codebook), _ptr(x), m, _ptr(y),
               code, _stream(stream)))
     return y
+
+
+def w4_lut16s_interleave(packed, scales, out=None, stream=None):
+    """The W4_LUT16S_IL records of a LUT16S weight (packed [n, k/2], scales
+    [n, k/64], k a multiple of 256) -> uint8 [n, k/256 * 144]."""
+    _need(packed, "packed", (torch.uint8,))
+    n, k = packed.shape[0], 2 * packed.shape[1]
+    _need(scales, "scales", _U16, (n, k // 64))
+    if out is None:
+        out = torch.empty((n, k // 256 * IL_RECORD), dtype=torch.uint8, device=packed.device)
+    _need(out, "out", (torch.uint8,), (n, k // 256 * IL_RECORD))
+    _check(_lib.w4_lut16s_interleave(n, k, _ptr(packed), _ptr(scales), _ptr(out),
+                                     _stream(stream)))
+    return out
 
 
 def w4_gemv(packed, x, codec=W4_DYADIC, *, scales=None, codebook=None, y=None,
@@ -311,7 +336,7 @@ def w4_gemv_batched_plan(problems, codec=W4_DYADIC, y_dtype=torch.float32):
     for i, p in enumerate(problems):
         packed, x, y = p["packed"], p["x"], p["y"]
         _need(packed, "packed", (torch.uint8,))
-        n, k = packed.shape[0], 2 * packed.shape[1]
+        n, k = packed.shape[0], _k_of(codec, packed)
         _side_tables(codec, n, k, p.get("scales"), p.get("codebook"))
         _need(x, "x", _U16, (x.shape[0], k))
         _need(y, "y", (torch.float32,) if code == W4_F32 else _U16, (x.shape[0], n))

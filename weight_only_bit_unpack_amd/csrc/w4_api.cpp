@@ -18,8 +18,11 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 bool valid_codec(int32_t c) {
   return c == W4_DYADIC || c == W4_LUT16 || c == W4_SIGNMAG8 || c == W4_LUT16S ||
-         c == W4_DYADIC5;
+         c == W4_DYADIC5 || c == W4_LUT16S_PERM || c == W4_LUT16S_IL;
 }
+
+// W4_LUT16S_PERM shares LUT16S's storage and every kernel but the GEMV's.
+int32_t storage_codec(int32_t c) { return c == W4_LUT16S_PERM ? W4_LUT16S : c; }
 
 // Checks the quantized-weight triple of a codec for an [n][k] weight.  k must
 // be a multiple of 64, or for SIGNMAG8 outside the matrix calls (whose kernels
@@ -29,14 +32,17 @@ w4_status check_weight(int32_t codec, int64_t n, int64_t k, const void* packed, 
   if (!valid_codec(codec)) return W4_EINVAL;
   if (n < 0 || k < 0) return W4_EINVAL;
   if (k % ((codec == W4_SIGNMAG8 && !matmul) ? 32 : 64)) return W4_ESHAPE;
+  if (codec == W4_LUT16S_IL && k % 256) return W4_ESHAPE;
   if (n == 0 || k == 0) return W4_OK;
   if (!packed) return W4_EINVAL;
   if (!aligned(packed, 16)) return W4_EALIGN;
+  codec = storage_codec(codec);
   if (codec == W4_DYADIC || codec == W4_LUT16 || codec == W4_LUT16S || codec == W4_DYADIC5) {
     if (!scales) return W4_EINVAL;
     if (!aligned(scales, 2)) return W4_EALIGN;
   }
-  if (codec == W4_LUT16 || codec == W4_SIGNMAG8 || codec == W4_LUT16S || codec == W4_DYADIC5) {
+  if (codec == W4_LUT16 || codec == W4_SIGNMAG8 || codec == W4_LUT16S || codec == W4_DYADIC5 ||
+      codec == W4_LUT16S_IL) {
     if (!codebook) return W4_EINVAL;
     if (!aligned(codebook, 16)) return W4_EALIGN;
   }
@@ -106,6 +112,8 @@ int32_t w4_group_size(int32_t codec) {
     case W4_DYADIC: return 64;
     case W4_LUT16: return 64;
     case W4_LUT16S: return 64;
+    case W4_LUT16S_PERM: return 64;
+    case W4_LUT16S_IL: return 64;
     case W4_DYADIC5: return 64;
     case W4_SIGNMAG8: return 32;
     default: return -1;
@@ -117,11 +125,11 @@ w4_status w4_quantize_pack(int32_t codec, int64_t n, int64_t k, const uint16_t* 
                            void* stream) {
   w4_status st = check_weight(codec, n, k, packed, scales, codebook);
   if (st != W4_OK) return st;
-  if (codec == W4_DYADIC5) return W4_EUNSUPPORTED;
+  if (codec == W4_DYADIC5 || codec == W4_LUT16S_IL) return W4_EUNSUPPORTED;
   if (n == 0 || k == 0) return W4_OK;
   if (!w) return W4_EINVAL;
   if (!aligned(w, 16)) return W4_EALIGN;
-  return launched(w4::launch_quantize(codec, n, k, w, packed, scales, codebook,
+  return launched(w4::launch_quantize(storage_codec(codec), n, k, w, packed, scales, codebook,
                                       static_cast<hipStream_t>(stream)));
 }
 
@@ -130,11 +138,23 @@ w4_status w4_unpack_dequant(int32_t codec, int64_t n, int64_t k, const uint8_t* 
                             void* stream) {
   w4_status st = check_weight(codec, n, k, packed, scales, codebook);
   if (st != W4_OK) return st;
+  if (codec == W4_LUT16S_IL) return W4_EUNSUPPORTED;
   if (n == 0 || k == 0) return W4_OK;
   if (!out) return W4_EINVAL;
   if (!aligned(out, 16)) return W4_EALIGN;
-  return launched(w4::launch_dequant(codec, n, k, packed, scales, codebook, out,
+  return launched(w4::launch_dequant(storage_codec(codec), n, k, packed, scales, codebook, out,
                                      static_cast<hipStream_t>(stream)));
+}
+
+w4_status w4_lut16s_interleave(int64_t n, int64_t k, const uint8_t* packed, const uint16_t* scales,
+                               uint8_t* out, void* stream) {
+  if (n < 0 || k < 0) return W4_EINVAL;
+  if (k % 256 != 0) return W4_ESHAPE;
+  if (n == 0 || k == 0) return W4_OK;
+  if (!packed || !scales || !out) return W4_EINVAL;
+  if (!aligned(packed, 16) || !aligned(out, 16) || !aligned(scales, 2)) return W4_EALIGN;
+  return launched(w4::launch_lut16s_interleave(n, k, packed, scales, out,
+                                               static_cast<hipStream_t>(stream)));
 }
 
 w4_status w4_quantize_dyadic5(int64_t n, int64_t k, const uint16_t* w, const uint8_t* widths,
@@ -206,12 +226,13 @@ w4_status w4_gemm(int32_t codec, int64_t n, int64_t k, const uint8_t* packed,
                   int32_t m, void* y, int32_t y_dtype, void* stream) {
   w4_status st = check_matmul(codec, n, k, packed, scales, codebook, x, m, y, y_dtype, kGemmMaxM);
   if (st != W4_OK) return st;
+  if (codec == W4_LUT16S_IL) return W4_EUNSUPPORTED;
   if (m == 0 || n == 0) return W4_OK;
   if (k == 0)  // the empty sum
     return launched(w4::launch_zero(y, (int64_t)m * n, y_dtype == W4_BF16,
                                     static_cast<hipStream_t>(stream)));
-  return launched(w4::launch_gemm(codec, problem(n, k, packed, scales, codebook, x, y), m,
-                                  y_dtype == W4_BF16, static_cast<hipStream_t>(stream), nullptr));
+  return launched(w4::launch_gemm(storage_codec(codec), problem(n, k, packed, scales, codebook, x, y),
+                                  m, y_dtype == W4_BF16, static_cast<hipStream_t>(stream), nullptr));
 }
 
 w4_status w4_gemm_noalloc(int32_t codec, int64_t n, int64_t k, const uint8_t* packed,
@@ -219,10 +240,12 @@ w4_status w4_gemm_noalloc(int32_t codec, int64_t n, int64_t k, const uint8_t* pa
                           int32_t m, void* y, int32_t y_dtype, void* stream) {
   w4_status st = check_matmul(codec, n, k, packed, scales, codebook, x, m, y, y_dtype, kGemmMaxM);
   if (st != W4_OK) return st;
+  if (codec == W4_LUT16S_IL) return W4_EUNSUPPORTED;
   if (m == 0 || n == 0) return W4_OK;
   if (k == 0)
     return launched(w4::launch_zero(y, (int64_t)m * n, y_dtype == W4_BF16,
                                     static_cast<hipStream_t>(stream)));
+  codec = storage_codec(codec);
   if (w4::gemm_workspace_bytes(codec, n, k, m) > w4::kNoallocScratchBytes) return W4_ESHAPE;
   char* ws = nullptr;
   if (w4::noalloc_scratch(&ws) != hipSuccess) return W4_EHIP;

@@ -302,6 +302,22 @@ __device__ __forceinline__ u32x4 lut16_rebuild(uint32_t p, const Lut16Table& t) 
   return o;
 }
 
+// ---------------------------------------------------------------- byte -> pair table
+// LUT16S decoded a byte at a time: entry b of a 256-entry LDS table holds the
+// two normalised levels (L[b & 15], L[b >> 4]) as fp32, so a packed byte
+// yields its two weights with one LDS read, two products by the group scale
+// (exact in fp32, as in lut16_table) and one conversion (the one RNE).  One
+// packed dword -> 8 bf16 values in natural k order.
+__device__ __forceinline__ u32x4 pair_rebuild(uint32_t p, float s, const f32x2* tab) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f32x2 v = tab[(p >> (8 * i)) & 0xFFu];
+    r[i] = cvt_pk_bf16(v.x * s, v.y * s);
+  }
+  return r;
+}
+
 // ---------------------------------------------------------------- SIGNMAG8
 // w_hat = +-M[mag] in fp16.  bf16 MFMA needs bf16 operands, so every fp16 level
 // is split exactly as M = H + Lo with H = RNE_bf16(M) and Lo = M - H (at most 3

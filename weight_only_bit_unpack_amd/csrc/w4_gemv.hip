@@ -100,10 +100,21 @@ struct Shuffle {
   }
 };
 
-// The one 16-level table of a LUT16S weight, loaded once per wave.
+// The one 16-level table of a LUT16S weight: as 16 bf16 levels in registers
+// for the v_perm decode (LUT16S_PERM), as the block's 256-entry pair table in
+// LDS for the byte -> pair decode (LUT16S, LUT16S_IL).
 struct SharedTable {
   u32x4 l0, l1;
+  const f32x2* tab;
 };
+
+// LUT16S weights are decoded a packed byte at a time through a 256-entry LDS
+// table of level pairs (measured faster on the decode stack than the
+// per-group byte-plane v_perm lookups of LUT16, which W4_LUT16S_PERM = 5
+// keeps for comparison).  W4_LUT16S_IL = 6 is LUT16S with each row's scales
+// interleaved into its packed bytes: per 256-k block a 144-byte record of 128
+// bytes of nibbles, the block's four bf16 scales and 8 zero bytes.
+constexpr uint32_t kIlRecord = 144;
 
 // Raw per-step loads of one lane: 32 packed bytes plus the side data of the
 // group(s) they belong to.  `sp` / `ss` are the step's uniform byte offsets
@@ -113,6 +124,7 @@ struct Raw;
 
 template <>
 struct Raw<0> {  // DYADIC: one bf16 scale per 64-group
+  static constexpr uint32_t kPackedStep = 128;  // packed bytes per row and 256-k step
   static constexpr uint32_t kSideStep = 8;  // 4 groups x 2 bytes per 256-k step
   u32x4 a0, a1;
   uint16_t sb;
@@ -141,6 +153,7 @@ struct Raw<0> {  // DYADIC: one bf16 scale per 64-group
 
 template <>
 struct Raw<1> {  // LUT16: 16 bf16 levels (side) + bf16 scale (side2) per 64-group
+  static constexpr uint32_t kPackedStep = 128;
   static constexpr uint32_t kSideStep = 128;  // 4 groups x 32 bytes
   u32x4 a0, a1, l0, l1;
   uint16_t sb;
@@ -167,6 +180,7 @@ struct Raw<1> {  // LUT16: 16 bf16 levels (side) + bf16 scale (side2) per 64-gro
 
 template <>
 struct Raw<2> {  // SIGNMAG8: two 32-groups, 8 fp16 magnitudes each
+  static constexpr uint32_t kPackedStep = 128;
   static constexpr uint32_t kSideStep = 128;  // 8 groups x 16 bytes
   u32x4 a0, a1, c0, c1;
   __device__ __forceinline__ void fetch(const Slice& S, const LaneBase& L, uint32_t sp,
@@ -194,8 +208,9 @@ struct Raw<2> {  // SIGNMAG8: two 32-groups, 8 fp16 magnitudes each
 };
 
 template <>
-struct Raw<3> {  // LUT16S: one bf16 scale per 64-group (side); levels shared
-  static constexpr uint32_t kSideStep = 8;  // 4 groups x 2 bytes per 256-k step
+struct Raw<3> {  // LUT16S: bf16 scale per 64-group; byte -> pair table (natural k order)
+  static constexpr uint32_t kPackedStep = 128;
+  static constexpr uint32_t kSideStep = 8;
   u32x4 a0, a1;
   uint16_t sb;
   __device__ __forceinline__ void fetch(const Slice& S, const LaneBase& L, uint32_t sp,
@@ -209,14 +224,15 @@ struct Raw<3> {  // LUT16S: one bf16 scale per 64-group (side); levels shared
     u32x4 p0, p1;
     sh(a0, a1, p0, p1);
     const uint32_t pw[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-    const Lut16Table t = lut16_table(sb, st.l0, st.l1);
+    const float s = bf16_bits_to_f32(sb);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) mma(j, lut16_rebuild(pw[j], t));
+    for (int j = 0; j < 8; ++j) mma(j, pair_rebuild(pw[j], s, st.tab));
   }
 };
 
 template <>
 struct Raw<4> {  // DYADIC5: bf16 scale per 64-group (side) + high-bit words (side2)
+  static constexpr uint32_t kPackedStep = 128;
   static constexpr uint32_t kSideStep = 8;  // 4 groups x 2 bytes per 256-k step
   u32x4 a0, a1;
   uint32_t h0, h1;  // high-bit words of the lane's two runs of 32 weights
@@ -270,6 +286,52 @@ struct Raw<4> {  // DYADIC5: bf16 scale per 64-group (side) + high-bit words (si
   }
 };
 
+template <>
+struct Raw<5> {  // LUT16S_PERM: LUT16S storage decoded by byte-plane v_perm lookups
+  static constexpr uint32_t kPackedStep = 128;
+  static constexpr uint32_t kSideStep = 8;  // 4 groups x 2 bytes per 256-k step
+  u32x4 a0, a1;
+  uint16_t sb;
+  __device__ __forceinline__ void fetch(const Slice& S, const LaneBase& L, uint32_t sp,
+                                        uint32_t ss) {
+    a0 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, L.pa + sp, 0, kPackedPolicy);
+    a1 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, L.pb + sp, 0, kPackedPolicy);
+    sb = __builtin_amdgcn_raw_buffer_load_b16(S.side, L.s + ss, 0, 0);
+  }
+  template <typename F>
+  __device__ __forceinline__ void apply(const Shuffle& sh, const SharedTable& st, F&& mma) const {
+    u32x4 p0, p1;
+    sh(a0, a1, p0, p1);
+    const uint32_t pw[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+    const Lut16Table t = lut16_table(sb, st.l0, st.l1);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mma(j, lut16_rebuild(pw[j], t));
+  }
+};
+
+template <>
+struct Raw<6> {  // LUT16S, scales interleaved into the packed records (side = packed)
+  static constexpr uint32_t kPackedStep = kIlRecord;
+  static constexpr uint32_t kSideStep = kIlRecord;
+  u32x4 a0, a1;
+  uint16_t sb;
+  __device__ __forceinline__ void fetch(const Slice& S, const LaneBase& L, uint32_t sp,
+                                        uint32_t ss) {
+    a0 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, L.pa + sp, 0, kPackedPolicy);
+    a1 = __builtin_amdgcn_raw_buffer_load_b128(S.packed, L.pb + sp, 0, kPackedPolicy);
+    sb = __builtin_amdgcn_raw_buffer_load_b16(S.packed, L.s + ss, 0, 0);
+  }
+  template <typename F>
+  __device__ __forceinline__ void apply(const Shuffle& sh, const SharedTable& st, F&& mma) const {
+    u32x4 p0, p1;
+    sh(a0, a1, p0, p1);
+    const uint32_t pw[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+    const float s = bf16_bits_to_f32(sb);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mma(j, pair_rebuild(pw[j], s, st.tab));
+  }
+};
+
 // k-chunk length staged in LDS for a given m and LDS capacity (16-byte units):
 // rows of kc/8 units plus one pad unit each.
 __host__ __device__ __forceinline__ int64_t gemv_chunk(int m, int xs_units, int64_t K) {
@@ -303,6 +365,8 @@ __global__ __launch_bounds__(64 * (KSPLIT > 4 ? KSPLIT : 4)) void gemv_kernel(
   constexpr int NT = 64 * WAVES;      // threads per block
   constexpr int RW = WAVES / KSPLIT;  // row tiles per block
   static_assert(!BATCHED || WAVES == 4, "the batched launch uses 4-wave blocks");
+  // the pair decode yields weights in natural k order, so x is staged as is
+  constexpr bool kNaturalX = CODEC == 3 || CODEC == 6;
   extern __shared__ u32x4 xs[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
@@ -357,10 +421,17 @@ __global__ __launch_bounds__(64 * (KSPLIT > 4 ? KSPLIT : 4)) void gemv_kernel(
   }
 
   Slice S;
-  const uint32_t row_bytes = (uint32_t)(K >> 1);
+  constexpr bool kIL = CODEC == 6;
+  // packed bytes of a row, and the packed offset of weight k0 (a multiple of 256)
+  const uint32_t row_bytes = kIL ? (uint32_t)(K >> 8) * kIlRecord : (uint32_t)(K >> 1);
+  auto pk_off = [&](int64_t kk) -> uint32_t {
+    return kIL ? (uint32_t)(kk >> 8) * kIlRecord : (uint32_t)(kk >> 1);
+  };
   const uint32_t g64 = (uint32_t)(K >> 6);  // 64-groups per row
-  S.packed = rsrc(P.packed + row0 * (K >> 1), (uint32_t)rows_here * row_bytes);
-  if constexpr (CODEC == 0 || CODEC == 3) {
+  S.packed = rsrc(P.packed + (int64_t)row0 * row_bytes, (uint32_t)rows_here * row_bytes);
+  if constexpr (kIL) {
+    S.side = S.packed;
+  } else if constexpr (CODEC == 0 || CODEC == 3 || CODEC == 5) {
     S.side = rsrc(P.scales + row0 * (K >> 6), (uint32_t)rows_here * g64 * 2);
   } else if constexpr (CODEC == 4) {
     S.side = rsrc(P.scales + row0 * (K >> 6), (uint32_t)rows_here * g64 * 2);
@@ -376,9 +447,17 @@ __global__ __launch_bounds__(64 * (KSPLIT > 4 ? KSPLIT : 4)) void gemv_kernel(
 
   const int64_t kc = gemv_chunk(m, xs_units, kend - kbeg);
   SharedTable st{};
-  if constexpr (CODEC == 3) {
+  if constexpr (CODEC == 5) {
     st.l0 = reinterpret_cast<const u32x4*>(P.codebook)[0];
     st.l1 = reinterpret_cast<const u32x4*>(P.codebook)[1];
+  }
+  if constexpr (CODEC == 3 || CODEC == 6) {
+    // the pair table after the shuffle areas; written here, read after the
+    // staging barrier of the first k-chunk
+    f32x2* tab = reinterpret_cast<f32x2*>(xs + xs_units + 128 * WAVES);
+    for (int t = tid; t < 256; t += NT)
+      tab[t] = (f32x2){bf16_bits_to_f32(P.codebook[t & 15]), bf16_bits_to_f32(P.codebook[t >> 4])};
+    st.tab = tab;
   }
   const int row_units = (int)(kc / 8) + 1;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -394,9 +473,10 @@ __global__ __launch_bounds__(64 * (KSPLIT > 4 ? KSPLIT : 4)) void gemv_kernel(
     LaneBase L;
     {
       const uint32_t g0 = rloc * g64 + (uint32_t)((k0 >> 6) + q);  // lane's first 64-group
-      L.pa = rowA * row_bytes + (uint32_t)(k0 >> 1) + chA;
-      L.pb = (rowA + 8) * row_bytes + (uint32_t)(k0 >> 1) + chB;
-      L.s = (CODEC == 0 || CODEC == 3 || CODEC == 4) ? g0 * 2 : g0 * 32;
+      L.pa = rowA * row_bytes + pk_off(k0) + chA;
+      L.pb = (rowA + 8) * row_bytes + pk_off(k0) + chB;
+      L.s = kIL ? rloc * row_bytes + pk_off(k0) + 128u + 2u * (uint32_t)q
+            : (CODEC == 0 || CODEC == 3 || CODEC == 4 || CODEC == 5) ? g0 * 2 : g0 * 32;
       L.s2 = CODEC == 4 ? rloc * (uint32_t)(K >> 3) + (uint32_t)(k0 >> 3) + 8u * (uint32_t)q
                         : g0 * 2;
     }
@@ -422,9 +502,11 @@ __global__ __launch_bounds__(64 * (KSPLIT > 4 ? KSPLIT : 4)) void gemv_kernel(
         M.pb = opaque(kst < limB ? L.pb : kOOBLane);
         M.s = opaque(kst < limS ? L.s : kOOBLane);
         M.s2 = opaque(kst < limS ? L.s2 : kOOBLane);
-        r.fetch(S, M, in ? st * 128u : kOOB, in ? st * Raw<CODEC>::kSideStep : kOOB);
+        r.fetch(S, M, in ? st * Raw<CODEC>::kPackedStep : kOOB,
+                in ? st * Raw<CODEC>::kSideStep : kOOB);
       } else {
-        r.fetch(S, L, in ? st * 128u : kOOB, in ? st * Raw<CODEC>::kSideStep : kOOB);
+        r.fetch(S, L, in ? st * Raw<CODEC>::kPackedStep : kOOB,
+                in ? st * Raw<CODEC>::kSideStep : kOOB);
       }
     };
     // x staging slots: (row mrow, pass ip) -> unit tid + NT ip of that row
@@ -456,7 +538,8 @@ __global__ __launch_bounds__(64 * (KSPLIT > 4 ? KSPLIT : 4)) void gemv_kernel(
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < kXFirst; ++i)
-      if (i < nslots && xu[i] < units) xs[xrow[i] * row_units + xu[i]] = x_to_sigma(xv[i]);
+      if (i < nslots && xu[i] < units)
+        xs[xrow[i] * row_units + xu[i]] = kNaturalX ? xv[i] : x_to_sigma(xv[i]);
     // the rest XG slots at a time, so their loads overlap
     for (int slot = kXFirst; slot < nslots; slot += XG) {
       u32x4 v[XG];
@@ -468,7 +551,8 @@ __global__ __launch_bounds__(64 * (KSPLIT > 4 ? KSPLIT : 4)) void gemv_kernel(
       }
 #pragma unroll
       for (int j = 0; j < XG; ++j)
-        if (slot + j < nslots && uu[j] < units) xs[mrow[j] * row_units + uu[j]] = x_to_sigma(v[j]);
+        if (slot + j < nslots && uu[j] < units)
+          xs[mrow[j] * row_units + uu[j]] = kNaturalX ? v[j] : x_to_sigma(v[j]);
     }
     lds_barrier();
 
@@ -569,10 +653,13 @@ __global__ __launch_bounds__(256) void zero_kernel(void* y, int64_t count, int y
 // LDS units for a launch whose blocks each cover `kspan` of k: the whole
 // padded span if it fits, else the cap; never less than the 1 KiB per wave
 // the in-block k-split reduction needs.
-int xs_units_for(int m, int64_t kspan, int waves = 4) {
+// extra: LDS units the codec keeps after the shuffle areas (the pair table).
+constexpr int extra_units(int codec) { return codec == 3 || codec == 6 ? 128 : 0; }
+
+int xs_units_for(int m, int64_t kspan, int waves = 4, int extra = 0) {
   const int64_t kpad = (kspan + 255) & ~(int64_t)255;
   int64_t u = (int64_t)m * (kpad / 8 + 1);
-  const int64_t cap = kLdsBlockUnits - 128 * waves;
+  const int64_t cap = kLdsBlockUnits - 128 * waves - extra;
   if (u > cap) u = cap;
   if (u < 64 * waves) u = 64 * waves;
   return (int)u;
@@ -637,10 +724,11 @@ hipError_t launch_one(const GemvProblem& p, int m, int y_bf16, const GemvShape& 
     if (e != hipSuccess) return e;
     sl.part = reinterpret_cast<float*>(ws);
   }
-  const int xu = xs_units_for(m, (int64_t)sh.slice_steps * 256, WAVES);
+  constexpr int EX = extra_units(CODEC);
+  const int xu = xs_units_for(m, (int64_t)sh.slice_steps * 256, WAVES, EX);
   gemv_kernel<CODEC, KSPLIT, false, 4, RAGGED>
-      <<<dim3((uint32_t)blocks, (uint32_t)sh.kslices), dim3(64 * WAVES), (xu + 128 * WAVES) * 16,
-         stream>>>(p, nullptr, 0, m, y_bf16, xu, sl);
+      <<<dim3((uint32_t)blocks, (uint32_t)sh.kslices), dim3(64 * WAVES),
+         (xu + 128 * WAVES + EX) * 16, stream>>>(p, nullptr, 0, m, y_bf16, xu, sl);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || sh.kslices == 1) return e;
   const int64_t total = (int64_t)m * p.n;
@@ -685,6 +773,8 @@ hipError_t launch_gemv(int codec, const GemvProblem& p, int m, int y_bf16, hipSt
   if (codec == 1) return launch_codec<1>(p, m, y_bf16, stream);
   if (codec == 3) return launch_codec<3>(p, m, y_bf16, stream);
   if (codec == 4) return launch_codec<4>(p, m, y_bf16, stream);
+  if (codec == 5) return launch_codec<5>(p, m, y_bf16, stream);
+  if (codec == 6) return launch_codec<6>(p, m, y_bf16, stream);
   return launch_codec<2>(p, m, y_bf16, stream);
 }
 
@@ -692,7 +782,8 @@ template <int CODEC, bool RAGGED>
 hipError_t launch_batched_codec(const GemvProblem* probs_dev, int count, int64_t total_tiles,
                                 int xu, int tile_rows, int m, int y_bf16, hipStream_t stream) {
   const dim3 block(256), grid((uint32_t)total_tiles);
-  const size_t lds = (size_t)(xu + 512) * 16;  // activations + 4 x 2 KiB shuffle areas
+  // activations + 4 x 2 KiB shuffle areas (+ the pair table)
+  const size_t lds = (size_t)(xu + 512 + extra_units(CODEC)) * 16;
   const GemvProblem none{};
   const Slicing whole{1, 0, nullptr};
   // m == 1: tiles of 64 / 32 / 16 rows = 4 / 2 / 1 row tiles of 16 per block,
@@ -725,8 +816,10 @@ hipError_t launch_batched_any(const GemvProblem* probs_dev, int count, int64_t t
 hipError_t launch_gemv_batched(int codec, const GemvProblem* probs_dev, int count,
                                int64_t total_tiles, int64_t k_max, int tile_rows, int m,
                                int y_bf16, bool ragged, hipStream_t stream) {
-  const int xu = xs_units_for(m, k_max);
+  const int xu = xs_units_for(m, k_max, 4, extra_units(codec));
   switch (codec) {
+    case 5: return launch_batched_any<5>(probs_dev, count, total_tiles, xu, tile_rows, m, y_bf16, ragged, stream);
+    case 6: return launch_batched_any<6>(probs_dev, count, total_tiles, xu, tile_rows, m, y_bf16, ragged, stream);
     case 0: return launch_batched_any<0>(probs_dev, count, total_tiles, xu, tile_rows, m, y_bf16, ragged, stream);
     case 1: return launch_batched_any<1>(probs_dev, count, total_tiles, xu, tile_rows, m, y_bf16, ragged, stream);
     case 3: return launch_batched_any<3>(probs_dev, count, total_tiles, xu, tile_rows, m, y_bf16, ragged, stream);

@@ -27,6 +27,10 @@ hipError_t launch_quantize_dyadic5(int64_t n, int64_t k, const uint16_t* w, cons
                                    uint8_t* packed, uint8_t* msb, uint16_t* scales,
                                    hipStream_t stream);
 
+// W4_LUT16S_IL records (k a multiple of 256) from planar LUT16S arrays
+hipError_t launch_lut16s_interleave(int64_t n, int64_t k, const uint8_t* packed,
+                                    const uint16_t* scales, uint8_t* out, hipStream_t stream);
+
 hipError_t launch_dequant(int codec, int64_t n, int64_t k, const uint8_t* packed,
                           const uint16_t* scales, const uint16_t* codebook, void* out,
                           hipStream_t stream);

@@ -297,7 +297,37 @@ __global__ __launch_bounds__(256) void quantize_dyadic5_kernel(const u32x4* __re
   }
 }
 
+// W4_LUT16S_IL records from the planar LUT16S arrays: per row and 256-k
+// block, chunks 0-7 are the block's 128 packed bytes and chunk 8 holds its
+// four bf16 scales followed by 8 zero bytes.  One thread per 16-byte chunk.
+__global__ __launch_bounds__(256) void lut16s_interleave_kernel(const u32x4* __restrict__ packed,
+                                                                const uint16_t* __restrict__ scales,
+                                                                u32x4* __restrict__ out,
+                                                                int64_t nchunks) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= nchunks) return;
+  const int64_t rb = t / 9, c = t % 9;  // record (row-major over rows and 256-k blocks), chunk
+  u32x4 v;
+  if (c < 8) {
+    v = packed[rb * 8 + c];
+  } else {
+    const uint16_t* sc = scales + rb * 4;
+    v = (u32x4){(uint32_t)sc[0] | ((uint32_t)sc[1] << 16), (uint32_t)sc[2] | ((uint32_t)sc[3] << 16),
+                0u, 0u};
+  }
+  out[t] = v;
+}
+
 }  // namespace
+
+hipError_t launch_lut16s_interleave(int64_t n, int64_t k, const uint8_t* packed,
+                                    const uint16_t* scales, uint8_t* out, hipStream_t stream) {
+  const int64_t nchunks = n * (k / 256) * 9;
+  const int64_t blocks = (nchunks + 255) / 256;
+  lut16s_interleave_kernel<<<dim3((uint32_t)blocks), dim3(256), 0, stream>>>(
+      reinterpret_cast<const u32x4*>(packed), scales, reinterpret_cast<u32x4*>(out), nchunks);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize_dyadic5(int64_t n, int64_t k, const uint16_t* w, const uint8_t* widths,
                                    uint8_t* packed, uint8_t* msb, uint16_t* scales,

@@ -12,9 +12,12 @@ bf16 scales + x + fp32 y) / step time, in GB/s.
 Also measured in the same run and reported under "rows": the same pass as
 168 separate w4_gemv calls, quantize_pack and unpack_dequant, the prefill GEMM
 (M = 256, K = N = 8192, in TFLOP/s) with quantize_pack of its 8192^2 weight,
-and the other workloads' rows.  "context" holds what HBM delivers on the box
-in the same run: a plain streaming read of 4 GiB with 16-byte loads (the read
-ceiling the GEMV is set against) and a 1 GiB device copy.  The CPU baseline
+and the other workloads' rows.  "context" holds what the box delivers in the
+same run: a plain streaming read of 4 GiB with 16-byte loads (the read
+ceiling the GEMV is set against), the end-to-end time of one such read over
+2.25 MiB (the floor under a single small call), a 1 GiB device copy, and the
+vendor library's dense bf16 GEMM (torch linear on an unquantized weight) at
+the prefill GEMM's shape.  The CPU baseline
 times the C oracle (OpenMP on the host's cores) on the whole decode stack,
 with further rows for the other workloads, each with its GPU:CPU ratio.
 
@@ -84,6 +87,22 @@ def stored_traffic(name, launches_bytes):
     return rec.get("bytes_per_launch")
 
 
+def timed_rotating(fns, stream, steps, warmup):
+    """ms per call of calls taken round robin from fns."""
+    import torch
+    for i in range(warmup):
+        fns[i % len(fns)]()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        fns[i % len(fns)]()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def timed(fn, stream, steps, warmup):
     import torch
     for _ in range(warmup):
@@ -102,7 +121,8 @@ def timed(fn, stream, steps, warmup):
 def read_ceiling(torch, dev, stream):
     """GB/s of a plain streaming read of 4 GiB with 16-byte nontemporal loads
     (libw4ctx.so), best of a few grid sizes: the read rate HBM delivers to a
-    read-only kernel on this machine."""
+    read-only kernel on this machine; and ms per call of the same kernel over
+    2.25 MiB, back to back."""
     import ctypes
     lib = ctypes.CDLL(os.path.join(ROOT, "weight_only_bit_unpack_amd", "libw4ctx.so"))
     lib.w4ctx_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
@@ -120,9 +140,20 @@ def read_ceiling(torch, dev, stream):
             assert rc == 0, rc
         ms = timed(run, stream, 20, 3)
         best = max(best, nbytes / (ms * 1e-3) / 1e9)
-    del buf, sink
+    # one call of the same kernel over 2.25 MiB (the 2048^2 weight's size):
+    # the time a launch of a small streaming kernel takes end to end
+    small = 9 << 18
+    buf2 = torch.full((small // 4,), 0x01010101, dtype=torch.int32, device=dev)
+
+    def run_small():
+        rc = lib.w4ctx_read_stream(ctypes.c_void_p(buf2.data_ptr()), small,
+                                   ctypes.c_void_p(sink.data_ptr()), 1024,
+                                   ctypes.c_void_p(stream.cuda_stream))
+        assert rc == 0, rc
+    ms_small = timed(run_small, stream, 200, 20)
+    del buf, buf2, sink
     torch.cuda.empty_cache()
-    return best
+    return best, ms_small
 
 
 def time_gemm(w4, synthetic, torch, dev, stream, args):
@@ -170,7 +201,16 @@ def other_configs(w4, synthetic, torch, dev, stream, args):
                args.steps, args.warmup)
     b = 2048 * 1024 + 2 * 2048 * 32 + 2 * 2048 + 4 * 2048
     rows["gemv_m1_2048x2048_single_call"] = {"ms": ms, "GB/s": b / (ms * 1e-3) / 1e9}
-    del W, P, S
+    # the same call rotating over 256 copies of the weight (about 600 MB, more
+    # than the 256 MB Infinity Cache holds), so each call reads its weight
+    # from HBM rather than from a cache that the previous call warmed
+    pool = [(P.clone(), S.clone()) for _ in range(256)]
+    calls = [lambda p=p, s=s: w4.w4_gemv(p, x, w4.W4_DYADIC, scales=s, y=y, stream=stream)
+             for p, s in pool]
+    ms = timed_rotating(calls, stream, max(args.steps, 256), min(args.warmup, 256))
+    rows["gemv_m1_2048x2048_rotating_256"] = {"ms": ms, "GB/s": b / (ms * 1e-3) / 1e9,
+                                              "copies": len(pool)}
+    del W, P, S, pool, calls
 
     # LUT16 on the 3.9B-sized shapes: k-means fit on the GPU, then GEMV at m = 1, 4, 16
     log("LUT16 3.9B-sized fit + GEMVs")
@@ -445,9 +485,10 @@ def main():
     gbs = gemv_bytes / (ms * 1e-3) / 1e9
     rows = {}
     log("HBM read ceiling (4 GiB streaming read)")
-    ceiling = read_ceiling(torch, dev, stream)
+    ceiling, ms_small = read_ceiling(torch, dev, stream)
     context = {"read_ceiling_4gib_GB/s": round(ceiling, 1),
-               "value_frac_of_read_ceiling": round(gbs / ceiling, 4)}
+               "value_frac_of_read_ceiling": round(gbs / ceiling, 4),
+               "read_2.25mib_single_call_us": round(ms_small * 1e3, 2)}
     traffic = stored_traffic("gemv_batched_dyadic_m1_llama1b_stack", gemv_bytes)
 
     if args.only is None:
@@ -511,6 +552,11 @@ def main():
                                          "frac_of_bf16_peak": tf / BF16_MFMA_PEAK_TFLOPS}
         W = synthetic.normal_bf16_device((8192, 8192), 0.02, synthetic.seed(5, 0, 0), dev)
         X = synthetic.normal_bf16_device((256, 8192), 1.0, synthetic.seed(5, 0, 1), dev)
+        # context: the vendor library's dense bf16 GEMM (torch linear) on the
+        # same shape with an unquantized bf16 weight
+        ms_d = timed(lambda: torch.nn.functional.linear(X, W), stream, 100, 10)
+        context["dense_bf16_linear_m256_k8192_n8192_TFLOP/s"] = round(
+            2 * 256 * 8192 * 8192 / (ms_d * 1e-3) / 1e12, 1)
         P, S = w4.w4_quantize_pack(W, w4.W4_DYADIC)
         Y = torch.empty((256, 8192), dtype=torch.float32, device=dev)
         ms_q5 = timed(lambda: w4.w4_quantize_pack(W, w4.W4_DYADIC, packed=P, scales=S,

@@ -181,7 +181,7 @@ def test_fullsize_lut16s_batched():
     weight): group scales = absmax (oracle, whole matrix), the table from the
     oracle's whole-weight k-means over the first 512 rows of each matrix;
     quantize + dequant bit-exact and one batched m = 1 GEMV over all three on
-    sampled rows."""
+    sampled rows, for each of the codec's three decodes."""
     import weight_only_bit_unpack_amd as w4
     report("fullsize_lut16s")
     probs, checks = [], []
@@ -212,6 +212,19 @@ def test_fullsize_lut16s_batched():
     torch.cuda.synchronize()
     for pr, (rows, w_hat) in zip(probs, checks):
         _check_outputs(pr["y"], rows, host_bits(pr["x"]), w_hat)
+    # the two other decodes of the same weights, as bench.py times them: the
+    # per-nibble v_perm lookups (W4_LUT16S_PERM) on the planar arrays, and the
+    # interleaved layout (W4_LUT16S_IL)
+    perm = [dict(pr, y=torch.full_like(pr["y"], float("nan"))) for pr in probs]
+    il = [dict(packed=w4.w4_lut16s_interleave(pr["packed"], pr["scales"]),
+               codebook=pr["codebook"], x=pr["x"], y=torch.full_like(pr["y"], float("nan")))
+          for pr in probs]
+    w4.w4_gemv_batched_plan(perm, w4.W4_LUT16S_PERM)()
+    w4.w4_gemv_batched_plan(il, w4.W4_LUT16S_IL)()
+    torch.cuda.synchronize()
+    for variant in (perm, il):
+        for pr, (rows, w_hat) in zip(variant, checks):
+            _check_outputs(pr["y"], rows, host_bits(pr["x"]), w_hat)
 
 
 # ------------------------------------------------------------ 2B SIGNMAG8, warm start

@@ -862,6 +862,39 @@ def test_matmul_k_zero_writes_zeros(w4, m):
             assert np.all(raw == 0)   # +0 bit patterns
 
 
+@pytest.mark.parametrize("codec", [0, 3, 5])
+@pytest.mark.parametrize("m", [1, 3])
+def test_gemv_batched_k_zero_problem(w4, codec, m):
+    """A batch holding a k = 0 problem among ordinary ones, planned and
+    launched through the C ABI with null side tables and a null x for the
+    empty problem (the ABI asks for none at k = 0): its y is +0, the other
+    problem's y matches the oracle.  Covers the LUT16S table set-up of the
+    pair-table (3) and v_perm (5) decodes, which must not read a table there."""
+    import ctypes
+    report("gemv_batched_k0", codec=codec, m=m)
+    n, k, n0 = 200, 512, 70
+    p, side, w_hat = _random_codec_case(3 if codec == 5 else codec, n, k, 3700 + codec)
+    x = dev_bf16(synthetic.normal_bf16((m, k), 1.0, 3701))
+    y = torch.full((m, n), float("nan"), device="cuda")
+    y0 = torch.full((m, n0), float("nan"), device="cuda")
+    pk = dev_u8(p)
+    arr = (w4.W4Problem * 2)()
+    ptr = lambda t: t.data_ptr() if t is not None else None
+    arr[0] = w4.W4Problem(pk.data_ptr(), ptr(side.get("scales")), ptr(side.get("codebook")),
+                          x.data_ptr(), y.data_ptr(), n, k, 0)
+    arr[1] = w4.W4Problem(pk.data_ptr(), None, None, None, y0.data_ptr(), n0, 0, 0)
+    info = w4.W4BatchInfo()
+    assert w4._lib.w4_gemv_batched_plan(codec, m, w4.W4_F32, arr, 2, ctypes.byref(info)) == 0
+    table = torch.frombuffer(bytearray(bytes(arr)), dtype=torch.uint8).to("cuda")
+    stream = torch.cuda.current_stream()
+    assert w4._lib.w4_gemv_batched(codec, m, w4.W4_F32, ctypes.c_void_p(table.data_ptr()),
+                                   ctypes.byref(info), ctypes.c_void_p(stream.cuda_stream)) == 0
+    torch.cuda.synchronize()
+    assert np.all(y0.view(torch.int32).cpu().numpy() == 0)
+    y_ref, bound = matmul.gemm_ref(host_bits(x), w_hat)
+    assert matmul.within_tolerance(host_f32(y), y_ref, bound).all()
+
+
 def test_signmag8_k_multiple_of_32_only(w4):
     """SIGNMAG8 quantize and dequant take k a multiple of the group of 32
     (here k = 96, an odd number of groups per row); the matrix calls still

@@ -446,17 +446,21 @@ __global__ __launch_bounds__(64 * (KSPLIT > 4 ? KSPLIT : 4)) void gemv_kernel(
   S.x = rsrc(P.x, (uint32_t)(m * K * 2));
 
   const int64_t kc = gemv_chunk(m, xs_units, kend - kbeg);
+  // (a problem with k = 0 of a batch may pass no table: nothing reads it then)
   SharedTable st{};
   if constexpr (CODEC == 5) {
-    st.l0 = reinterpret_cast<const u32x4*>(P.codebook)[0];
-    st.l1 = reinterpret_cast<const u32x4*>(P.codebook)[1];
+    if (K > 0) {
+      st.l0 = reinterpret_cast<const u32x4*>(P.codebook)[0];
+      st.l1 = reinterpret_cast<const u32x4*>(P.codebook)[1];
+    }
   }
   if constexpr (CODEC == 3 || CODEC == 6) {
     // the pair table after the shuffle areas; written here, read after the
     // staging barrier of the first k-chunk
     f32x2* tab = reinterpret_cast<f32x2*>(xs + xs_units + 128 * WAVES);
-    for (int t = tid; t < 256; t += NT)
-      tab[t] = (f32x2){bf16_bits_to_f32(P.codebook[t & 15]), bf16_bits_to_f32(P.codebook[t >> 4])};
+    if (K > 0)
+      for (int t = tid; t < 256; t += NT)
+        tab[t] = (f32x2){bf16_bits_to_f32(P.codebook[t & 15]), bf16_bits_to_f32(P.codebook[t >> 4])};
     st.tab = tab;
   }
   const int row_units = (int)(kc / 8) + 1;

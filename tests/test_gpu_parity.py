@@ -702,6 +702,32 @@ def test_gemv_batched_codecs(w4, codec, m, shapes):
             _gemv_check(pr["y"], x, w_hat, False)
 
 
+# bf16 outputs of the batched launch: the m = 1 kernels at each tile height
+# (64 rows for the first case, 16 for the small ones) and the m > 1 kernel
+@pytest.mark.parametrize("codec,m,shapes", [
+    (0, 1, [(2048, 2048), (5632, 2048), (70000, 256)]),
+    (0, 1, [(300, 1024), (70, 832)]),
+    (0, 5, [(300, 1024), (70, 832)]),
+    (2, 1, [(300, 1024), (65, 2048)]),
+    (3, 1, [(300, 1024), (129, 2048)]),
+    (4, 2, [(300, 1024), (129, 2048)]),
+])
+def test_gemv_batched_bf16_output(w4, codec, m, shapes):
+    report("gemv_batched_bf16", codec=codec, m=m, count=len(shapes))
+    probs, refs = [], []
+    for i, (n, k) in enumerate(shapes):
+        p, side, w_hat = _batched_case(codec, n, k, 4200 + 10 * codec + i)
+        x = synthetic.normal_bf16((m, k), 1.0, 4300 + 10 * codec + i)
+        y = torch.full((m, n), float("nan"), dtype=torch.bfloat16, device="cuda")
+        probs.append(dict(packed=dev_u8(p), x=dev_bf16(x), y=y, **side))
+        refs.append((x, w_hat))
+    batch = w4.w4_gemv_batched_plan(probs, codec, y_dtype=torch.bfloat16)
+    batch()
+    torch.cuda.synchronize()
+    for pr, (x, w_hat) in zip(probs, refs):
+        _gemv_check(pr["y"], x, w_hat, True)
+
+
 @pytest.mark.parametrize("m", [1, 4])
 def test_gemv_batched_many_problems(w4, m):
     """More problems than a block's 256 threads look up in one round (the

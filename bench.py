@@ -362,6 +362,14 @@ def main():
         PL, _ = w4.w4_quantize_pack(W, w4.W4_LUT16, scales=sl, codebook=L)
         cb = w4.w4_signmag8_fit(W, 1)
         P8, _ = w4.w4_quantize_pack(W, w4.W4_SIGNMAG8, codebook=cb)
+        # quantize against the fitted tables / magnitudes (exact nearest level)
+        for name, fn in (("quantize_lut16", lambda: w4.w4_quantize_pack(
+                              W, w4.W4_LUT16, scales=sl, codebook=L, packed=PL, stream=stream)),
+                         ("quantize_signmag8", lambda: w4.w4_quantize_pack(
+                              W, w4.W4_SIGNMAG8, codebook=cb, packed=P8, stream=stream))):
+            ms = timed(fn, stream, args.steps, args.warmup)
+            print(json.dumps({"target": name, "ms": ms, "GB/s": (2 * n * k + n * k // 2) /
+                              (ms * 1e-3) / 1e9}), flush=True)
         wd = torch.full((n, k // 64), 4, dtype=torch.uint8, device=dev)
         P5, M5, S5 = w4.w4_quantize_dyadic5(W, wd)
         out = torch.empty((n, k), dtype=torch.bfloat16, device=dev)

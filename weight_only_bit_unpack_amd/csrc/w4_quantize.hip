@@ -157,26 +157,61 @@ __device__ __forceinline__ uint32_t nearest_settle(double x, const double (&v)[N
   return bi;
 }
 
+// Levels in strictly increasing order whose midpoints (v_t + v_t+1) / 2 are
+// exact in double (the sum's two-sum error is zero, which also rules out an
+// infinite level): the lowest nearest level of x is then the number of
+// midpoints strictly below x, since x lies nearer v_t+1 than v_t exactly
+// when x > m_t, and x = m_t, a tie, keeps the lower index.  Fitted tables
+// and magnitudes are sorted and distinct; any other table takes the scan.
+template <int NL>
+__device__ __forceinline__ bool exact_midpoints(const double (&v)[NL], double (&mid)[NL - 1]) {
+  bool ok = true;
+#pragma unroll
+  for (int t = 0; t < NL - 1; ++t) {
+    const double a = v[t], b = v[t + 1];
+    const double sum = a + b;
+    const double bp = sum - a;
+    const double ap = sum - bp;
+    const double e = (a - ap) + (b - bp);
+    ok = ok && a < b && e == 0.0;
+    mid[t] = sum * 0.5;
+  }
+  return ok;
+}
+
 // Eight weights against NL levels: the packed word of their indices (plus
-// the sign bits for SIGNMAG8, where x = |w|).  The wave settles ties only if
-// one of its lanes has one.
+// the sign bits for SIGNMAG8, where x = |w|).  Lanes whose levels qualify
+// count midpoints; a wave with any other lane also runs the scan for those,
+// and settles ties only if one of its lanes has one.
 template <int NL, bool SIGNMAG>
-__device__ __forceinline__ uint32_t nearest8(const float (&f)[8], const double (&v)[NL]) {
+__device__ __forceinline__ uint32_t nearest8(const float (&f)[8], const double (&v)[NL],
+                                             const double (&mid)[NL - 1], bool counted) {
   uint32_t idx[8];
-  double dmin[8];
-  bool any_tie = false;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const double x = SIGNMAG ? (double)__builtin_fabsf(f[i]) : (double)f[i];
-    bool t;
-    idx[i] = nearest_scan<NL>(x, v, dmin[i], t);
-    any_tie = any_tie || t;
+    uint32_t n = 0;
+#pragma unroll
+    for (int t = 0; t < NL - 1; ++t) n += x > mid[t] ? 1u : 0u;
+    idx[i] = n;
   }
-  if (__builtin_expect(__any(any_tie), 0)) {
+  if (__builtin_expect(__any(!counted), 0)) {
+    double dmin[8];
+    bool any_tie = false;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const double x = SIGNMAG ? (double)__builtin_fabsf(f[i]) : (double)f[i];
-      if (dmin[i] != __builtin_inf()) idx[i] = nearest_settle<NL>(x, v, dmin[i]);
+      bool t;
+      const uint32_t j = nearest_scan<NL>(x, v, dmin[i], t);
+      if (!counted) idx[i] = j;
+      any_tie = any_tie || (t && !counted);
+    }
+    if (__builtin_expect(__any(any_tie), 0)) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const double x = SIGNMAG ? (double)__builtin_fabsf(f[i]) : (double)f[i];
+        if (!counted && dmin[i] != __builtin_inf()) idx[i] = nearest_settle<NL>(x, v, dmin[i]);
+      }
     }
   }
   uint32_t word = 0;
@@ -189,16 +224,21 @@ __device__ __forceinline__ uint32_t nearest8(const float (&f)[8], const double (
 }
 
 // LUT16 / LUT16S: levels v_j = s * L_j (exact in double); index = the exact
-// nearest level.  shared: one table for every group (LUT16S).
+// nearest level.  shared: one table for every group (LUT16S).  One thread
+// per group of 64: the levels and their midpoints are set up once for the
+// group's eight chunks, whose loads are all issued first (cached loads: the
+// lanes' chunks interleave within lines that the next loads reuse).
 __global__ __launch_bounds__(256) void quantize_lut16_kernel(const u32x4* __restrict__ w,
                                                              uint32_t* __restrict__ packed,
                                                              const uint16_t* __restrict__ scales,
                                                              const u32x4* __restrict__ lut,
-                                                             int64_t nchunks, int shared) {
-  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (c >= nchunks) return;
-  const int64_t g = c >> 3, gt = shared ? 0 : g;
-  const u32x4 v = __builtin_nontemporal_load(&w[c]);
+                                                             int64_t ngroups, int shared) {
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (g >= ngroups) return;
+  const int64_t gt = shared ? 0 : g;
+  u32x4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = w[8 * g + i];
   const double s = (double)bf16_bits_to_f32(scales[g]);
   const u32x4 l0 = lut[2 * gt], l1 = lut[2 * gt + 1];
   const uint32_t lw[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
@@ -208,20 +248,28 @@ __global__ __launch_bounds__(256) void quantize_lut16_kernel(const u32x4* __rest
     lv[2 * i] = (double)bf16_bits_to_f32(lw[i] & 0xFFFFu) * s;
     lv[2 * i + 1] = (double)__builtin_bit_cast(float, lw[i] & 0xFFFF0000u) * s;
   }
-  float f[8];
-  unpack8(v, f);
-  packed[c] = nearest8<16, false>(f, lv);
+  double mid[15];
+  const bool counted = exact_midpoints<16>(lv, mid);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float f[8];
+    unpack8(v[i], f);
+    packed[8 * g + i] = nearest8<16, false>(f, lv, mid, counted);
+  }
 }
 
-// SIGNMAG8: nibble = (w < 0) << 3 | the exact nearest magnitude to |w|.
+// SIGNMAG8: nibble = (w < 0) << 3 | the exact nearest magnitude to |w|.  One
+// thread per group of 32 (four chunks), as for LUT16.
 __global__ __launch_bounds__(256) void quantize_signmag8_kernel(const u32x4* __restrict__ w,
                                                                 uint32_t* __restrict__ packed,
                                                                 const u32x4* __restrict__ cb,
-                                                                int64_t nchunks) {
-  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (c >= nchunks) return;
-  const u32x4 v = __builtin_nontemporal_load(&w[c]);
-  const u32x4 m = cb[c >> 2];  // group of 32 = 4 chunks
+                                                                int64_t ngroups) {
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (g >= ngroups) return;
+  u32x4 v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = w[4 * g + i];
+  const u32x4 m = cb[g];
   const uint32_t mw[4] = {m.x, m.y, m.z, m.w};
   double mv[8];
 #pragma unroll
@@ -230,9 +278,14 @@ __global__ __launch_bounds__(256) void quantize_signmag8_kernel(const u32x4* __r
     mv[2 * i] = (double)(float)h.x;
     mv[2 * i + 1] = (double)(float)h.y;
   }
-  float f[8];
-  unpack8(v, f);
-  packed[c] = nearest8<8, true>(f, mv);
+  double mid[7];
+  const bool counted = exact_midpoints<8>(mv, mid);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float f[8];
+    unpack8(v[i], f);
+    packed[4 * g + i] = nearest8<8, true>(f, mv, mid, counted);
+  }
 }
 
 // Bit of a run's 32-bit high-bit word that holds weight i (0..31) of the run
@@ -349,11 +402,11 @@ hipError_t launch_quantize(int codec, int64_t n, int64_t k, const uint16_t* w, u
   if (codec == 0)
     quantize_dyadic_kernel<<<dim3((uint32_t)blocks), dim3(256), 0, stream>>>(wv, pk, scales, nchunks);
   else if (codec == 1 || codec == 3)
-    quantize_lut16_kernel<<<dim3((uint32_t)blocks), dim3(256), 0, stream>>>(
-        wv, pk, scales, reinterpret_cast<const u32x4*>(codebook), nchunks, codec == 3);
+    quantize_lut16_kernel<<<dim3((uint32_t)((nchunks / 8 + 255) / 256)), dim3(256), 0, stream>>>(
+        wv, pk, scales, reinterpret_cast<const u32x4*>(codebook), nchunks / 8, codec == 3);
   else
-    quantize_signmag8_kernel<<<dim3((uint32_t)blocks), dim3(256), 0, stream>>>(
-        wv, pk, reinterpret_cast<const u32x4*>(codebook), nchunks);
+    quantize_signmag8_kernel<<<dim3((uint32_t)((nchunks / 4 + 255) / 256)), dim3(256), 0, stream>>>(
+        wv, pk, reinterpret_cast<const u32x4*>(codebook), nchunks / 4);
   return hipGetLastError();
 }
 

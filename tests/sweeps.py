@@ -76,6 +76,14 @@ def lut16_cases():
         L[::7, 3:5] = 0x0000      # duplicated levels
         s = np.full((rows, 1), sb, np.uint16)
         yield f"sorted s={sb:#06x}", w, s, np.ascontiguousarray(L.reshape(rows, 1, 16))
+    # the uniform grid (j - 8) / 8: sorted and distinct, with every midpoint
+    # (2j - 15) / 16 itself a bf16 value, so the sweep hits exact ties at all
+    # of them (the lower level must win)
+    grid = bits.rne_bf16((np.arange(16) - 8) / 8.0)
+    for sb in (0x3F80, 0x4300):
+        s = np.full((rows, 1), sb, np.uint16)
+        L = np.ascontiguousarray(np.broadcast_to(grid, (rows, 1, 16)))
+        yield f"grid s={sb:#06x}", w, s, L
     for i, L in enumerate(_adversarial_tables(rows, g)):
         for sb in (0x3F80, 0x0080, 0x7E00):
             s = np.full((rows, 1), sb, np.uint16)
@@ -102,8 +110,11 @@ def signmag8_cases():
     w = all_finite_bf16(64)
     ng = 2 * w.shape[0]  # groups of 32
     g = np.random.default_rng(72)
-    for kind in range(5):
-        if kind == 0:
+    for kind in range(6):
+        if kind == 5:
+            # the grid j / 8: every midpoint (2j + 1) / 16 is a bf16 value
+            mags = np.broadcast_to(np.arange(8) / 8.0, (ng, 8)).copy()
+        elif kind == 0:
             mags = np.sort(g.uniform(0, 0.1, (ng, 8)), axis=-1)
         elif kind == 1:
             mags = np.sort(2.0 ** g.uniform(-26, -10, (ng, 8)), axis=-1)
@@ -116,8 +127,9 @@ def signmag8_cases():
         else:
             mags = np.sort(g.uniform(0, 2, (ng, 8)), axis=-1)
         cb = bits.rne_fp16(mags)
-        cb[::5, 2] = cb[::5, 1]   # a duplicated level
-        cb[::3, 0] = 0
+        if kind != 5:
+            cb[::5, 2] = cb[::5, 1]   # a duplicated level
+            cb[::3, 0] = 0
         if kind == 4:
             cb[:, 6:] = 0x7C00    # +inf magnitudes, as the fit gives beyond fp16
             cb[::4, :] = 0x7C00   # groups whose every magnitude is +inf

@@ -98,10 +98,13 @@ def test_dyadic5_quantize_exhaustive_values(w4):
 
 def test_lut16_quantize_exhaustive_values(w4):
     """LUT16 and LUT16S exact nearest level: every finite bf16 weight against
-    sorted tables, tables with levels far apart in magnitude, symmetric pairs
-    and unsorted entries beyond [-1, 1], under scales from the smallest
-    subnormal to the largest finite bf16 (tests/sweeps.py; the CPU tests pin
-    the C checker to integer brute force on exactly these inputs)."""
+    sorted tables (with and without duplicated levels), the uniform grid
+    whose every midpoint is a bf16 weight (exact ties), tables with levels
+    far apart in magnitude, symmetric pairs and unsorted entries beyond
+    [-1, 1], under scales from the smallest subnormal to the largest finite
+    bf16 (tests/sweeps.py; the CPU tests pin the C checker to integer brute
+    force on exactly these inputs).  Sorted distinct tables take the kernel's
+    midpoint count, the others its distance scan."""
     report("lut16_quantize_exhaustive")
     for name, w, s, L in sweeps.lut16_cases():
         p, _ = w4.w4_quantize_pack(dev_bf16(w), w4.W4_LUT16, scales=dev_bf16(s),
@@ -145,7 +148,8 @@ def test_lut16_dequant_extreme_scales_and_tables(w4):
 def test_signmag8_quantize_exhaustive_values(w4):
     """SIGNMAG8 sign + exact nearest magnitude: every finite bf16 weight
     against codebooks with subnormal, duplicated, zero, unsorted, maximal
-    (65504) and +inf fp16 magnitudes (tests/sweeps.py, pinned on the CPU)."""
+    (65504) and +inf fp16 magnitudes, and the grid j / 8 whose midpoints are
+    bf16 weights (tests/sweeps.py, pinned on the CPU)."""
     report("signmag8_quantize_exhaustive")
     for name, w, cb in sweeps.signmag8_cases():
         p, _ = w4.w4_quantize_pack(dev_bf16(w), w4.W4_SIGNMAG8, codebook=dev_f16(cb))

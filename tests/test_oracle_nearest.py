@@ -17,7 +17,12 @@ from oracle import bits, dyadic, lut16, native, signmag8
 from tests import exact, sweeps
 
 
-@pytest.mark.parametrize("case", range(13))
+N_LUT16 = sum(1 for _ in sweeps.lut16_cases())
+N_LUT16S = sum(1 for _ in sweeps.lut16s_cases())
+N_SIGNMAG8 = sum(1 for _ in sweeps.signmag8_cases())
+
+
+@pytest.mark.parametrize("case", range(N_LUT16))
 def test_lut16_sweep_numpy_and_c_equal_integer_argmin(case):
     name, w, s, L = list(sweeps.lut16_cases())[case]
     want = exact.lut16_exact_indices(w, s, L)
@@ -26,7 +31,7 @@ def test_lut16_sweep_numpy_and_c_equal_integer_argmin(case):
     assert np.array_equal(native.lut16_indices(w, s, L), want), name
 
 
-@pytest.mark.parametrize("case", range(8))
+@pytest.mark.parametrize("case", range(N_LUT16S))
 def test_lut16s_sweep_numpy_and_c_equal_integer_argmin(case):
     name, w, s, T = list(sweeps.lut16s_cases())[case]
     tables = np.ascontiguousarray(np.broadcast_to(T, (w.shape[0], 1, 16)))
@@ -35,7 +40,7 @@ def test_lut16s_sweep_numpy_and_c_equal_integer_argmin(case):
     assert np.array_equal(native.lut16_indices(w, s, tables), want), name
 
 
-@pytest.mark.parametrize("case", range(5))
+@pytest.mark.parametrize("case", range(N_SIGNMAG8))
 def test_signmag8_sweep_numpy_and_c_equal_integer_argmin(case):
     name, w, cb = list(sweeps.signmag8_cases())[case]
     want = exact.signmag8_exact_indices(w, cb)

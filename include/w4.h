@@ -90,12 +90,15 @@ typedef enum {
  * group's width only restricts which codes it may take; see
  * w4_quantize_dyadic5.  Reconstruction RNE_bf16((s/16) * (j5 - 16)). */
 /* [KM] sec. 2.2 decodes by looking up precomputed values of every byte and
- * stores the scales with the indices.  The W4_LUT16S GEMV decodes a packed
- * byte at a time through a 256-entry table of level pairs (L[b & 15],
- * L[b >> 4]) held in LDS.  Two variants are kept for comparison:
- * W4_LUT16S_PERM: the LUT16S storage and results, with a GEMV that looks the
- *   levels up per nibble from byte-plane tables with v_perm, as LUT16 does.
- *   Every other call treats it exactly as W4_LUT16S.
+ * stores the scales with the indices.  The W4_LUT16S batched GEMV on 64-row
+ * tiles decodes a packed byte at a time through a 256-entry table of level
+ * pairs (L[b & 15], L[b >> 4]) that each block builds in LDS; its single
+ * calls and its batches of short tiles decode per nibble as W4_LUT16S_PERM,
+ * measured as fast or faster there.  Results are bit-identical either way.
+ * Two variants are kept for comparison:
+ * W4_LUT16S_PERM: the LUT16S storage and results, with a GEMV that always
+ *   looks the levels up per nibble from byte-plane tables with v_perm, as
+ *   LUT16 does.  Every other call treats it exactly as W4_LUT16S.
  * W4_LUT16S_IL: the LUT16S weight with each row's scales interleaved into its
  *   packed bytes (k a multiple of 256): per 256-k block a 144-byte record of
  *   the block's 128 packed bytes, its four bf16 scales and 8 zero bytes, so

@@ -775,9 +775,11 @@ hipError_t launch_zero(void* y, int64_t count, int y_bf16, hipStream_t stream) {
 hipError_t launch_gemv(int codec, const GemvProblem& p, int m, int y_bf16, hipStream_t stream) {
   if (codec == 0) return launch_codec<0>(p, m, y_bf16, stream);
   if (codec == 1) return launch_codec<1>(p, m, y_bf16, stream);
-  if (codec == 3) return launch_codec<3>(p, m, y_bf16, stream);
+  // LUT16S single calls decode per nibble: measured as fast as the byte ->
+  // pair table or faster on every shape tried (2048^2 to 32768 x 4096, up
+  // to 9% at 11008 x 4096), the table being built again by every block
+  if (codec == 3 || codec == 5) return launch_codec<5>(p, m, y_bf16, stream);
   if (codec == 4) return launch_codec<4>(p, m, y_bf16, stream);
-  if (codec == 5) return launch_codec<5>(p, m, y_bf16, stream);
   if (codec == 6) return launch_codec<6>(p, m, y_bf16, stream);
   return launch_codec<2>(p, m, y_bf16, stream);
 }
@@ -820,6 +822,12 @@ hipError_t launch_batched_any(const GemvProblem* probs_dev, int count, int64_t t
 hipError_t launch_gemv_batched(int codec, const GemvProblem* probs_dev, int count,
                                int64_t total_tiles, int64_t k_max, int tile_rows, int m,
                                int y_bf16, bool ragged, hipStream_t stream) {
+  // LUT16S: the byte -> pair table is built once per block, which pays on
+  // 64-row tiles; the short tiles of a batch of a few large matrices decode
+  // faster through the per-nibble lookups of the same storage (measured on
+  // the three 3.9B-sized matrices: 18.4 against 22.4 us; the 168 decode-stack
+  // matrices keep 64-row tiles, where the pair table is the faster one)
+  if (codec == 3 && tile_rows < 64) codec = 5;
   const int xu = xs_units_for(m, k_max, 4, extra_units(codec));
   switch (codec) {
     case 5: return launch_batched_any<5>(probs_dev, count, total_tiles, xu, tile_rows, m, y_bf16, ragged, stream);

@@ -196,16 +196,18 @@ def _gemv_check(y, x_bits, w_hat, bf16_out):
                              f"got {host_f32(y)[tuple(bad[0])]} want {y_ref[tuple(bad[0])]}")
 
 
-# m > 1 on few row tiles splits k across blocks (k slices, partial sums added
-# in order by a second kernel): (37, 320, 3) has a ragged last slice, (70,
-# 49472, 16) more activations per slice than fit in LDS (chunks inside a
-# slice), (130, 2944, 7) an odd m over uneven slices; (33, 65600, 1) takes k
-# in three chunks inside each block (the last one ragged), (33, 65600, 2) in
-# slices.
+# m > 1 on few row tiles: while the m x k activations fit one block's LDS,
+# 16-row tiles with k split between a block's waves ((37, 320, 3) ragged,
+# (300, 1024, 4 and 16), (130, 2944, 7), (40000, 128, 2)); else k split across
+# blocks (k slices, partial sums added in order by a second kernel): (37,
+# 20800, 3) has a ragged last slice, (70, 49472, 16) more activations per
+# slice than fit in LDS (chunks inside a slice), (64, 4096, 16) even slices,
+# (33, 65600, 2) many.  (33, 65600, 1) takes k in three chunks inside each
+# block (the last one ragged).
 @pytest.mark.parametrize("n,k,m", [(2048, 2048, 1), (37, 320, 1), (37, 320, 3), (300, 1024, 4),
                                    (300, 1024, 16), (64, 4096, 16), (40000, 128, 2),
                                    (70000, 64, 1), (70, 49472, 16), (130, 2944, 7),
-                                   (33, 65600, 1), (33, 65600, 2)])
+                                   (33, 65600, 1), (33, 65600, 2), (37, 20800, 3)])
 @pytest.mark.parametrize("ybf16", [False, True])
 def test_dyadic_gemv(w4, n, k, m, ybf16):
     report("dyadic_gemv", n=n, k=k, m=m, ybf16=ybf16)

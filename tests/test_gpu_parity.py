@@ -688,6 +688,9 @@ def _batched_case(codec, n, k, seed):
     (3, 16, [(300, 1024), (70, 832)]),
     (4, 1, [(2048, 2048), (300, 1024), (70, 832)]),
     (4, 8, [(300, 1024), (129, 2048)]),
+    # m x k activations beyond one block's LDS: staged in k chunks
+    (0, 16, [(300, 5632), (70, 2048), (130, 2880)]),
+    (1, 16, [(200, 5632)]),
 ])
 def test_gemv_batched_codecs(w4, codec, m, shapes):
     report("gemv_batched_codecs", codec=codec, m=m, count=len(shapes))

@@ -23,9 +23,10 @@
 // order (w4_device.h, SIGMA), in k-chunks when m * k does not fit.
 // A block is max(4, KSPLIT) waves = KSPLIT waves along k x (waves / KSPLIT)
 // row tiles of 16.  With KSPLIT > 1 the waves' partial sums are added in LDS
-// in a fixed order.  KSPLIT = 8 and 16 (blocks of 8 and 16 waves, one row
-// tile) serve single m = 1 calls on matrices too short to fill the GPU with
-// 4-wave blocks: the waves of one 16-row tile take every 8th or 16th step.
+// in a fixed order.  KSPLIT = 4, 8 and 16 (one row tile per block of 4, 8 or
+// 16 waves) serve single calls on matrices too short to fill the GPU with
+// 64-row blocks (for m >= 2 when the activations fit the block's LDS): the
+// waves of one 16-row tile take every 4th, 8th or 16th step.
 #include "w4_device.h"
 #include "w4_launch.h"
 

@@ -12,7 +12,9 @@ passes when ``|y - y_ref| <= 1e-3 * B + 1e-6``; a bf16 output adds the one
 rounding of the output, ``2**-8 * |y_ref|``.  Why any fp32 summation order
 passes: a product of a bf16 and a bf16 (or fp16) value is exact in fp32, and
 recursive fp32 summation of K terms errs by at most ``K * 2**-24 * B``, below
-``1e-3 * B`` for K <= 16760.
+``1e-3 * B`` for K <= 16760.  Longer sums stay inside the bound when they are
+added as blocks of products (dot products of 16 or 32 terms, then the block
+sums): about ``(K / 16 + 16) * 2**-24 * B``.
 """
 
 import numpy as np

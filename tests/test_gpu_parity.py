@@ -682,6 +682,11 @@ def _batched_case(codec, n, k, seed):
 @pytest.mark.parametrize("codec,m,shapes", [
     (0, 1, [(2048, 2048), (5632, 2048), (2048, 5632), (100, 1024), (70, 832)]),
     (0, 4, [(1000, 2048), (64, 1024), (333, 832)]),
+    # m >= 5: the deeper activation staging (16 units in flight per thread),
+    # with whole and partial last 256-k steps
+    (0, 5, [(1000, 2048), (333, 832)]),
+    (0, 6, [(130, 2880), (64, 256)]),
+    (2, 12, [(300, 1024), (65, 2048), (77, 832)]),
     (1, 1, [(300, 1024), (129, 2048)]),
     (2, 3, [(300, 1024), (65, 2048)]),
     (3, 1, [(300, 1024), (129, 2048), (64, 64)]),
@@ -1019,7 +1024,7 @@ def test_lut16s_perm_and_interleaved_gemv(w4, m, n, k):
 
 
 @pytest.mark.parametrize("codec", [3, 5, 6])
-@pytest.mark.parametrize("m", [1, 4])
+@pytest.mark.parametrize("m", [1, 4, 9])
 def test_lut16s_variants_batched(w4, codec, m):
     """LUT16S and both variants through the batched launch: problems of
     several shapes (64-row tiles and, for m = 1 over few rows, 32 / 16-row

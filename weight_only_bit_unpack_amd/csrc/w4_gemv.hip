@@ -357,7 +357,11 @@ struct Slicing {
 
 // XG: x units per thread kept in flight together while staging (after the
 // first).  The batched m = 1 decode pass stages at most a few units per thread
-// and runs fastest with the fewest registers, XG = 1; elsewhere XG = 4.
+// and runs fastest with the fewest registers, XG = 1; batched m >= 5 stages
+// m x k activations per 64-row tile, as many bytes as the tile's weights at
+// m = 16, and gains 6-11% from having all of a thread's units in flight at
+// once, XG = 16; elsewhere XG = 4 (single calls' blocks of up to 1024 threads
+// cannot spend the registers of a deeper staging).
 template <int CODEC, int KSPLIT, bool BATCHED, int XG, bool RAGGED>
 __global__ __launch_bounds__(64 * (KSPLIT > 4 ? KSPLIT : 4)) void gemv_kernel(
     GemvProblem single, const GemvProblem* probs, int count, int m, int y_bf16, int xs_units,
@@ -821,8 +825,11 @@ hipError_t launch_batched_codec(const GemvProblem* probs_dev, int count, int64_t
   else if (m == 1)
     gemv_kernel<CODEC, 1, true, 1, RAGGED>
         <<<grid, block, lds, stream>>>(none, probs_dev, count, m, y_bf16, xu, whole);
-  else
+  else if (m <= 4)  // (a deeper staging measured no faster at m <= 4 and slower at m = 2)
     gemv_kernel<CODEC, 1, true, 4, RAGGED>
+        <<<grid, block, lds, stream>>>(none, probs_dev, count, m, y_bf16, xu, whole);
+  else
+    gemv_kernel<CODEC, 1, true, 16, RAGGED>
         <<<grid, block, lds, stream>>>(none, probs_dev, count, m, y_bf16, xu, whole);
   return hipGetLastError();
 }

@@ -12,7 +12,7 @@ bf16 scales + x + fp32 y) / step time, in GB/s.
 Also measured in the same run and reported under "rows": the same pass as
 168 separate w4_gemv calls, quantize_pack and unpack_dequant, the prefill GEMM
 (M = 256, K = N = 8192, in TFLOP/s) with quantize_pack of its 8192^2 weight,
-and the other workloads' rows.  "context" holds what the box delivers in the
+and the other workloads' rows.  "context" holds what this GPU delivers in the
 same run: a plain streaming read of 4 GiB with 16-byte loads (the read
 ceiling the GEMV is set against), the end-to-end time of one such read over
 2.25 MiB (the floor under a single small call), a 1 GiB device copy, and the
@@ -121,7 +121,7 @@ def timed(fn, stream, steps, warmup):
 def read_ceiling(torch, dev, stream):
     """GB/s of a plain streaming read of 4 GiB with 16-byte nontemporal loads
     (libw4ctx.so), best of a few grid sizes: the read rate HBM delivers to a
-    read-only kernel on this machine; and ms per call of the same kernel over
+    read-only kernel on this GPU; and ms per call of the same kernel over
     2.25 MiB, back to back."""
     import ctypes
     lib = ctypes.CDLL(os.path.join(ROOT, "weight_only_bit_unpack_amd", "libw4ctx.so"))

@@ -1,7 +1,7 @@
 // Measurement context for the benchmark, not part of the W4 library: a plain
 // streaming read of a device buffer with 16-byte nontemporal loads, the same
 // load width and cache policy the GEMV uses for its packed weights.  Its rate
-// is what HBM delivers to a read-only kernel on the box at hand, beside which
+// is what HBM delivers to a read-only kernel on the GPU at hand, beside which
 // the GEMV's bandwidth is reported.  Built as its own libw4ctx.so.
 #include <hip/hip_runtime.h>
 #include <stdint.h>

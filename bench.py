@@ -12,7 +12,10 @@ bf16 scales + x + fp32 y) / step time, in GB/s.
 Also measured in the same run and reported under "rows": the same pass as
 168 separate w4_gemv calls, quantize_pack and unpack_dequant, the prefill GEMM
 (M = 256, K = N = 8192, in TFLOP/s) with quantize_pack of its 8192^2 weight,
-and the other workloads' rows.  "context" holds what this GPU delivers in the
+and the other workloads' rows.  Single GEMV calls on one weight are also timed
+rotating over copies that together exceed the 256 MB Infinity Cache (rows
+ending in "_rotating"), so that each call reads its weight from HBM.
+"context" holds what this GPU delivers in the
 same run: a plain streaming read of 4 GiB with 16-byte loads (the read
 ceiling the GEMV is set against), the end-to-end time of one such read over
 2.25 MiB (the floor under a single small call), a 1 GiB device copy, and the
@@ -85,6 +88,15 @@ def stored_traffic(name, launches_bytes):
     if rec.get("source_hash") != kernel_source_hash():
         return None
     return rec.get("bytes_per_launch")
+
+
+INFINITY_CACHE_BYTES = 256 << 20  # the MI355X's last-level (MALL) cache
+
+
+def rotation_copies(weight_bytes):
+    """Copies of a weight whose bytes together exceed twice the Infinity
+    Cache, so that rotating over them makes every call read from HBM."""
+    return max(2, -(-2 * INFINITY_CACHE_BYTES // weight_bytes))
 
 
 def timed_rotating(fns, stream, steps, warmup):
@@ -225,14 +237,23 @@ def other_configs(w4, synthetic, torch, dev, stream, args):
                                       "Gweights/s": n * k / (ms * 1e-3) / 1e9}
         P, _ = w4.w4_quantize_pack(W, w4.W4_LUT16, scales=sc, codebook=L)
         del W
+        wb = n * k // 2 + n * (k // 64) * 34
+        pool = [(P.clone(), sc.clone(), L.clone()) for _ in range(rotation_copies(wb))]
         for m in (1, 4, 16):
             x = synthetic.normal_bf16_device((m, k), 1.0, synthetic.seed(3, i, 1), dev)
             y = torch.empty((m, n), device=dev)
             ms = timed(lambda: w4.w4_gemv(P, x, w4.W4_LUT16, scales=sc, codebook=L, y=y,
                                           stream=stream), stream, args.steps, args.warmup)
-            b = n * k // 2 + n * (k // 64) * 34 + 2 * m * k + 4 * m * n
+            b = wb + 2 * m * k + 4 * m * n
             rows[f"lut16_gemv_m{m}_{n}x{k}"] = {"ms": ms, "GB/s": b / (ms * 1e-3) / 1e9}
-        del P, sc, L
+            # the same call over copies of the weight totalling more than the
+            # Infinity Cache holds, so each call reads its weight from HBM
+            calls = [lambda p=p, s=s, c=c: w4.w4_gemv(p, x, w4.W4_LUT16, scales=s, codebook=c,
+                                                      y=y, stream=stream) for p, s, c in pool]
+            ms = timed_rotating(calls, stream, max(args.steps, 4 * len(pool)), args.warmup)
+            rows[f"lut16_gemv_m{m}_{n}x{k}_rotating"] = {
+                "ms": ms, "GB/s": b / (ms * 1e-3) / 1e9, "copies": len(pool)}
+        del P, sc, L, pool
 
     # LUT16S (one table per matrix, 4.25 bits per weight): the three 3.9B-sized
     # matrices in one batched m = 1 launch
@@ -587,6 +608,15 @@ def main():
                       stream, args.steps, args.warmup)
         vb = 8192 * 4096 + 2 * 8192 * 128 + 2 * 8192 + 4 * 8192
         rows["gemv_m1_8192x8192"] = {"ms": ms_v5, "GB/s": vb / (ms_v5 * 1e-3) / 1e9}
+        # the same call over copies of the weight totalling more than the
+        # Infinity Cache holds, so each call reads its weight from HBM
+        pool = [(P.clone(), S.clone()) for _ in range(rotation_copies(8192 * 4096 + 2 * 8192 * 128))]
+        calls = [lambda p=p, s=s: w4.w4_gemv(p, xv, w4.W4_DYADIC, scales=s, y=yv, stream=stream)
+                 for p, s in pool]
+        ms_r5 = timed_rotating(calls, stream, max(args.steps, 4 * len(pool)), args.warmup)
+        rows["gemv_m1_8192x8192_rotating"] = {"ms": ms_r5, "GB/s": vb / (ms_r5 * 1e-3) / 1e9,
+                                              "copies": len(pool)}
+        del pool, calls
         D = torch.empty((8192, 8192), dtype=torch.bfloat16, device=dev)
         ms_d5 = timed(lambda: w4.w4_unpack_dequant(P, w4.W4_DYADIC, scales=S, out=D,
                                                    stream=stream), stream, 50, 5)

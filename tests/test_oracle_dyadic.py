@@ -211,16 +211,16 @@ def _dequant_int(sbits, idx):
     return out | (0x8000 if (d < 0) != (sbits >= 0x8000) else 0)
 
 
-def test_dequant_exhaustive_positive_scales():
+def test_dequant_exhaustive_all_scales():
+    """Every finite bf16 scale of either sign (a caller may pass its own
+    scales) x every index, numpy and C oracles, against the integer RNE."""
     allb = bits.all_finite_bf16()
-    pos = allb[(allb & 0x8000) == 0]
     idx = np.arange(16, dtype=np.uint8)
     # one "row" per scale: 64 copies of the 16 indices with the scale repeated
-    out = dyadic.dequant_from_indices(np.tile(idx, (len(pos), 4)), pos[:, None])
-    got = out[:, :16]
-    for i, s in enumerate(pos):
-        for j in range(16):
-            assert got[i, j] == _dequant_int(s, j), (hex(s), j)
+    rows = np.tile(idx, (len(allb), 4))
+    want = np.array([[_dequant_int(s, j) for j in range(16)] for s in allb], dtype=np.uint16)
+    assert np.array_equal(dyadic.dequant_from_indices(rows, allb[:, None])[:, :16], want)
+    assert np.array_equal(native.dyadic_dequant(rows, allb[:, None])[:, :16], want)
 
 
 def test_dequant_on_code_grid():

@@ -71,6 +71,57 @@ def test_lut16_dequant_exact_product_rounding():
                 v == 0 and deq[r, c] in (0, 0x8000))
 
 
+def _rne_bf16_product_int(abits, bbits):
+    """Bits of RNE_bf16(a * b) for two finite bf16 numbers, in integer
+    arithmetic (overflow to +-inf, a zero result keeps the product's sign)."""
+    def dec(u):
+        e, m = (u >> 7) & 0xFF, u & 0x7F
+        return (m, -133) if e == 0 else (m + 128, e - 134)   # value = S * 2**a
+    abits, bbits = int(abits), int(bbits)
+    sign = 0x8000 if (abits ^ bbits) & 0x8000 else 0
+    (sa, ea), (sb, eb) = dec(abits), dec(bbits)
+    P, f = sa * sb, ea + eb
+    if P == 0:
+        return sign
+    q = max(P.bit_length() - 1 + f - 7, -133)   # exponent of the result's last bit
+    sh = q - f
+    if sh <= 0:
+        r = P << (-sh)
+    else:
+        r, rem = P >> sh, P & ((1 << sh) - 1)
+        half = 1 << (sh - 1)
+        if rem > half or (rem == half and r & 1):
+            r += 1
+    if r == 256:
+        r, q = 128, q + 1
+    if r < 128:
+        return sign | r                           # subnormal or zero
+    E = q + 134
+    if E >= 255:
+        return sign | 0x7F80
+    return sign | (E << 7) | (r - 128)
+
+
+def test_lut16_dequant_every_level_extreme_scales():
+    """RNE_bf16(s * L) for every finite bf16 level (tables beyond [-1, 1],
+    signed zeros, subnormals) under scales from the smallest subnormal to the
+    largest finite bf16 (both signs), against integer rounding: the products
+    overflow, round to the largest finite value, or underflow.  The scales
+    include every one the GPU's extreme-table dequant test uses."""
+    allb = bits.all_finite_bf16()
+    scales = np.array([0x0001, 0x0080, 0x3F80, 0x7F7F, 0x7F00, 0x4000, 0x00FF, 0x3C23,
+                       0xBF80, 0x8001], np.uint16)
+    n = (len(allb) + 15) // 16
+    levels = np.resize(allb, n * 16).reshape(n, 1, 16)
+    idx = np.tile(np.arange(16, dtype=np.uint8), 4)[None, :].repeat(n, axis=0)
+    for sb in scales:
+        s = np.full((n, 1), sb, np.uint16)
+        want = np.array([[_rne_bf16_product_int(sb, l) for l in row] for row in levels[:, 0]],
+                        np.uint16)
+        got = lut16.dequant_from_indices(idx, s, levels)[:, :16]
+        assert np.array_equal(got, want), hex(sb)
+
+
 # ------------------------------------------------------------------ Lloyd
 def _optimal_kmeans_cost(x, k):
     """Optimal 1D k-means SSE by dynamic programming over the sorted points

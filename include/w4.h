@@ -407,7 +407,8 @@ typedef struct {
   int32_t tile_rows;   /* rows per work tile: 64, or 32 / 16 (m == 1 only)
                           when 64-row tiles would give fewer than 1024 */
   int32_t flags;       /* bit 0: some problem's k is not a multiple of 256
-                          (the kernel then zeroes the lanes past its k);
+                          (the kernel then zeroes the lanes past its k;
+                          W4_LUT16S_IL, whose k must be, gets W4_ESHAPE);
                           written by the plan like the rest of the record */
 } w4_gemv_batch_info;
 

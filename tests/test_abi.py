@@ -212,9 +212,15 @@ def test_signmag8_group_rule(w4):
 
 def test_batched_flags_checked(w4):
     """w4_gemv_batched rejects an info record whose flags hold bits the plan
-    never writes (before any launch)."""
+    never writes, and a ragged plan launched as W4_LUT16S_IL (before any
+    launch)."""
     info = w4.W4BatchInfo(total_tiles=1, k_min=64, k_max=64, count=1, m=1, tile_rows=64, flags=2)
     assert w4._lib.w4_gemv_batched(0, 1, 0, ctypes.c_void_p(16), ctypes.byref(info), None) == 1
+    # a plan with a k that is not a multiple of 256 (bit 0) cannot run as the
+    # interleaved LUT16S layout, whose records are whole 256-k blocks
+    ragged = w4.W4BatchInfo(total_tiles=1, k_min=64, k_max=64, count=1, m=1, tile_rows=64,
+                            flags=1)
+    assert w4._lib.w4_gemv_batched(6, 1, 0, ctypes.c_void_p(16), ctypes.byref(ragged), None) == 2
 
 
 def test_lut16s_variants_rules(w4):

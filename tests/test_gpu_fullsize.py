@@ -298,7 +298,8 @@ def test_fullsize_gemm_8192(w4):
     """M = 256, K = N = 8192, dyadic N(0, 0.02^2) weights: quantize_pack
     bit-exact on every row, GEMM (pack + split-k kernel + reduction, as
     bench.py times it) on 40 sampled weight rows x all 256 batch rows, fp32
-    and bf16 outputs."""
+    and bf16 outputs; and the m = 1 GEMV on the same weight (the single-call
+    launch of 16-row tiles with k split over 8 waves that bench.py times)."""
     n = k = 8192
     m = 256
     report("fullsize_gemm", m=m, n=n, k=k)
@@ -317,3 +318,7 @@ def test_fullsize_gemm_8192(w4):
     torch.cuda.synchronize()
     _check_outputs(y, rows, host_bits(x), w_hat)
     _check_outputs(yb, rows, host_bits(x), w_hat, bf16_out=True)
+    xv = x[:1].contiguous()
+    yv = w4.w4_gemv(p, xv, w4.W4_DYADIC, scales=s)
+    torch.cuda.synchronize()
+    _check_outputs(yv, rows, host_bits(xv), w_hat)

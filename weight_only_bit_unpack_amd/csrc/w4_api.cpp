@@ -324,6 +324,8 @@ w4_status w4_gemv_batched(int32_t codec, int32_t m, int32_t y_dtype,
   if (m < 1) return m < 0 ? W4_EINVAL : W4_ESHAPE;
   if (m > kGemvMaxM) return W4_ESHAPE;
   if (y_dtype != W4_F32 && y_dtype != W4_BF16) return W4_EUNSUPPORTED;
+  // the interleaved layout needs every k a multiple of 256
+  if (codec == W4_LUT16S_IL && (info->flags & 1)) return W4_ESHAPE;
   if (info->count == 0 || info->total_tiles == 0) return W4_OK;
   if (info->tile_rows != 64 && !(m == 1 && (info->tile_rows == 32 || info->tile_rows == 16)))
     return W4_EINVAL;

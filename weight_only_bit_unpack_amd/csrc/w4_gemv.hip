@@ -780,7 +780,9 @@ hipError_t launch_shape(const GemvProblem& p, int m, int y_bf16, const GemvShape
 template <int CODEC>
 hipError_t launch_codec(const GemvProblem& p, int m, int y_bf16, hipStream_t stream) {
   const GemvShape sh = gemv_shape(p.n, p.k, m);
-  if (p.k % 256) return launch_shape<CODEC, true>(p, m, y_bf16, sh, stream);
+  // (the interleaved layout holds whole 256-k records, so its k never is)
+  if constexpr (CODEC != 6)
+    if (p.k % 256) return launch_shape<CODEC, true>(p, m, y_bf16, sh, stream);
   return launch_shape<CODEC, false>(p, m, y_bf16, sh, stream);
 }
 
@@ -837,9 +839,12 @@ hipError_t launch_batched_codec(const GemvProblem* probs_dev, int count, int64_t
 template <int CODEC>
 hipError_t launch_batched_any(const GemvProblem* probs_dev, int count, int64_t total_tiles, int xu,
                               int tile_rows, int m, int y_bf16, bool ragged, hipStream_t stream) {
-  if (ragged)
+  if constexpr (CODEC == 6) {  // whole 256-k records: never ragged (checked by the caller)
+    if (ragged) return hipErrorInvalidValue;
+  } else if (ragged) {
     return launch_batched_codec<CODEC, true>(probs_dev, count, total_tiles, xu, tile_rows, m,
                                              y_bf16, stream);
+  }
   return launch_batched_codec<CODEC, false>(probs_dev, count, total_tiles, xu, tile_rows, m,
                                             y_bf16, stream);
 }

@@ -49,14 +49,16 @@ def parse():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["headline", "gemm", "copy", "fit", "codec", "singles",
-                                       "lut16s"],
+                                       "lut16s", "variants"],
                     default=None,
                     help="run one target only (for profiler runs): the batched decode pass, "
                          "the M=256 GEMM, a 1 GiB device copy that calibrates HBM counters, "
                          "the table / magnitude fits, quantize + dequant of one 8192^2 "
                          "weight for every codec, single m = 1 GEMV calls (DYADIC 8192^2, "
-                         "LUT16 on the 3.9B shapes), or the decode stack as LUT16S in its three "
-                         "decode variants")
+                         "LUT16 on the 3.9B shapes), the decode stack as LUT16S in its three "
+                         "decode variants, or the batched m = 1 passes of the other codecs "
+                         "(DYADIC5 decode stack, 224-matrix SIGNMAG8 stack, the 3.9B-sized "
+                         "matrices as LUT16S in its three decode variants)")
     ap.add_argument("--only-headline", action="store_true", help="same as --only headline")
     a = ap.parse_args()
     if a.only_headline:
@@ -200,6 +202,56 @@ def shared_table_levels(w):
 FIT_STEPS = 5  # timed k-means fits per shape (each takes milliseconds)
 
 
+def lut16s_shapes_problems(w4, synthetic, torch, dev):
+    """The three 3.9B-sized matrices as LUT16S (N(0, 0.015^2) + outliers, a
+    table of 16 quantiles per matrix), one m = 1 problem each; returns the
+    problems and their algorithmic bytes."""
+    probs, total = [], 0
+    for i, (n, k) in enumerate([(4096, 4096), (11008, 4096), (4096, 11008)]):
+        W = synthetic.normal_outliers_bf16_device((n, k), 0.015, 0.001, 0.15,
+                                                  synthetic.seed(6, i, 0), dev)
+        sc, T = shared_table_levels(W)
+        P, _ = w4.w4_quantize_pack(W, w4.W4_LUT16S, scales=sc, codebook=T)
+        del W
+        x = synthetic.normal_bf16_device((1, k), 1.0, synthetic.seed(6, i, 1), dev)
+        probs.append({"packed": P, "scales": sc, "codebook": T, "x": x,
+                      "y": torch.empty((1, n), device=dev)})
+        total += n * k // 2 + n * (k // 64) * 2 + 32 + 2 * k + 4 * n
+    return probs, total
+
+
+def dyadic5_stack_problems(w4, synthetic, torch, dev, gen):
+    """The 1B decode stack as DYADIC5 with widths 3, 4, 5 drawn per group
+    from gen, one m = 1 problem per matrix; problems and algorithmic bytes."""
+    probs, total = [], 0
+    for i, (n, k) in enumerate(synthetic.llama1b_stack_shapes()):
+        W = synthetic.student_t_bf16_device((n, k), 4, 0.02, synthetic.seed(2, i, 0), dev)
+        wd = torch.randint(3, 6, (n, k // 64), dtype=torch.uint8, device=dev, generator=gen)
+        P, M, S = w4.w4_quantize_dyadic5(W, wd)
+        del W, wd
+        x = synthetic.normal_bf16_device((1, k), 1.0, synthetic.seed(2, i, 1), dev)
+        probs.append({"packed": P, "codebook": M, "scales": S, "x": x,
+                      "y": torch.empty((1, n), device=dev)})
+        total += n * k // 2 + n * k // 8 + 2 * n * (k // 64) + 2 * k + 4 * n
+    return probs, total
+
+
+def signmag8_stack_problems(w4, synthetic, torch, dev, stream):
+    """The 2B model's 224 [2048, 2048] matrices (Student-t nu = 5) as SIGNMAG8
+    with magnitudes fitted on the GPU, one m = 1 problem each; problems and
+    algorithmic (actual) bytes."""
+    probs, total = [], 0
+    for i in range(224):
+        W = synthetic.student_t_bf16_device((2048, 2048), 5, 0.02, synthetic.seed(4, i, 0), dev)
+        cb = w4.w4_signmag8_fit(W, 25, stream=stream)
+        P, _ = w4.w4_quantize_pack(W, w4.W4_SIGNMAG8, codebook=cb, stream=stream)
+        del W
+        x = synthetic.normal_bf16_device((1, 2048), 1.0, synthetic.seed(4, i, 1), dev)
+        probs.append({"packed": P, "codebook": cb, "x": x, "y": torch.empty((1, 2048), device=dev)})
+        total += 2048 * 1024 + 2048 * 64 * 16 + 2 * 2048 + 4 * 2048
+    return probs, total
+
+
 def other_configs(w4, synthetic, torch, dev, stream, args):
     """Rows for the 2048^2 single GEMV, the 3.9B-sized LUT16 fits and GEMVs and
     the 2B SIGNMAG8 dequant + batched GEMV."""
@@ -258,17 +310,7 @@ def other_configs(w4, synthetic, torch, dev, stream, args):
     # LUT16S (one table per matrix, 4.25 bits per weight): the three 3.9B-sized
     # matrices in one batched m = 1 launch
     log("LUT16S 3.9B-sized batched GEMV")
-    probs, total = [], 0
-    for i, (n, k) in enumerate([(4096, 4096), (11008, 4096), (4096, 11008)]):
-        W = synthetic.normal_outliers_bf16_device((n, k), 0.015, 0.001, 0.15,
-                                                  synthetic.seed(6, i, 0), dev)
-        sc, T = shared_table_levels(W)
-        P, _ = w4.w4_quantize_pack(W, w4.W4_LUT16S, scales=sc, codebook=T)
-        del W
-        x = synthetic.normal_bf16_device((1, k), 1.0, synthetic.seed(6, i, 1), dev)
-        probs.append({"packed": P, "scales": sc, "codebook": T, "x": x,
-                      "y": torch.empty((1, n), device=dev)})
-        total += n * k // 2 + n * (k // 64) * 2 + 32 + 2 * k + 4 * n
+    probs, total = lut16s_shapes_problems(w4, synthetic, torch, dev)
     batch = w4.w4_gemv_batched_plan(probs, w4.W4_LUT16S)
     ms = timed(lambda: batch(stream), stream, args.steps, args.warmup)
     rows["lut16s_gemv_m1_3.9b_shapes_batched"] = {"ms": ms, "GB/s": total / (ms * 1e-3) / 1e9}
@@ -291,16 +333,7 @@ def other_configs(w4, synthetic, torch, dev, stream, args):
     # quantizer on the 8192^2 prefill weight
     log("DYADIC5 1B stack batched GEMV")
     gen = torch.Generator(device=dev).manual_seed(synthetic.seed(7, 0, 0))
-    probs, total = [], 0
-    for i, (n, k) in enumerate(synthetic.llama1b_stack_shapes()):
-        W = synthetic.student_t_bf16_device((n, k), 4, 0.02, synthetic.seed(2, i, 0), dev)
-        wd = torch.randint(3, 6, (n, k // 64), dtype=torch.uint8, device=dev, generator=gen)
-        P, M, S = w4.w4_quantize_dyadic5(W, wd)
-        del W, wd
-        x = synthetic.normal_bf16_device((1, k), 1.0, synthetic.seed(2, i, 1), dev)
-        probs.append({"packed": P, "codebook": M, "scales": S, "x": x,
-                      "y": torch.empty((1, n), device=dev)})
-        total += n * k // 2 + n * k // 8 + 2 * n * (k // 64) + 2 * k + 4 * n
+    probs, total = dyadic5_stack_problems(w4, synthetic, torch, dev, gen)
     batch = w4.w4_gemv_batched_plan(probs, w4.W4_DYADIC5)
     ms = timed(lambda: batch(stream), stream, args.steps, args.warmup)
     rows["dyadic5_gemv_m1_llama1b_stack_batched"] = {"ms": ms, "GB/s": total / (ms * 1e-3) / 1e9}
@@ -316,25 +349,16 @@ def other_configs(w4, synthetic, torch, dev, stream, args):
 
     # SIGNMAG8: 224 x 2048^2, Student-t nu = 5; dense dequant + one batched m = 1 GEMV
     log("SIGNMAG8 2B stack")
-    probs, total = [], 0
-    for i in range(224):
-        W = synthetic.student_t_bf16_device((2048, 2048), 5, 0.02, synthetic.seed(4, i, 0), dev)
-        cb = w4.w4_signmag8_fit(W, 25, stream=stream)
-        if i == 0:
-            ms = timed(lambda: w4.w4_signmag8_fit(W, 25, codebook=cb, stream=stream), stream,
-                       FIT_STEPS, 1)
-            rows["signmag8_fit_2048x2048"] = {"ms": ms,
-                                              "Mgroups/s": 2048 * 64 / (ms * 1e-3) / 1e6,
-                                              "Gweights/s": 2048 * 2048 / (ms * 1e-3) / 1e9}
-            ms = timed(lambda: w4.w4_signmag8_fit_warm(W, 25, stream=stream), stream,
-                       FIT_STEPS, 1)
-            rows["signmag8_fit_warm_2048x2048"] = {"ms": ms,
-                                                   "Mgroups/s": 2048 * 64 / (ms * 1e-3) / 1e6}
-        P, _ = w4.w4_quantize_pack(W, w4.W4_SIGNMAG8, codebook=cb, stream=stream)
-        del W
-        x = synthetic.normal_bf16_device((1, 2048), 1.0, synthetic.seed(4, i, 1), dev)
-        probs.append({"packed": P, "codebook": cb, "x": x, "y": torch.empty((1, 2048), device=dev)})
-        total += 2048 * 1024 + 2048 * 64 * 16 + 2 * 2048 + 4 * 2048
+    W = synthetic.student_t_bf16_device((2048, 2048), 5, 0.02, synthetic.seed(4, 0, 0), dev)
+    cb = w4.w4_signmag8_fit(W, 25, stream=stream)
+    ms = timed(lambda: w4.w4_signmag8_fit(W, 25, codebook=cb, stream=stream), stream,
+               FIT_STEPS, 1)
+    rows["signmag8_fit_2048x2048"] = {"ms": ms, "Mgroups/s": 2048 * 64 / (ms * 1e-3) / 1e6,
+                                      "Gweights/s": 2048 * 2048 / (ms * 1e-3) / 1e9}
+    ms = timed(lambda: w4.w4_signmag8_fit_warm(W, 25, stream=stream), stream, FIT_STEPS, 1)
+    rows["signmag8_fit_warm_2048x2048"] = {"ms": ms, "Mgroups/s": 2048 * 64 / (ms * 1e-3) / 1e6}
+    del W, cb
+    probs, total = signmag8_stack_problems(w4, synthetic, torch, dev, stream)
     batch = w4.w4_gemv_batched_plan(probs, w4.W4_SIGNMAG8)
     ms = timed(lambda: batch(stream), stream, args.steps, args.warmup)
     nominal = 224 * (2048 * 2048 * 4.25 / 8 + 2 * 2048 + 4 * 2048)
@@ -461,6 +485,24 @@ def main():
             ms = timed(lambda: batch(stream), stream, args.steps, args.warmup)
             print(json.dumps({"target": f"{name}_gemv_m1_llama1b_stack", "ms": ms,
                               "GB/s": total / (ms * 1e-3) / 1e9}), flush=True)
+        return
+    if args.only == "variants":
+        gen = torch.Generator(device=dev).manual_seed(synthetic.seed(7, 0, 0))
+        probs, total = dyadic5_stack_problems(w4, synthetic, torch, dev, gen)
+        cases = [("dyadic5_gemv_m1_llama1b_stack", w4.W4_DYADIC5, probs, total)]
+        probs, total = signmag8_stack_problems(w4, synthetic, torch, dev, stream)
+        cases.append(("signmag8_gemv_m1_224x2048x2048", w4.W4_SIGNMAG8, probs, total))
+        probs, total = lut16s_shapes_problems(w4, synthetic, torch, dev)
+        il = [dict(packed=w4.w4_lut16s_interleave(p["packed"], p["scales"]),
+                   codebook=p["codebook"], x=p["x"], y=p["y"]) for p in probs]
+        cases += [("lut16s_gemv_m1_3.9b_shapes", w4.W4_LUT16S, probs, total),
+                  ("lut16s_perm_gemv_m1_3.9b_shapes", w4.W4_LUT16S_PERM, probs, total),
+                  ("lut16s_il_gemv_m1_3.9b_shapes", w4.W4_LUT16S_IL, il, total)]
+        for name, codec, pr, b in cases:
+            batch = w4.w4_gemv_batched_plan(pr, codec)
+            ms = timed(lambda: batch(stream), stream, args.steps, args.warmup)
+            print(json.dumps({"target": name, "ms": ms, "GB/s": b / (ms * 1e-3) / 1e9}),
+                  flush=True)
         return
     if args.only == "singles":
         W = synthetic.normal_bf16_device((8192, 8192), 0.02, synthetic.seed(5, 0, 0), dev)

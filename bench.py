@@ -12,9 +12,11 @@ bf16 scales + x + fp32 y) / step time, in GB/s.
 Also measured in the same run and reported under "rows": the same pass as
 168 separate w4_gemv calls, quantize_pack and unpack_dequant, the prefill GEMM
 (M = 256, K = N = 8192, in TFLOP/s) with quantize_pack of its 8192^2 weight,
-and the other workloads' rows.  Single GEMV calls on one weight are also timed
-rotating over copies that together exceed the 256 MB Infinity Cache (rows
-ending in "_rotating"), so that each call reads its weight from HBM.
+and the other workloads' rows.  Single GEMV calls are timed as replays of a HIP
+graph of many such calls, so that the rate is the GPU's and not that of the
+Python binding's per-call checks (one row gives the latter); they are also
+timed rotating over copies of the weight that together exceed the 256 MB
+Infinity Cache (rows ending in "_rotating"), so that each call reads HBM.
 "context" holds what this GPU delivers in the
 same run: a plain streaming read of 4 GiB with 16-byte loads (the read
 ceiling the GEMV is set against), the end-to-end time of one such read over
@@ -101,20 +103,26 @@ def rotation_copies(weight_bytes):
     return max(2, -(-2 * INFINITY_CACHE_BYTES // weight_bytes))
 
 
-def timed_rotating(fns, stream, steps, warmup):
-    """ms per call of calls taken round robin from fns."""
+def timed_calls(calls, stream, steps, warmup, per_graph=32):
+    """ms per call of single library calls on the GPU: `calls` (each takes
+    the stream to enqueue on), round robin, at least per_graph of them
+    captured into one HIP graph whose replays are timed.  Called one by one
+    from Python, a small call is bound by the host instead: the binding's
+    argument checks take longer than a 2048^2 GEMV's kernel."""
     import torch
-    for i in range(warmup):
-        fns[i % len(fns)]()
+    seq = [calls[i % len(calls)] for i in range(max(per_graph, len(calls)))]
+    cap = torch.cuda.Stream()
+    with torch.cuda.stream(cap):
+        for f in seq:  # eagerly first: a call's workspace is made outside the capture
+            f(cap)
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(steps):
-        fns[i % len(fns)]()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap):
+        for f in seq:
+            f(cap)
+    ms = timed(graph.replay, stream, max(2, steps // len(seq)), max(1, warmup // len(seq)))
+    del graph
+    return ms / len(seq)
 
 
 def timed(fn, stream, steps, warmup):
@@ -261,17 +269,22 @@ def other_configs(w4, synthetic, torch, dev, stream, args):
     x = synthetic.normal_bf16_device((1, 2048), 1.0, synthetic.seed(0, 0, 1), dev)
     P, S = w4.w4_quantize_pack(W, w4.W4_DYADIC)
     y = torch.empty((1, 2048), device=dev)
+    b = 2048 * 1024 + 2 * 2048 * 32 + 2 * 2048 + 4 * 2048
+    ms = timed_calls([lambda st: w4.w4_gemv(P, x, w4.W4_DYADIC, scales=S, y=y, stream=st)],
+                     stream, args.steps, args.warmup)
+    rows["gemv_m1_2048x2048_single_call"] = {"ms": ms, "GB/s": b / (ms * 1e-3) / 1e9}
+    # the same call issued one by one from Python: the binding's per-call
+    # host cost, not the GPU, sets this rate
     ms = timed(lambda: w4.w4_gemv(P, x, w4.W4_DYADIC, scales=S, y=y, stream=stream), stream,
                args.steps, args.warmup)
-    b = 2048 * 1024 + 2 * 2048 * 32 + 2 * 2048 + 4 * 2048
-    rows["gemv_m1_2048x2048_single_call"] = {"ms": ms, "GB/s": b / (ms * 1e-3) / 1e9}
+    rows["gemv_m1_2048x2048_python_call"] = {"ms": ms, "GB/s": b / (ms * 1e-3) / 1e9}
     # the same call rotating over 256 copies of the weight (about 600 MB, more
     # than the 256 MB Infinity Cache holds), so each call reads its weight
     # from HBM rather than from a cache that the previous call warmed
     pool = [(P.clone(), S.clone()) for _ in range(256)]
-    calls = [lambda p=p, s=s: w4.w4_gemv(p, x, w4.W4_DYADIC, scales=s, y=y, stream=stream)
+    calls = [lambda st, p=p, s=s: w4.w4_gemv(p, x, w4.W4_DYADIC, scales=s, y=y, stream=st)
              for p, s in pool]
-    ms = timed_rotating(calls, stream, max(args.steps, 256), min(args.warmup, 256))
+    ms = timed_calls(calls, stream, max(args.steps, 256), min(args.warmup, 256))
     rows["gemv_m1_2048x2048_rotating_256"] = {"ms": ms, "GB/s": b / (ms * 1e-3) / 1e9,
                                               "copies": len(pool)}
     del W, P, S, pool, calls
@@ -294,15 +307,17 @@ def other_configs(w4, synthetic, torch, dev, stream, args):
         for m in (1, 4, 16):
             x = synthetic.normal_bf16_device((m, k), 1.0, synthetic.seed(3, i, 1), dev)
             y = torch.empty((m, n), device=dev)
-            ms = timed(lambda: w4.w4_gemv(P, x, w4.W4_LUT16, scales=sc, codebook=L, y=y,
-                                          stream=stream), stream, args.steps, args.warmup)
+            ms = timed_calls([lambda st: w4.w4_gemv(P, x, w4.W4_LUT16, scales=sc, codebook=L,
+                                                    y=y, stream=st)],
+                             stream, args.steps, args.warmup)
             b = wb + 2 * m * k + 4 * m * n
             rows[f"lut16_gemv_m{m}_{n}x{k}"] = {"ms": ms, "GB/s": b / (ms * 1e-3) / 1e9}
             # the same call over copies of the weight totalling more than the
             # Infinity Cache holds, so each call reads its weight from HBM
-            calls = [lambda p=p, s=s, c=c: w4.w4_gemv(p, x, w4.W4_LUT16, scales=s, codebook=c,
-                                                      y=y, stream=stream) for p, s, c in pool]
-            ms = timed_rotating(calls, stream, max(args.steps, 4 * len(pool)), args.warmup)
+            calls = [lambda st, p=p, s=s, c=c: w4.w4_gemv(p, x, w4.W4_LUT16, scales=s,
+                                                          codebook=c, y=y, stream=st)
+                     for p, s, c in pool]
+            ms = timed_calls(calls, stream, max(args.steps, 4 * len(pool)), args.warmup)
             rows[f"lut16_gemv_m{m}_{n}x{k}_rotating"] = {
                 "ms": ms, "GB/s": b / (ms * 1e-3) / 1e9, "copies": len(pool)}
         del P, sc, L, pool
@@ -509,8 +524,8 @@ def main():
         P, S = w4.w4_quantize_pack(W, w4.W4_DYADIC)
         x = synthetic.normal_bf16_device((1, 8192), 1.0, synthetic.seed(5, 0, 1), dev)
         y = torch.empty((1, 8192), device=dev)
-        ms = timed(lambda: w4.w4_gemv(P, x, w4.W4_DYADIC, scales=S, y=y, stream=stream),
-                   stream, args.steps, args.warmup)
+        ms = timed_calls([lambda st: w4.w4_gemv(P, x, w4.W4_DYADIC, scales=S, y=y, stream=st)],
+                         stream, args.steps, args.warmup)
         b = 8192 * 4096 + 2 * 8192 * 128 + 2 * 8192 + 4 * 8192
         print(json.dumps({"target": "gemv_m1_8192x8192", "ms": ms, "GB/s": b / (ms * 1e-3) / 1e9}),
               flush=True)
@@ -522,8 +537,9 @@ def main():
             P, _ = w4.w4_quantize_pack(W, w4.W4_LUT16, scales=sc, codebook=L)
             x = synthetic.normal_bf16_device((1, k), 1.0, synthetic.seed(3, i, 1), dev)
             y = torch.empty((1, n), device=dev)
-            ms = timed(lambda: w4.w4_gemv(P, x, w4.W4_LUT16, scales=sc, codebook=L, y=y,
-                                          stream=stream), stream, args.steps, args.warmup)
+            ms = timed_calls([lambda st: w4.w4_gemv(P, x, w4.W4_LUT16, scales=sc, codebook=L,
+                                                    y=y, stream=st)],
+                             stream, args.steps, args.warmup)
             b = n * k // 2 + n * (k // 64) * 34 + 2 * k + 4 * n
             print(json.dumps({"target": f"lut16_gemv_m1_{n}x{k}", "ms": ms,
                               "GB/s": b / (ms * 1e-3) / 1e9}), flush=True)
@@ -646,16 +662,16 @@ def main():
             del Xm, Ym
         xv = torch.empty((1, 8192), dtype=torch.bfloat16, device=dev).copy_(X[:1])
         yv = torch.empty((1, 8192), dtype=torch.float32, device=dev)
-        ms_v5 = timed(lambda: w4.w4_gemv(P, xv, w4.W4_DYADIC, scales=S, y=yv, stream=stream),
-                      stream, args.steps, args.warmup)
+        ms_v5 = timed_calls([lambda st: w4.w4_gemv(P, xv, w4.W4_DYADIC, scales=S, y=yv,
+                                                   stream=st)], stream, args.steps, args.warmup)
         vb = 8192 * 4096 + 2 * 8192 * 128 + 2 * 8192 + 4 * 8192
         rows["gemv_m1_8192x8192"] = {"ms": ms_v5, "GB/s": vb / (ms_v5 * 1e-3) / 1e9}
         # the same call over copies of the weight totalling more than the
         # Infinity Cache holds, so each call reads its weight from HBM
         pool = [(P.clone(), S.clone()) for _ in range(rotation_copies(8192 * 4096 + 2 * 8192 * 128))]
-        calls = [lambda p=p, s=s: w4.w4_gemv(p, xv, w4.W4_DYADIC, scales=s, y=yv, stream=stream)
+        calls = [lambda st, p=p, s=s: w4.w4_gemv(p, xv, w4.W4_DYADIC, scales=s, y=yv, stream=st)
                  for p, s in pool]
-        ms_r5 = timed_rotating(calls, stream, max(args.steps, 4 * len(pool)), args.warmup)
+        ms_r5 = timed_calls(calls, stream, max(args.steps, 4 * len(pool)), args.warmup)
         rows["gemv_m1_8192x8192_rotating"] = {"ms": ms_r5, "GB/s": vb / (ms_r5 * 1e-3) / 1e9,
                                               "copies": len(pool)}
         del pool, calls

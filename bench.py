@@ -12,9 +12,10 @@ bf16 scales + x + fp32 y) / step time, in GB/s.
 Also measured in the same run and reported under "rows": the same pass as
 168 separate w4_gemv calls, quantize_pack and unpack_dequant, the prefill GEMM
 (M = 256, K = N = 8192, in TFLOP/s) with quantize_pack of its 8192^2 weight,
-and the other workloads' rows.  Single GEMV calls are timed as replays of a HIP
-graph of many such calls, so that the rate is the GPU's and not that of the
-Python binding's per-call checks (one row gives the latter); they are also
+and the other workloads' rows.  Single calls are timed both by a Python launch
+loop and as replays of a HIP graph of many such calls, and the faster counts
+(from Python a small call is bound by the binding's per-call checks on the
+host; one row gives that rate); single GEMV calls are also
 timed rotating over copies of the weight that together exceed the 256 MB
 Infinity Cache (rows ending in "_rotating"), so that each call reads HBM.
 "context" holds what this GPU delivers in the
@@ -51,7 +52,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["headline", "gemm", "copy", "fit", "codec", "singles",
-                                       "lut16s", "variants"],
+                                       "lut16s", "variants", "floors"],
                     default=None,
                     help="run one target only (for profiler runs): the batched decode pass, "
                          "the M=256 GEMM, a 1 GiB device copy that calibrates HBM counters, "
@@ -60,7 +61,10 @@ def parse():
                          "LUT16 on the 3.9B shapes), the decode stack as LUT16S in its three "
                          "decode variants, or the batched m = 1 passes of the other codecs "
                          "(DYADIC5 decode stack, 224-matrix SIGNMAG8 stack, the 3.9B-sized "
-                         "matrices as LUT16S in its three decode variants)")
+                         "matrices as LUT16S in its three decode variants), or what single "
+                         "calls can reach: a plain read of 2.4 MB and of 37.7 MB per call "
+                         "(one buffer, and rotating over 16) beside the 8192^2 DYADIC GEMV, "
+                         "each by a launch loop and by graph replays")
     ap.add_argument("--only-headline", action="store_true", help="same as --only headline")
     a = ap.parse_args()
     if a.only_headline:
@@ -103,12 +107,34 @@ def rotation_copies(weight_bytes):
     return max(2, -(-2 * INFINITY_CACHE_BYTES // weight_bytes))
 
 
+def timed_single(calls, stream, steps, warmup):
+    """ms per call of back-to-back single library calls (`calls`, each taking
+    the stream to enqueue on, round robin), and how it was timed: the faster
+    of a Python launch loop and replays of a HIP graph of the same calls.
+    From Python, a small call is bound by the host (the binding's argument
+    checks take longer than a 2048^2 GEMV's kernel); a graph removes that
+    cost but adds a little per node (0.8 us on the 8192^2 GEMV on one
+    machine), so each method wins somewhere."""
+    import torch
+    for i in range(warmup):
+        calls[i % len(calls)](stream)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        calls[i % len(calls)](stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_loop = e0.elapsed_time(e1) / steps
+    ms_graph = timed_calls(calls, stream, steps, warmup)
+    return (ms_graph, "graph") if ms_graph < ms_loop else (ms_loop, "python_loop")
+
+
 def timed_calls(calls, stream, steps, warmup, per_graph=32):
     """ms per call of single library calls on the GPU: `calls` (each takes
     the stream to enqueue on), round robin, at least per_graph of them
-    captured into one HIP graph whose replays are timed.  Called one by one
-    from Python, a small call is bound by the host instead: the binding's
-    argument checks take longer than a 2048^2 GEMV's kernel."""
+    captured into one HIP graph whose replays are timed."""
     import torch
     seq = [calls[i % len(calls)] for i in range(max(per_graph, len(calls)))]
     cap = torch.cuda.Stream()
@@ -144,7 +170,7 @@ def read_ceiling(torch, dev, stream):
     """GB/s of a plain streaming read of 4 GiB with 16-byte nontemporal loads
     (libw4ctx.so), best of a few grid sizes: the read rate HBM delivers to a
     read-only kernel on this GPU; and ms per call of the same kernel over
-    2.25 MiB, back to back."""
+    2.25 MiB, back to back, timed as the single GEMV calls are."""
     import ctypes
     lib = ctypes.CDLL(os.path.join(ROOT, "weight_only_bit_unpack_amd", "libw4ctx.so"))
     lib.w4ctx_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
@@ -167,12 +193,12 @@ def read_ceiling(torch, dev, stream):
     small = 9 << 18
     buf2 = torch.full((small // 4,), 0x01010101, dtype=torch.int32, device=dev)
 
-    def run_small():
+    def run_small(st):
         rc = lib.w4ctx_read_stream(ctypes.c_void_p(buf2.data_ptr()), small,
                                    ctypes.c_void_p(sink.data_ptr()), 1024,
-                                   ctypes.c_void_p(stream.cuda_stream))
+                                   ctypes.c_void_p(st.cuda_stream))
         assert rc == 0, rc
-    ms_small = timed(run_small, stream, 200, 20)
+    ms_small, _ = timed_single([run_small], stream, 320, 32)  # as single GEMV calls are timed
     del buf, buf2, sink
     torch.cuda.empty_cache()
     return best, ms_small
@@ -270,9 +296,10 @@ def other_configs(w4, synthetic, torch, dev, stream, args):
     P, S = w4.w4_quantize_pack(W, w4.W4_DYADIC)
     y = torch.empty((1, 2048), device=dev)
     b = 2048 * 1024 + 2 * 2048 * 32 + 2 * 2048 + 4 * 2048
-    ms = timed_calls([lambda st: w4.w4_gemv(P, x, w4.W4_DYADIC, scales=S, y=y, stream=st)],
-                     stream, args.steps, args.warmup)
-    rows["gemv_m1_2048x2048_single_call"] = {"ms": ms, "GB/s": b / (ms * 1e-3) / 1e9}
+    ms, how = timed_single([lambda st: w4.w4_gemv(P, x, w4.W4_DYADIC, scales=S, y=y, stream=st)],
+                           stream, args.steps, args.warmup)
+    rows["gemv_m1_2048x2048_single_call"] = {"ms": ms, "GB/s": b / (ms * 1e-3) / 1e9,
+                                             "timing": how}
     # the same call issued one by one from Python: the binding's per-call
     # host cost, not the GPU, sets this rate
     ms = timed(lambda: w4.w4_gemv(P, x, w4.W4_DYADIC, scales=S, y=y, stream=stream), stream,
@@ -284,9 +311,9 @@ def other_configs(w4, synthetic, torch, dev, stream, args):
     pool = [(P.clone(), S.clone()) for _ in range(256)]
     calls = [lambda st, p=p, s=s: w4.w4_gemv(p, x, w4.W4_DYADIC, scales=s, y=y, stream=st)
              for p, s in pool]
-    ms = timed_calls(calls, stream, max(args.steps, 256), min(args.warmup, 256))
+    ms, how = timed_single(calls, stream, max(args.steps, 256), min(args.warmup, 256))
     rows["gemv_m1_2048x2048_rotating_256"] = {"ms": ms, "GB/s": b / (ms * 1e-3) / 1e9,
-                                              "copies": len(pool)}
+                                              "copies": len(pool), "timing": how}
     del W, P, S, pool, calls
 
     # LUT16 on the 3.9B-sized shapes: k-means fit on the GPU, then GEMV at m = 1, 4, 16
@@ -307,19 +334,20 @@ def other_configs(w4, synthetic, torch, dev, stream, args):
         for m in (1, 4, 16):
             x = synthetic.normal_bf16_device((m, k), 1.0, synthetic.seed(3, i, 1), dev)
             y = torch.empty((m, n), device=dev)
-            ms = timed_calls([lambda st: w4.w4_gemv(P, x, w4.W4_LUT16, scales=sc, codebook=L,
-                                                    y=y, stream=st)],
-                             stream, args.steps, args.warmup)
+            ms, how = timed_single([lambda st: w4.w4_gemv(P, x, w4.W4_LUT16, scales=sc,
+                                                          codebook=L, y=y, stream=st)],
+                                   stream, args.steps, args.warmup)
             b = wb + 2 * m * k + 4 * m * n
-            rows[f"lut16_gemv_m{m}_{n}x{k}"] = {"ms": ms, "GB/s": b / (ms * 1e-3) / 1e9}
+            rows[f"lut16_gemv_m{m}_{n}x{k}"] = {"ms": ms, "GB/s": b / (ms * 1e-3) / 1e9,
+                                                "timing": how}
             # the same call over copies of the weight totalling more than the
             # Infinity Cache holds, so each call reads its weight from HBM
             calls = [lambda st, p=p, s=s, c=c: w4.w4_gemv(p, x, w4.W4_LUT16, scales=s,
                                                           codebook=c, y=y, stream=st)
                      for p, s, c in pool]
-            ms = timed_calls(calls, stream, max(args.steps, 4 * len(pool)), args.warmup)
+            ms, how = timed_single(calls, stream, max(args.steps, 4 * len(pool)), args.warmup)
             rows[f"lut16_gemv_m{m}_{n}x{k}_rotating"] = {
-                "ms": ms, "GB/s": b / (ms * 1e-3) / 1e9, "copies": len(pool)}
+                "ms": ms, "GB/s": b / (ms * 1e-3) / 1e9, "copies": len(pool), "timing": how}
         del P, sc, L, pool
 
     # LUT16S (one table per matrix, 4.25 bits per weight): the three 3.9B-sized
@@ -382,8 +410,9 @@ def other_configs(w4, synthetic, torch, dev, stream, args):
         "GB/s_at_nominal_4.25_bits": nominal / (ms * 1e-3) / 1e9}
     out = torch.empty((2048, 2048), dtype=torch.float16, device=dev)
     p0 = probs[0]
-    ms = timed(lambda: w4.w4_unpack_dequant(p0["packed"], w4.W4_SIGNMAG8, codebook=p0["codebook"],
-                                            out=out, stream=stream), stream, args.steps, args.warmup)
+    ms = timed_single([lambda st: w4.w4_unpack_dequant(p0["packed"], w4.W4_SIGNMAG8,
+                                                       codebook=p0["codebook"], out=out, stream=st)],
+                      stream, args.steps, args.warmup)[0]
     b = 2048 * 1024 + 2048 * 64 * 16 + 2 * 2048 * 2048
     rows["signmag8_dequant_2048x2048"] = {"ms": ms, "GB/s": b / (ms * 1e-3) / 1e9}
     del probs, batch, out
@@ -519,16 +548,51 @@ def main():
             print(json.dumps({"target": name, "ms": ms, "GB/s": b / (ms * 1e-3) / 1e9}),
                   flush=True)
         return
+    if args.only == "floors":
+        import ctypes
+        lib = ctypes.CDLL(os.path.join(ROOT, "weight_only_bit_unpack_amd", "libw4ctx.so"))
+        lib.w4ctx_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                          ctypes.c_int32, ctypes.c_void_p]
+        sink = torch.zeros(1024, dtype=torch.int32, device=dev)
+
+        def both(calls):  # us per call: launch loop, graph replays
+            t0 = timed(lambda: [c(stream) for c in calls], stream, max(1, args.steps // len(calls)),
+                       max(1, args.warmup // len(calls))) / len(calls)
+            return t0 * 1e3, timed_calls(calls, stream, args.steps, args.warmup) * 1e3
+        for nbytes, copies in ((9 << 18, 1), (36 << 20, 1), (36 << 20, 16)):
+            bufs = [torch.full((nbytes // 4,), 0x01010101, dtype=torch.int32, device=dev)
+                    for _ in range(copies)]
+            for blocks in (256, 1024, 4096):
+                calls = [lambda st, b=b: lib.w4ctx_read_stream(
+                    b.data_ptr(), nbytes, sink.data_ptr(), blocks, st.cuda_stream) for b in bufs]
+                us_loop, us_graph = both(calls)
+                print(json.dumps({"target": "read", "bytes": nbytes, "copies": copies,
+                                  "blocks": blocks, "us_loop": us_loop, "us_graph": us_graph}),
+                      flush=True)
+            del bufs
+        W = synthetic.normal_bf16_device((8192, 8192), 0.02, synthetic.seed(5, 0, 0), dev)
+        P, S = w4.w4_quantize_pack(W, w4.W4_DYADIC)
+        del W
+        x = synthetic.normal_bf16_device((1, 8192), 1.0, synthetic.seed(5, 0, 1), dev)
+        y = torch.empty((1, 8192), device=dev)
+        for copies in (1, 16):
+            pool = [(P, S)] + [(P.clone(), S.clone()) for _ in range(copies - 1)]
+            calls = [lambda st, p=p, s=s: w4.w4_gemv(p, x, w4.W4_DYADIC, scales=s, y=y, stream=st)
+                     for p, s in pool]
+            us_loop, us_graph = both(calls)
+            print(json.dumps({"target": "gemv_m1_8192x8192", "copies": copies,
+                              "us_loop": us_loop, "us_graph": us_graph}), flush=True)
+        return
     if args.only == "singles":
         W = synthetic.normal_bf16_device((8192, 8192), 0.02, synthetic.seed(5, 0, 0), dev)
         P, S = w4.w4_quantize_pack(W, w4.W4_DYADIC)
         x = synthetic.normal_bf16_device((1, 8192), 1.0, synthetic.seed(5, 0, 1), dev)
         y = torch.empty((1, 8192), device=dev)
-        ms = timed_calls([lambda st: w4.w4_gemv(P, x, w4.W4_DYADIC, scales=S, y=y, stream=st)],
-                         stream, args.steps, args.warmup)
+        ms, how = timed_single([lambda st: w4.w4_gemv(P, x, w4.W4_DYADIC, scales=S, y=y,
+                                                      stream=st)], stream, args.steps, args.warmup)
         b = 8192 * 4096 + 2 * 8192 * 128 + 2 * 8192 + 4 * 8192
-        print(json.dumps({"target": "gemv_m1_8192x8192", "ms": ms, "GB/s": b / (ms * 1e-3) / 1e9}),
-              flush=True)
+        print(json.dumps({"target": "gemv_m1_8192x8192", "ms": ms, "GB/s": b / (ms * 1e-3) / 1e9,
+                          "timing": how}), flush=True)
         del W, P, S
         for i, (n, k) in enumerate([(4096, 4096), (11008, 4096), (4096, 11008)]):
             W = synthetic.normal_outliers_bf16_device((n, k), 0.015, 0.001, 0.15,
@@ -537,11 +601,11 @@ def main():
             P, _ = w4.w4_quantize_pack(W, w4.W4_LUT16, scales=sc, codebook=L)
             x = synthetic.normal_bf16_device((1, k), 1.0, synthetic.seed(3, i, 1), dev)
             y = torch.empty((1, n), device=dev)
-            ms = timed_calls([lambda st: w4.w4_gemv(P, x, w4.W4_LUT16, scales=sc, codebook=L,
-                                                    y=y, stream=st)],
-                             stream, args.steps, args.warmup)
+            ms, how = timed_single([lambda st: w4.w4_gemv(P, x, w4.W4_LUT16, scales=sc,
+                                                          codebook=L, y=y, stream=st)],
+                                   stream, args.steps, args.warmup)
             b = n * k // 2 + n * (k // 64) * 34 + 2 * k + 4 * n
-            print(json.dumps({"target": f"lut16_gemv_m1_{n}x{k}", "ms": ms,
+            print(json.dumps({"target": f"lut16_gemv_m1_{n}x{k}", "ms": ms, "timing": how,
                               "GB/s": b / (ms * 1e-3) / 1e9}), flush=True)
             del W, P, sc, L
         return
@@ -609,21 +673,20 @@ def main():
         # quantize_pack and unpack_dequant over the stack
         q_bytes = sum(2 * n * k + n * k // 2 + 2 * n * (k // 64) for n, k in shapes)
 
-        def quant():
-            for m in mats:
-                w4.w4_quantize_pack(m["w"], w4.W4_DYADIC, packed=m["packed"], scales=m["scales"],
-                                    stream=stream)
-        ms_q = timed(quant, stream, 3, 1)
+        # (small calls: timed as the single GEMV calls are)
+        quant = [lambda st, m=m: w4.w4_quantize_pack(m["w"], w4.W4_DYADIC, packed=m["packed"],
+                                                     scales=m["scales"], stream=st)
+                 for m in mats]
+        ms_q = timed_single(quant, stream, 3 * len(quant), len(quant))[0] * len(quant)
         rows["quantize_pack_stack"] = {"ms": ms_q, "GB/s": q_bytes / (ms_q * 1e-3) / 1e9}
 
         outs = [torch.empty((n, k), dtype=torch.bfloat16, device=dev) for n, k in shapes[:7]]
         d_bytes = sum(n * k // 2 + 2 * n * (k // 64) + 2 * n * k for n, k in shapes[:7])
 
-        def deq():
-            for m, o in zip(mats[:7], outs):
-                w4.w4_unpack_dequant(m["packed"], w4.W4_DYADIC, scales=m["scales"], out=o,
-                                     stream=stream)
-        ms_d = timed(deq, stream, 10, 2)
+        deq = [lambda st, m=m, o=o: w4.w4_unpack_dequant(m["packed"], w4.W4_DYADIC,
+                                                         scales=m["scales"], out=o, stream=st)
+               for m, o in zip(mats[:7], outs)]
+        ms_d = timed_single(deq, stream, 10 * 35, 70)[0] * len(deq)
         rows["unpack_dequant_block"] = {"ms": ms_d, "GB/s": d_bytes / (ms_d * 1e-3) / 1e9,
                                         "matrices": 7}
         del outs
@@ -662,18 +725,20 @@ def main():
             del Xm, Ym
         xv = torch.empty((1, 8192), dtype=torch.bfloat16, device=dev).copy_(X[:1])
         yv = torch.empty((1, 8192), dtype=torch.float32, device=dev)
-        ms_v5 = timed_calls([lambda st: w4.w4_gemv(P, xv, w4.W4_DYADIC, scales=S, y=yv,
-                                                   stream=st)], stream, args.steps, args.warmup)
+        ms_v5, how = timed_single([lambda st: w4.w4_gemv(P, xv, w4.W4_DYADIC, scales=S, y=yv,
+                                                         stream=st)], stream, args.steps,
+                                  args.warmup)
         vb = 8192 * 4096 + 2 * 8192 * 128 + 2 * 8192 + 4 * 8192
-        rows["gemv_m1_8192x8192"] = {"ms": ms_v5, "GB/s": vb / (ms_v5 * 1e-3) / 1e9}
+        rows["gemv_m1_8192x8192"] = {"ms": ms_v5, "GB/s": vb / (ms_v5 * 1e-3) / 1e9,
+                                     "timing": how}
         # the same call over copies of the weight totalling more than the
         # Infinity Cache holds, so each call reads its weight from HBM
         pool = [(P.clone(), S.clone()) for _ in range(rotation_copies(8192 * 4096 + 2 * 8192 * 128))]
         calls = [lambda st, p=p, s=s: w4.w4_gemv(p, xv, w4.W4_DYADIC, scales=s, y=yv, stream=st)
                  for p, s in pool]
-        ms_r5 = timed_calls(calls, stream, max(args.steps, 4 * len(pool)), args.warmup)
+        ms_r5, how = timed_single(calls, stream, max(args.steps, 4 * len(pool)), args.warmup)
         rows["gemv_m1_8192x8192_rotating"] = {"ms": ms_r5, "GB/s": vb / (ms_r5 * 1e-3) / 1e9,
-                                              "copies": len(pool)}
+                                              "copies": len(pool), "timing": how}
         del pool, calls
         D = torch.empty((8192, 8192), dtype=torch.bfloat16, device=dev)
         ms_d5 = timed(lambda: w4.w4_unpack_dequant(P, w4.W4_DYADIC, scales=S, out=D,

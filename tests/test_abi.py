@@ -240,3 +240,19 @@ def test_lut16s_variants_rules(w4):
     assert w4._lib.w4_lut16s_interleave(4, 192, None, None, None, None) == E["shape"]
     assert w4._lib.w4_lut16s_interleave(4, 256, None, None, None, None) == E["inval"]
     assert w4._lib.w4_lut16s_interleave(-1, 256, None, None, None, None) == E["inval"]
+
+
+def test_binding_rejects_host_tensors(w4):
+    """The Python binding checks its tensors before calling the library: a
+    tensor in host memory is refused with ValueError (no GPU is touched)."""
+    import torch
+    packed = torch.zeros((4, 32), dtype=torch.uint8)
+    scales = torch.zeros((4, 1), dtype=torch.bfloat16)
+    x = torch.zeros((1, 64), dtype=torch.bfloat16)
+    for fn in (w4.w4_gemv, w4.w4_gemm, w4.w4_linear):
+        with pytest.raises(ValueError, match="packed must be a CUDA"):
+            fn(packed, x, w4.W4_DYADIC, scales=scales)
+    with pytest.raises(ValueError, match="w must be a CUDA"):
+        w4.w4_quantize_pack(torch.zeros((4, 64), dtype=torch.bfloat16), w4.W4_DYADIC)
+    with pytest.raises(ValueError, match="packed is required"):
+        w4.w4_gemv(None, x, w4.W4_DYADIC, scales=scales)

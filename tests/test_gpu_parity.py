@@ -1048,3 +1048,55 @@ def test_lut16s_variants_batched(w4, codec, m):
     torch.cuda.synchronize()
     for pr, (x, w_hat) in zip(probs, refs):
         _gemv_check(pr["y"], x, w_hat, False)
+
+
+def test_binding_validation(w4):
+    """The Python binding's checks of device tensors (dtype, shape,
+    contiguity, side-table shape) raise ValueError before any launch, and a
+    well-formed call after them still runs."""
+    report("binding_validation")
+    n, k = 64, 128
+    p = torch.zeros((n, k // 2), dtype=torch.uint8, device="cuda")
+    s = torch.zeros((n, k // 64), dtype=torch.bfloat16, device="cuda")
+    x = torch.zeros((2, k), dtype=torch.bfloat16, device="cuda")
+    bad = [
+        (dict(packed=p.float()), "packed has dtype"),
+        (dict(x=x.float()), "x has dtype"),
+        (dict(x=torch.zeros((2, k + 64), dtype=torch.bfloat16, device="cuda")), "x must be"),
+        (dict(scales=torch.zeros((n, 1), dtype=torch.bfloat16, device="cuda")),
+         "scales has shape"),
+        (dict(scales=torch.zeros((k // 64, n), dtype=torch.bfloat16, device="cuda").t()),
+         "scales must be contiguous"),
+        (dict(y=torch.empty((2, n + 1), device="cuda")), "y has shape"),
+        (dict(y=torch.empty((2, n), dtype=torch.float16, device="cuda")), "y has dtype"),
+    ]
+    for over, msg in bad:
+        a = dict(packed=p, x=x, scales=s, y=None)
+        a.update(over)
+        with pytest.raises(ValueError, match=msg):
+            w4.w4_gemv(a["packed"], a["x"], w4.W4_DYADIC, scales=a["scales"], y=a["y"])
+    y = w4.w4_gemv(p, x, w4.W4_DYADIC, scales=s)
+    torch.cuda.synchronize()
+    assert torch.equal(y, torch.zeros((2, n), device="cuda"))
+
+
+def test_binding_current_stream(w4):
+    """With no stream given, a call enqueues on torch's current stream (the
+    binding reads its handle through a cheaper query): the same handle as
+    torch.cuda.current_stream(), also inside a stream context, and a call
+    made there is ordered after that stream's earlier work."""
+    report("binding_current_stream")
+    assert w4._stream(None) == torch.cuda.current_stream().cuda_stream
+    side = torch.cuda.Stream()
+    n, k = 256, 2048
+    w = synthetic.normal_bf16((n, k), 0.02, 5100)
+    idx, s = native.dyadic_quantize(w)
+    p, sd = dev_u8(packing.pack(idx)), dev_bf16(s)
+    with torch.cuda.stream(side):
+        assert w4._stream(None) == side.cuda_stream
+        xb = synthetic.normal_bf16((1, k), 1.0, 5101)
+        x = torch.empty((1, k), dtype=torch.bfloat16, device="cuda")
+        x.view(torch.int16).copy_(torch.from_numpy(xb.view(np.int16)))  # on `side`
+        y = w4.w4_gemv(p, x, w4.W4_DYADIC, scales=sd)
+    side.synchronize()
+    _gemv_check(y, xb, bits.bf16_to_f64(native.dyadic_dequant(idx, s)), False)

@@ -93,28 +93,44 @@ def w4_group_size(codec):
 _U16 = (torch.bfloat16, torch.float16, torch.int16, torch.uint16)
 
 
+# (the declared argtypes let ctypes take plain ints for the pointer arguments)
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()
 
 
-def _stream(stream):
-    s = torch.cuda.current_stream() if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+# The current stream's handle without building a Stream object (which costs
+# a few microseconds per call), where this torch build has the query.
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
-def _need(t, name, dtypes, shape=None):
+def _stream(stream, dev=None):
+    """HIP stream handle: the given torch stream, else the current stream of
+    device dev (default: the current device)."""
+    if stream is not None:
+        return stream.cuda_stream
+    if _raw_stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return _raw_stream(torch.cuda.current_device() if dev is None else dev)
+
+
+def _need(t, name, dtypes, shape=None, dev=None):
+    """Checks a tensor argument; dev: the current device's index when the
+    caller already has it (a small call's checks cost more than its kernel)."""
     if t is None:
         raise ValueError(f"{name} is required")
-    if not t.is_cuda:
+    d = t.get_device()
+    if d < 0:
         raise ValueError(f"{name} must be a CUDA (HIP) tensor")
-    if t.device.index != torch.cuda.current_device():
+    if dev is None:
+        dev = torch.cuda.current_device()
+    if d != dev:
         raise ValueError(f"{name} is on {t.device}; the library works on the current device "
-                         f"(cuda:{torch.cuda.current_device()})")
+                         f"(cuda:{dev})")
     if t.dtype not in dtypes:
         raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    if shape is not None and tuple(t.shape) != tuple(shape):
+    if shape is not None and t.shape != shape:
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     return t
 
@@ -126,18 +142,18 @@ def _k_of(codec, packed):
     return 2 * packed.shape[1]
 
 
-def _side_tables(codec, n, k, scales, codebook):
+def _side_tables(codec, n, k, scales, codebook, dev=None):
     g = GROUP[codec]
     if codec in (W4_DYADIC, W4_LUT16, W4_LUT16S, W4_DYADIC5, W4_LUT16S_PERM):
-        _need(scales, "scales", _U16, (n, k // 64))
+        _need(scales, "scales", _U16, (n, k // 64), dev)
     if codec == W4_DYADIC5:
-        _need(codebook, "codebook (high-bit plane)", (torch.uint8,), (n, k // 8))
+        _need(codebook, "codebook (high-bit plane)", (torch.uint8,), (n, k // 8), dev)
     if codec == W4_LUT16:
-        _need(codebook, "codebook", _U16, (n, k // 64, 16))
+        _need(codebook, "codebook", _U16, (n, k // 64, 16), dev)
     if codec in (W4_LUT16S, W4_LUT16S_PERM, W4_LUT16S_IL):
-        _need(codebook, "codebook", _U16, (16,))
+        _need(codebook, "codebook", _U16, (16,), dev)
     if codec == W4_SIGNMAG8:
-        _need(codebook, "codebook", _U16, (n, k // g, 8))
+        _need(codebook, "codebook", _U16, (n, k // g, 8), dev)
 
 
 def w4_quantize_pack(w, codec=W4_DYADIC, *, scales=None, codebook=None, packed=None,
@@ -248,10 +264,11 @@ def w4_signmag8_fit_warm(w, iters=25, *, codebook=None, params=None, stream=None
 
 def _matmul(fn, packed, x, codec, scales, codebook, y, y_dtype, stream):
     _need(packed, "packed", (torch.uint8,))
+    dev = packed.get_device()  # the current device, as just checked
     n = packed.shape[0]
     k = _k_of(codec, packed)
-    _side_tables(codec, n, k, scales, codebook)
-    _need(x, "x", _U16)
+    _side_tables(codec, n, k, scales, codebook, dev)
+    _need(x, "x", _U16, None, dev)
     if x.dim() != 2 or x.shape[1] != k:
         raise ValueError(f"x must be [m, {k}]")
     m = x.shape[0]
@@ -259,9 +276,9 @@ def _matmul(fn, packed, x, codec, scales, codebook, y, y_dtype, stream):
     if y is None:
         y = torch.empty((m, n), dtype=torch.bfloat16 if code == W4_BF16 else torch.float32,
                         device=packed.device)
-    _need(y, "y", (torch.float32,) if code == W4_F32 else _U16, (m, n))
+    _need(y, "y", (torch.float32,) if code == W4_F32 else _U16, (m, n), dev)
     _check(fn(codec, n, k, _ptr(packed), _ptr(scales), _ptr(codebook), _ptr(x), m, _ptr(y),
-              code, _stream(stream)))
+              code, _stream(stream, dev)))
     return y
 
 
@@ -320,8 +337,7 @@ class W4GemvBatch:
         return self.info.total_tiles
 
     def __call__(self, stream=None):
-        _check(_lib.w4_gemv_batched(self.codec, self.m, self.y_dtype,
-                                    ctypes.c_void_p(self.table.data_ptr()),
+        _check(_lib.w4_gemv_batched(self.codec, self.m, self.y_dtype, self.table.data_ptr(),
                                     ctypes.byref(self.info), _stream(stream)))
 
 

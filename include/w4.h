@@ -94,7 +94,9 @@ typedef enum {
  * tiles decodes a packed byte at a time through a 256-entry table of level
  * pairs (L[b & 15], L[b >> 4]) that each block builds in LDS; its single
  * calls and its batches of short tiles decode per nibble as W4_LUT16S_PERM,
- * measured as fast or faster there.  Results are bit-identical either way.
+ * measured as fast or faster there.  The two decodes give the matrix core the
+ * same products in a different order within each group of 8 weights, so
+ * their results agree within the GEMV tolerance but not always bit for bit.
  * Two variants are kept for comparison:
  * W4_LUT16S_PERM: the LUT16S storage and results, with a GEMV that always
  *   looks the levels up per nibble from byte-plane tables with v_perm, as
@@ -104,7 +106,8 @@ typedef enum {
  *   the block's 128 packed bytes, its four bf16 scales and 8 zero bytes, so
  *   `packed` is uint8 [n][k/256 * 144] and `scales` is unused.  Built from the
  *   planar arrays by w4_lut16s_interleave; taken by w4_gemv and the batched
- *   GEMV (bit-identical to W4_LUT16S); the other calls return
+ *   GEMV (decoded through the pair table, within the GEMV tolerance of
+ *   W4_LUT16S as above); the other calls return
  *   W4_EUNSUPPORTED. */
 typedef enum {
   W4_DYADIC = 0,

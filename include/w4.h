@@ -294,8 +294,12 @@ w4_status w4_signmag8_fit_warm(int64_t n, int64_t k, const uint16_t* w, uint16_t
  * the codebook in registers).
  * x: bf16 [m][k], 16-byte aligned.  m: 1..16 (m == 0: nothing to do).
  * y: [m][n] of y_dtype W4_F32 (4-byte aligned) or W4_BF16 (RNE, 2-byte aligned).
- * The result is within 1e-3 * sum_c |x w_hat| + 1e-6 of the exact sum, and the
- * same inputs always give the same bits.  k == 0 (with m, n > 0): y = +0.
+ * The result is within 1e-3 * sum_c |x w_hat| + 1e-6 of the exact sum (bf16 y:
+ * plus its own rounding, 2^-8 |y|), and the same inputs always give the same
+ * bits.  The bound follows from the fp32 sums alone for k <= 16760; above
+ * that it rests on the matrix core summing each instruction's products
+ * before adding them to the accumulator (tested to k = 65600).
+ * k == 0 (with m, n > 0): y = +0.
  * Workspace: with m >= 2 and n <= 65536 the call may split k into S <= 32
  * slices across blocks and enqueue a second kernel that adds the slices' fp32
  * partial sums in slice order; the partials use a device buffer of
@@ -311,8 +315,8 @@ w4_status w4_gemv(int32_t codec, int64_t n, int64_t k, const uint8_t* packed,
  * w4_gemm -- fused dequant + matrix product for prefill-sized batches,
  * Y[i][r] = sum_c X[i][c] * w_hat[r][c] with bf16 MFMA and fp32 accumulation;
  * the weight tiles are rebuilt into LDS.  [KM] sec. 4.1 (the 4-bit mixed kernel
- * band, m up to 256).  Same arguments as w4_gemv; m >= 1 (tuned for m >= 128).
- * k == 0 (with m, n > 0): y = +0.
+ * band, m up to 256).  Same arguments, tolerance and determinism as w4_gemv;
+ * m >= 1 (tuned for m >= 128).  k == 0 (with m, n > 0): y = +0.
  * Workspace: the call enqueues up to three kernels (an activation re-layout,
  * the product, and an in-order sum of the k-split partials) that use a device
  * buffer of ceil(m/B) * B * k * 2 bytes plus, when k is split S <= 8 ways,

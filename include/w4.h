@@ -385,7 +385,9 @@ w4_status w4_linear(int32_t codec, int64_t n, int64_t k, const uint8_t* packed,
  *    problems with larger k get earlier work) and fills *info.
  * 2. Copy the count records byte for byte into device memory (16-byte
  *    aligned).  The table is only read, so it can be launched any number of
- *    times, also concurrently.
+ *    times; each launch writes every problem's y, so launches that overlap
+ *    in time write the same outputs and must be ordered by the caller if
+ *    anything reads or changes those buffers in between.
  * 3. Call w4_gemv_batched with that device table and the plan's info.  The
  *    kernel trusts the device copy: it must equal an array the plan accepted.
  * Errors: W4_EINVAL / W4_ESHAPE / W4_EALIGN / W4_EUNSUPPORTED as for w4_gemv

@@ -105,6 +105,46 @@ def test_dequant_every_index_vs_exact(sbits):
         assert out[0, j] == _rne_int(sbits, j % 32), (hex(sbits), j)
 
 
+def _rne_int_fast(sbits, j5):
+    """RNE_bf16((s/16)(j5 - 16)) in integer arithmetic (the same result as
+    _rne_int, fast enough for every scale): an exact zero is +0, a nonzero
+    product rounding to zero keeps its sign."""
+    d = j5 - 16
+    e, m = (sbits >> 7) & 0xFF, sbits & 0x7F
+    S, a = (m, -133) if e == 0 else (m + 128, e - 134)    # |s| = S * 2**a
+    if S == 0 or d == 0:
+        return 0
+    sign = 0x8000 if (d < 0) != (sbits >= 0x8000) else 0
+    P, f = S * abs(d), a - 4                                # |value| = P * 2**f
+    q = max(P.bit_length() - 1 + f - 7, -133)
+    sh = q - f
+    if sh <= 0:
+        r = P << (-sh)
+    else:
+        r, rem = P >> sh, P & ((1 << sh) - 1)
+        if rem > (1 << (sh - 1)) or (rem == (1 << (sh - 1)) and r & 1):
+            r += 1
+    if r == 256:
+        r, q = 128, q + 1
+    if r < 128:
+        return sign | r                                     # subnormal, or rounded to zero
+    return sign | ((q + 134) << 7) | (r - 128)
+
+
+def test_dequant_every_scale_every_index():
+    """Every finite bf16 scale of either sign x all 32 indices against the
+    integer rounding, which agrees with the exact-fraction rounding above on
+    the scales that test uses."""
+    for sb in (0x3C23, 0x0001, 0x007F, 0x0080, 0x1234, 0x7F7F, 0x7E01, 0x4F00, 0xBC23, 0x8001):
+        for j in range(32):
+            assert _rne_int_fast(int(sb), j) == _rne_int(int(sb), j), (hex(sb), j)
+    allb = bits.all_finite_bf16()
+    idx = np.tile(np.arange(32, dtype=np.uint8), 2)[None, :].repeat(len(allb), axis=0)
+    got = dyadic5.dequant_from_indices(idx, allb[:, None])[:, :32]
+    want = np.array([[_rne_int_fast(int(sb), j) for j in range(32)] for sb in allb], np.uint16)
+    assert np.array_equal(got, want)
+
+
 def test_msb_layout_is_a_bijection():
     pos = sorted(dyadic5.msb_bit(i) for i in range(32))
     assert pos == list(range(32))

@@ -325,6 +325,31 @@ def test_signmag8_dequant_sign_and_exact_levels():
     assert np.array_equal((nib >> 3).astype(bool), wv < 0)
 
 
+def test_signmag8_dequant_every_magnitude():
+    """(nib & 8 ? -1 : +1) * M for every finite fp16 magnitude pattern (both
+    zeros, subnormals, the largest) and +-inf, with both signs, as exact values:
+    the oracle's rebuild is the exact product by +-1."""
+    u = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    pats = u[((u >> 10) & 0x1F) != 0x1F]                        # every finite fp16
+    pats = np.concatenate([pats, np.array([0x7C00, 0xFC00], np.uint16)])
+    n = (len(pats) + 7) // 8
+    cb = np.resize(pats, n * 8).reshape(n, 1, 8)
+    nib = np.tile(np.arange(16, dtype=np.uint8), 2)[None, :].repeat(n, axis=0)   # [n, 32]
+    deq = signmag8.dequant_from_indices(nib, cb)
+    for r in range(n):
+        for c in range(16):
+            m = int(cb[r, 0, c & 7])
+            got = int(deq[r, c])
+            if (m & 0x7FFF) == 0x7C00:                           # +-inf
+                assert got & 0x7FFF == 0x7C00
+                assert bool(got & 0x8000) == (bool(m & 0x8000) != bool(c & 8))
+                continue
+            want = exact.f16_fraction(m) * (-1 if c & 8 else 1)
+            assert exact.f16_fraction(got) == want, (hex(m), c)
+            if want == 0:                                        # the sign of a zero product
+                assert bool(got & 0x8000) == (bool(m & 0x8000) != bool(c & 8))
+
+
 def test_signmag8_fit_monotone_and_c_matches():
     w = _sm_data(16, 1024, 33)
     cb = signmag8.fit(w)

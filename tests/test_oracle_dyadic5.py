@@ -57,6 +57,33 @@ def test_argmin_vs_exact_rational_bruteforce():
             assert idx[r, c] == _brute(w[r, c], s[r, c // 64], int(widths[r, c // 64])), (r, c)
 
 
+def test_indices_on_the_gpu_sweeps_by_midpoint_count():
+    """The oracle's rule (first minimum of the fp64 distances) against a
+    different route to the nearest code, on the inputs of the GPU's
+    exhaustive DYADIC5 test (every finite bf16 value of magnitude <= s, seven
+    scales, widths 3 / 4 / 5): the codes are sorted and distinct, so the
+    lowest nearest one is the number of midpoints strictly below w; each
+    midpoint s (2t + 1 - 2h) / (2h) is exact in double, and so is each
+    comparison with a bf16 weight."""
+    from tests import sweeps
+    for sb in (0x3F80, 0x3FFF, 0x3C23, 0x0001, 0x0080, 0x7F7F, 0x7A01):
+        w = sweeps.groups_with_absmax(sb, 64)
+        widths = np.resize(np.array([3, 4, 5], np.uint8), (w.shape[0], 1))
+        s = dyadic.scales(w)
+        got = dyadic5.indices(w, s, widths)
+        wv = bits.bf16_to_f64(w)
+        sv = bits.bf16_to_f64(s)[:, 0]
+        for r in range(w.shape[0]):
+            h = 2 ** (int(widths[r, 0]) - 1)
+            if sv[r] == 0.0:
+                want = np.full(64, 16, np.uint8)
+            else:
+                mids = sv[r] * (2 * np.arange(2 * h - 1) + 1 - 2 * h) / (2 * h)
+                j = (wv[r][:, None] > mids[None, :]).sum(axis=1)
+                want = (j * 2 ** (5 - int(widths[r, 0]))).astype(np.uint8)
+            assert np.array_equal(got[r], want), (hex(sb), r)
+
+
 def test_width4_nests_in_the_4bit_codec():
     w = synthetic.student_t_bf16((16, 1024), 4, 0.02, 17)
     w[3, 64:128] = 0
